@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE EP low-latency dispatch + combine path on one MI355X.
+
+One step = ep_layout -> ep_dispatch -> ep_combine over one batch of seeded
+synthetic inputs already resident in HBM (the expert computation between
+dispatch and combine is outside the path; combine reads synthetic expert
+outputs).  Default workload: 128 tokens x hidden 7168, top-8 of 288 experts
+in 16 destination partitions, fp8 e4m3fn dispatch with per-128 scales, bf16
+combine -- the low-latency test shape the sources quote (MoRI PR #614,
+test_low_latency.py argument paragraph).  Steps are replayed from a HIP
+graph (small-token regime) and timed with HIP events on the stream they run
+on, between a synchronize on both sides.
+
+Prints ONE JSON line: value = algorithmic HBM bytes per step / time per
+step (GB/s; metadata excluded), plus the roofline of the dominant kernel and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine µs and HBM GB/s (% of 8 TB/s) at 128 tok×7168, topk 8"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+
+
+def algo_bytes(wl, N):
+    """Bytes the method must move (payload only): per phase and per step."""
+    T, H = wl.T, wl.H
+    if wl.payload == "fp8":
+        disp = T * 2 * H + N * (H + (H // 128) * 4)
+    else:
+        disp = T * 2 * H + N * 2 * H
+    comb = N * 2 * H + T * 2 * H
+    return {"dispatch": disp, "combine": comb, "layout": 0, "step": disp + comb}
+
+
+class Path:
+    """Device inputs + persistent buffers for one workload."""
+
+    def __init__(self, wl, seed=None):
+        import torch
+        import combine_ep_layout_05_amd as ep
+        from workloads import generate
+        self.ep, self.torch, self.wl = ep, torch, wl
+        self.d = generate(wl, seed=seed)
+        dev = torch.device("cuda:0")
+
+        def up(a, dt=None):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            return (t.view(dt) if dt is not None else t).to(dev)
+        self.idx = up(self.d["idx"])
+        self.w = up(self.d["w"])
+        self.x = up(self.d["x"].view(np.int16), torch.bfloat16)
+        self.y = up(self.d["y"].view(np.int16), torch.bfloat16)
+        self.buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+        self.stream = torch.cuda.Stream()
+        self.N = self.d["N"]
+
+    def enqueue(self, phase="step"):
+        s, b = self.stream, self.buf
+        if phase in ("step", "layout"):
+            b.layout(self.idx, s)
+        if phase in ("step", "dispatch"):
+            b.dispatch(self.x, s)
+        if phase in ("step", "combine"):
+            b.combine(self.y, self.w, s)
+
+    def capture(self, phase="step", reps=1):
+        ep, torch = self.ep, self.torch
+        with torch.cuda.stream(self.stream):
+            ep.ep_graph_begin(self.stream)
+            for _ in range(reps):
+                self.enqueue(phase)
+            return ep.ep_graph_end(self.stream)
+
+    def time_graph(self, g, launches, warmup=3):
+        torch = self.torch
+        for _ in range(warmup):
+            g.launch(self.stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(launches):
+            g.launch(self.stream)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / launches      # us per launch
+
+    def time_eager(self, iters, warmup=3):
+        torch = self.torch
+        for _ in range(warmup):
+            self.enqueue()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(iters):
+            self.enqueue()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / iters
+
+    def phase_us(self, phase, reps=50, launches=10):
+        """Average duration of one launch of a phase: a graph of `reps`
+        back-to-back launches, replayed `launches` times, timed with events."""
+        g = self.capture(phase, reps)
+        us = self.time_graph(g, launches) / reps
+        g.destroy()
+        return us
+
+
+def cpu_baseline(wl, d, N, min_seconds):
+    """The oracle as it stands (single-threaded C), full steps of the same
+    workload on the host, repeated until min_seconds have elapsed."""
+    import oracle
+    bytes_step = algo_bytes(wl, N)["step"]
+    n, t0 = 0, time.perf_counter()
+    while True:
+        lo = oracle.layout(d["idx"], wl.E, wl.P)
+        if wl.payload == "fp8":
+            oracle.dispatch_fp8(d["x"], lo["row_of_pair"], wl.K)
+        else:
+            oracle.dispatch_bf16(d["x"], lo["row_of_pair"], wl.K)
+        oracle.combine(d["y"], lo["row_of_pair"], d["w"], wl.T, wl.H, wl.K)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds and n >= 2:
+            break
+    per = el / n
+    return {"value": round(bytes_step / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full steps (layout+dispatch+combine) of %s, %.1f ms/step" % (n, wl.name, per * 1e3)}
+
+
+def measure(wl, steps, warmup, graph=True):
+    p = Path(wl)
+    b = algo_bytes(wl, p.N)
+    torch = p.torch
+    if graph:
+        g = p.capture("step")
+        for _ in range(warmup):
+            g.launch(p.stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(p.stream)
+        for _ in range(steps):
+            g.launch(p.stream)
+        e1.record(p.stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        g.destroy()
+    else:
+        us = p.time_eager(steps, warmup)
+    return p, b, us
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="ll_128x7168")
+    ap.add_argument("--eager", action="store_true", help="time host-launched steps, no graph")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-targets", action="store_true")
+    ap.add_argument("--only", choices=["layout", "dispatch", "combine", "step"],
+                    help="profiling mode: launch only this phase (eagerly) steps times, print nothing else")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="profiling mode: first run one device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the EP traffic; runs on more than one GPU "
+              "are not part of this build (asked for --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from workloads import WORKLOADS
+    wl = WORKLOADS[args.workload]
+
+    if args.only or args.calib_copy_mib:
+        if args.calib_copy_mib:
+            n = args.calib_copy_mib << 20
+            src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            print("calib copy %d bytes" % n, flush=True)
+        if args.only:
+            p = Path(wl)
+            p.enqueue("step")
+            torch.cuda.synchronize()
+            for _ in range(args.warmup + args.steps):
+                p.enqueue(args.only)
+            torch.cuda.synchronize()
+            print("profiled %s x%d on %s" % (args.only, args.warmup + args.steps, wl.name), flush=True)
+        return
+
+    p, b, us = measure(wl, args.steps, args.warmup, graph=not args.eager)
+    eager_us = p.time_eager(200)
+    phases = {ph: p.phase_us(ph) for ph in ("layout", "dispatch", "combine")}
+    dom = max(("dispatch", "combine"), key=lambda ph: phases[ph])
+    achieved = b[dom] / (phases[dom] * 1e-6) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_launch": b[dom], "us_per_launch": round(phases[dom], 3)}
+    value = b["step"] / (us * 1e-6) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
+        "us_per_step": round(us, 3),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "payload": "fp8_e4m3fn+fp32 per-128 scales dispatch, bf16 combine" if wl.payload == "fp8"
+        else "bf16 dispatch, bf16 combine",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.H, "experts": wl.E,
+                   "partitions": wl.P, "topk": wl.K, "valid_pairs": p.N,
+                   "timing": "eager" if args.eager else "hipgraph replay of one step",
+                   "parallelism": "single GPU (partitions stand in for EP ranks)"},
+        "bytes_per_step": b["step"],
+        "phases_us": {k: round(v, 3) for k, v in phases.items()},
+        "eager_us_per_step": round(eager_us, 3),
+        "roofline": roof,
+    }
+
+    if not args.no_targets:
+        tg = {}
+        pw, bw_, us4 = measure(WORKLOADS["sweep_4x6144"], 2000, 50)
+        tg["sweep_4x6144_us_per_step_graph"] = round(us4, 3)
+        tg["sweep_4x6144_target_us"] = 15.0
+        del pw
+        pb, bb, usb = measure(WORKLOADS["bw_4096x7168_zipf"], 50, 5)
+        tg["bw_4096x7168_zipf_us_per_step"] = round(usb, 2)
+        tg["bw_4096x7168_zipf_hbm_frac"] = round(bb["step"] / (usb * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        tg["bw_4096x7168_zipf_target_frac"] = 0.60
+        tg["bw_4096x7168_zipf_phases_us"] = {ph: round(pb.phase_us(ph, reps=10, launches=3), 2)
+                                            for ph in ("layout", "dispatch", "combine")}
+        del pb
+        res["targets"] = tg
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, p.d, p.N, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

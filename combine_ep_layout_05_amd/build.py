@@ -1,0 +1,48 @@
+"""Builds libep_mi355x.so, the HIP library behind include/ep.h, for gfx950.
+
+hipcc, -O3, one shared object from every .hip file under csrc/.  Device code
+is compiled without FP contraction (every fused multiply-add is written as
+one) and without packed-fp32 instructions.
+"""
+import glob
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libep_mi355x.so")
+ARCH = os.environ.get("EP_OFFLOAD_ARCH", "gfx950")
+
+FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-mcode-object-version=5",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["hipcc", *FLAGS, *extra_flags, *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 feature and says so; that is harmless
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + msg)
+    if verbose and msg.strip():
+        print(msg)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

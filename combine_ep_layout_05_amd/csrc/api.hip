@@ -1,0 +1,137 @@
+// api.hip -- the C entry points declared in include/ep.h: argument checks,
+// launches, error reporting and HIP graph capture helpers.
+//
+// Every check runs on the host before anything is enqueued, so a rejected
+// call leaves the stream untouched (configuration errors are refused early
+// and loudly, as the tuning CLI of MoRI PR #614 "perf(ep): InterNodeV1LL
+// low-token latency on MI300X + CX7" does for its environment knobs).
+#include "../../include/ep.h"
+#include "ep_device.h"
+#include "ep_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool ptr_ok(const void* p, uintptr_t a) { return p != nullptr && aligned(p, a); }
+
+int from_hip(hipError_t e)
+{
+    if (e == hipSuccess) return EP_OK;
+    g_last_hip_error = (int)e;
+    return EP_EHIP;
+}
+
+bool routing_ok(int T, int K)
+{
+    return T >= 0 && K >= 1 && K <= EP_MAX_TOPK && (int64_t)T * K < ((int64_t)1 << 31);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ep_layout_workspace_bytes(int T, int K, int E)
+{
+    if (!routing_ok(T, K) || E < 1 || E > EP_MAX_EXPERTS) return 0;
+    return ep::layout_workspace_bytes(T, K, E);
+}
+
+int ep_layout(const int32_t* topk_idx, int T, int K, int E, int P,
+              int32_t* expert_count, int32_t* expert_offset, int32_t* part_count,
+              int32_t* part_offset, int32_t* row_of_pair, int32_t* src_pair, uint32_t* status,
+              void* ws, size_t ws_bytes, void* stream)
+{
+    if (!routing_ok(T, K) || E < 1 || E > EP_MAX_EXPERTS || P < 1 || E % P != 0) return EP_EINVAL;
+    if (!ptr_ok(expert_count, 4) || !ptr_ok(expert_offset, 4) || !ptr_ok(part_count, 4) ||
+        !ptr_ok(part_offset, 4) || !ptr_ok(status, 4))
+        return EP_EINVAL;
+    if (T > 0 && (!ptr_ok(topk_idx, 4) || !ptr_ok(row_of_pair, 4) || !ptr_ok(src_pair, 4)))
+        return EP_EINVAL;
+    const size_t need = ep::layout_workspace_bytes(T, K, E);
+    if (need > 0 && (ws_bytes < need || !ptr_ok(ws, 16))) return EP_EINVAL;
+    return from_hip(ep::launch_layout(topk_idx, T, K, E, P, expert_count, expert_offset, part_count,
+                                      part_offset, row_of_pair, src_pair, status, ws,
+                                      (hipStream_t)stream));
+}
+
+int ep_dispatch(const uint16_t* x, int T, int H, int K, const int32_t* row_of_pair, int payload,
+                void* recv_x, float* recv_scales, void* stream)
+{
+    if (payload != EP_PAYLOAD_FP8_E4M3FN && payload != EP_PAYLOAD_BF16) return EP_ENOTSUP;
+    if (!routing_ok(T, K) || H <= 0) return EP_EINVAL;
+    if (payload == EP_PAYLOAD_FP8_E4M3FN && H % ep::kScaleBlock != 0) return EP_EINVAL;
+    if (payload == EP_PAYLOAD_BF16 && H % ep::kColsPerLane != 0) return EP_EINVAL;
+    if (T == 0) return EP_OK;
+    if (!ptr_ok(x, 16) || !ptr_ok(row_of_pair, 4) || !ptr_ok(recv_x, 16)) return EP_EINVAL;
+    if (payload == EP_PAYLOAD_FP8_E4M3FN && !ptr_ok(recv_scales, 4)) return EP_EINVAL;
+    return from_hip(ep::launch_dispatch(x, T, H, K, row_of_pair, payload, recv_x, recv_scales,
+                                        (hipStream_t)stream));
+}
+
+int ep_combine(const uint16_t* expert_out, const int32_t* row_of_pair, const float* topk_w, int T,
+               int H, int K, uint16_t* out, void* stream)
+{
+    if (!routing_ok(T, K) || H <= 0 || H % ep::kColsPerLane != 0) return EP_EINVAL;
+    if (T == 0) return EP_OK;
+    if (!ptr_ok(expert_out, 16) || !ptr_ok(row_of_pair, 4) || !ptr_ok(topk_w, 4) || !ptr_ok(out, 16))
+        return EP_EINVAL;
+    return from_hip(ep::launch_combine(expert_out, row_of_pair, topk_w, T, H, K, out,
+                                       (hipStream_t)stream));
+}
+
+int ep_e4m3fn_encode(const float* in, int64_t n, uint8_t* out, void* stream)
+{
+    if (n < 0) return EP_EINVAL;
+    if (n == 0) return EP_OK;
+    if (!ptr_ok(in, 4) || out == nullptr) return EP_EINVAL;
+    return from_hip(ep::launch_e4m3fn_encode(in, n, out, (hipStream_t)stream));
+}
+
+int ep_graph_begin(void* stream)
+{
+    if (stream == nullptr) return EP_EINVAL;
+    return from_hip(hipStreamBeginCapture((hipStream_t)stream, hipStreamCaptureModeThreadLocal));
+}
+
+int ep_graph_end(void* stream, void** graph)
+{
+    if (stream == nullptr || graph == nullptr) return EP_EINVAL;
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture((hipStream_t)stream, &g);
+    if (e != hipSuccess) return from_hip(e);
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess) return from_hip(e);
+    *graph = (void*)exec;
+    return EP_OK;
+}
+
+int ep_graph_launch(void* graph, void* stream)
+{
+    if (graph == nullptr) return EP_EINVAL;
+    return from_hip(hipGraphLaunch((hipGraphExec_t)graph, (hipStream_t)stream));
+}
+
+int ep_graph_destroy(void* graph)
+{
+    if (graph == nullptr) return EP_EINVAL;
+    return from_hip(hipGraphExecDestroy((hipGraphExec_t)graph));
+}
+
+const char* ep_strerror(int code)
+{
+    switch (code) {
+    case EP_OK: return "ok";
+    case EP_EINVAL: return "invalid argument (size, divisibility, null or misaligned pointer, workspace)";
+    case EP_ENOTSUP: return "unsupported payload";
+    case EP_EHIP: return "HIP launch failed (see ep_last_hip_error)";
+    default: return "unknown ep error code";
+    }
+}
+
+int ep_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

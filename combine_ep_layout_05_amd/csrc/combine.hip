@@ -1,0 +1,105 @@
+// combine.hip -- gather each token's top-k expert outputs and reduce them in
+// fp32 with the top-k weights, written out as bf16 (gfx950).
+//
+// out[t, c] = bf16_rne(acc); acc = 0.0f, then for k = 0..K-1 with
+// r = row_of_pair[t*K+k] >= 0: acc = fmaf(w[t,k], y[r, c], acc).
+// The expert outputs y are read in place from the caller's buffer, in the
+// receive-row layout of the dispatch (MoRI PR #614 "perf(ep): InterNodeV1LL
+// low-token latency on MI300X + CX7", zero-copy combine paragraph: no
+// staging copy of the combine input).
+//
+// Work split: one wave per (token, 512-column step), items strided flatly
+// over the whole grid -- partitioning by (token, hidden slice) rather than by
+// token keeps every wave busy at small token counts (same PR, CombineSync
+// paragraph), and 512 columns per wave is the floor the same PR measured
+// best (MultiWarpIter paragraph).  Each lane owns 8 columns: it issues all of
+// its K 16-byte loads (one per expert row, each wave-wide load a contiguous
+// 1 KB) before the first FMA so the K rows are in flight together, then
+// accumulates in k order and stores 16 bytes of bf16.
+#include "ep_device.h"
+#include "ep_launch.h"
+#include "ep_numerics.h"
+
+namespace ep {
+namespace {
+
+template <int kMaxK>
+__global__ __launch_bounds__(kMoveThreads) void combine_kernel(
+    const uint16_t* __restrict__ y, const int32_t* __restrict__ row_of_pair,
+    const float* __restrict__ topk_w, int H, int K, uint16_t* __restrict__ out,
+    int steps_per_token, int n_items, int n_rows)
+{
+    const int lane = threadIdx.x % kWave;
+    const int stride = gridDim.x * kMoveWaves;
+    for (int item = blockIdx.x * kMoveWaves + wave_uniform(threadIdx.x / kWave); item < n_items;
+         item += stride) {                   // n_items + stride < 2^31 (checked by the launcher)
+        const int t = item / steps_per_token;
+        const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
+        const bool active = col0 < H;
+        int myrow = (lane < K) ? row_of_pair[(int64_t)t * K + lane] : -1;
+        if (myrow >= n_rows) myrow = -1;     // not a receive row: treated as masked
+        const float myw = (lane < K) ? topk_w[(int64_t)t * K + lane] : 0.0f;
+
+        uint4 v[kMaxK];
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) {
+            v[k] = make_uint4(0, 0, 0, 0);
+            if (k < K) {
+                const int r = read_lane(myrow, k);
+                if (r >= 0 && active) v[k] = *reinterpret_cast<const uint4*>(y + (int64_t)r * H + col0);
+            }
+        }
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) {
+            if (k < K) {
+                const int r = read_lane(myrow, k);
+                if (r >= 0) {
+                    const float wk = __builtin_bit_cast(float, read_lane(__builtin_bit_cast(int, myw), k));
+                    acc[0] = __builtin_fmaf(wk, bf16_lo(v[k].x), acc[0]);
+                    acc[1] = __builtin_fmaf(wk, bf16_hi(v[k].x), acc[1]);
+                    acc[2] = __builtin_fmaf(wk, bf16_lo(v[k].y), acc[2]);
+                    acc[3] = __builtin_fmaf(wk, bf16_hi(v[k].y), acc[3]);
+                    acc[4] = __builtin_fmaf(wk, bf16_lo(v[k].z), acc[4]);
+                    acc[5] = __builtin_fmaf(wk, bf16_hi(v[k].z), acc[5]);
+                    acc[6] = __builtin_fmaf(wk, bf16_lo(v[k].w), acc[6]);
+                    acc[7] = __builtin_fmaf(wk, bf16_hi(v[k].w), acc[7]);
+                }
+            }
+        }
+        if (active) {
+            uint4 o;
+            o.x = pack2_bf16(acc[0], acc[1]);
+            o.y = pack2_bf16(acc[2], acc[3]);
+            o.z = pack2_bf16(acc[4], acc[5]);
+            o.w = pack2_bf16(acc[6], acc[7]);
+            *reinterpret_cast<uint4*>(out + (int64_t)t * H + col0) = o;
+        }
+    }
+}
+
+constexpr int64_t kMaxGridBlocks = 1 << 20;
+
+}  // namespace
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* row_of_pair, const float* topk_w,
+                          int T, int H, int K, uint16_t* out, hipStream_t stream)
+{
+    const int steps = (H + kStepCols - 1) / kStepCols;
+    const int64_t items = (int64_t)T * steps;
+    if (items == 0) return hipSuccess;
+    if (items + kMaxGridBlocks * kMoveWaves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
+    if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
+    if (K <= 8)
+        hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)blocks), dim3(kMoveThreads), 0, stream,
+                           y, row_of_pair, topk_w, H, K, out, steps, (int)items, T * K);
+    else
+        hipLaunchKernelGGL(combine_kernel<16>, dim3((unsigned)blocks), dim3(kMoveThreads), 0, stream,
+                           y, row_of_pair, topk_w, H, K, out, steps, (int)items, T * K);
+    return hipGetLastError();
+}
+
+}  // namespace ep

@@ -1,0 +1,55 @@
+// ep_device.h -- constants and wave-level device helpers shared by the
+// layout, dispatch and combine kernels (gfx950, wave64).
+//
+// One source of truth for every size the host launch code and the kernels
+// both depend on: block shapes, the single-workgroup layout limit, the chunk
+// size of the multi-workgroup layout and the column span one wave covers per
+// step.  The sources show what goes wrong when a host-side buffer count and a
+// device-side constant are defined apart (DeepEP PR #693, review comments on
+// the staging-buffer count); here both sides include this header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+constexpr int kWave = 64;                  // gfx950 wavefront width
+
+// ---- layout ---------------------------------------------------------------
+constexpr int kLayoutThreads = 1024;       // one pair per thread per round
+constexpr int kLayoutWaves = kLayoutThreads / kWave;
+constexpr int kMaxExperts = 1024;          // one expert column per thread
+constexpr int kSmallMaxPairs = 4096;       // single-workgroup layout up to this
+constexpr int kChunkPairs = 2048;          // pairs per workgroup above it
+static_assert(kMaxExperts <= kLayoutThreads, "scan assigns one expert per thread");
+static_assert(kChunkPairs % kLayoutThreads == 0, "a chunk is whole rounds");
+static_assert(kLayoutWaves * kWave <= 0xFFFF, "per-wave counts fit in uint16");
+
+// ---- dispatch / combine ---------------------------------------------------
+constexpr int kMoveThreads = 256;          // 4 waves per workgroup
+constexpr int kMoveWaves = kMoveThreads / kWave;
+constexpr int kColsPerLane = 8;            // 16 B of bf16 per lane per step
+constexpr int kStepCols = kWave * kColsPerLane;   // 512 columns per wave step
+constexpr int kScaleBlock = 128;           // columns per fp8 scale
+constexpr int kLanesPerScaleBlock = kScaleBlock / kColsPerLane;   // 16 = one DPP row
+static_assert(kLanesPerScaleBlock == 16, "a scale block must be one 16-lane DPP row");
+
+// Bits of v strictly below this lane set in `mask` (wave64).
+__device__ __forceinline__ int lanes_below(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ int wave_uniform(int v)
+{
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ int read_lane(int v, int lane)
+{
+    return __builtin_amdgcn_readlane(v, lane);
+}
+
+}  // namespace ep

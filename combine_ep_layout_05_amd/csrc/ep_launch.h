@@ -1,0 +1,31 @@
+// ep_launch.h -- host-side launchers of the kernels (one per .hip file).
+// Arguments are validated by the C entry points before these are called;
+// each returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+size_t layout_workspace_bytes(int T, int K, int E);
+
+hipError_t launch_layout(const int32_t* topk_idx, int T, int K, int E, int P,
+                         int32_t* expert_count, int32_t* expert_offset,
+                         int32_t* part_count, int32_t* part_offset,
+                         int32_t* row_of_pair, int32_t* src_pair, uint32_t* status,
+                         void* ws, hipStream_t stream);
+
+hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K,
+                           const int32_t* row_of_pair, int payload,
+                           void* recv_x, float* recv_scales, hipStream_t stream);
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* row_of_pair,
+                          const float* topk_w, int T, int H, int K,
+                          uint16_t* out, hipStream_t stream);
+
+hipError_t launch_e4m3fn_encode(const float* in, int64_t n, uint8_t* out,
+                                hipStream_t stream);
+
+}  // namespace ep

@@ -1,0 +1,353 @@
+// layout.hip -- per-expert / per-destination counts, exclusive scans and
+// deterministic receive slots for MoE expert-parallel dispatch (gfx950).
+//
+// What is computed (UCCL PR #749 "[EP] Low-latency mode batch tokens per
+// destination": a destination's batch is the sum of its local experts'
+// counts; MoRI PR #614 "perf(ep): InterNodeV1LL low-token latency on MI300X +
+// CX7", DispatchIntraNode paragraph: work items are the flat (t, k) entries
+// t*K + i; routing-scan paragraph: negative ids are sentinels):
+//   count[e], offset = exclusive scan of count, part_count[p] = sum of count
+//   over experts p*L .. p*L+L-1, part_offset[p] = offset[p*L], and for every
+//   valid entry row = offset[e] + (number of earlier entries, in flat (t, k)
+//   order, with the same expert).
+//
+// The pages' systems learn each destination's size by spinning on
+// per-expert completion counters and claim slots with atomics, which makes
+// the slot order depend on timing.  Here the counts are known before any
+// payload moves and slots come from prefix sums only:
+//   - in-wave rank: the lanes holding the same expert ("peers") are found
+//     with one ballot per bit of the expert id (match-any); a lane's rank is
+//     the number of its peers in lower lanes (mbcnt), the lowest peer is the
+//     group leader;
+//   - across the 16 waves of a round: each leader writes its group size to
+//     an LDS table [wave][expert]; one thread per expert turns its column
+//     into an exclusive prefix over waves;
+//   - across rounds: a running per-expert cursor in LDS;
+//   - across workgroups (large batches): per-chunk histograms in the
+//     workspace, scanned over chunks by a second kernel, and a third kernel
+//     adds the chunk base to the in-chunk rank.
+// No atomic's return value ever decides a slot, so the result is the same on
+// every run.  LDS atomics are used only for order-free histogram sums.
+#include "ep_device.h"
+#include "ep_launch.h"
+
+namespace ep {
+namespace {
+
+struct LayoutSmem {
+    int32_t hist[kMaxExperts];
+    int32_t cursor[kMaxExperts];
+    uint16_t wtab[kLayoutWaves][kMaxExperts];   // per-wave group sizes / prefixes
+    int32_t wsum[kLayoutWaves];
+    uint32_t bad;
+    int32_t total;
+};
+
+__device__ __forceinline__ int id_bits(int E)
+{
+    // bits needed to tell apart ids 0..E-1
+    return E <= 1 ? 0 : 32 - __builtin_clz((unsigned)(E - 1));
+}
+
+// Lanes of this wave whose valid expert id equals this lane's (0 if invalid).
+// Must be called by all 64 lanes (ballots).
+__device__ __forceinline__ uint64_t match_peers(int e, bool valid, int nbits)
+{
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    return valid ? peers : 0ull;
+}
+
+__device__ __forceinline__ void zero_smem(LayoutSmem& s, int E)
+{
+    const int tid = threadIdx.x;
+    if (tid < E) {
+        s.hist[tid] = 0;
+        s.cursor[tid] = 0;
+        for (int w = 0; w < kLayoutWaves; ++w) s.wtab[w][tid] = 0;
+    }
+    if (tid == 0) s.bad = 0u;
+}
+
+// Rank one round of kLayoutThreads pairs [base, base + kLayoutThreads) of the
+// flat entry array (entries >= n are padding).  On entry s.cursor[e] is the
+// first free row of expert e; on exit it has moved past this round's entries.
+// Writes row_of_pair for every real entry (-1 when masked) and src_pair for
+// valid ones when src_pair is non-null.
+__device__ void rank_round(const int32_t* __restrict__ idx, int64_t base, int64_t n,
+                           int E, int nbits, LayoutSmem& s,
+                           int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair)
+{
+    const int tid = threadIdx.x;
+    const int w = tid / kWave;
+    const int64_t p = base + tid;
+    const int e = (p < n) ? idx[p] : -1;
+    const bool valid = (e >= 0) && (e < E);
+    if (p < n && e >= E) s.bad = 1u;           // benign race: every writer stores 1
+
+    const uint64_t peers = match_peers(e, valid, nbits);
+    const int rank = lanes_below(peers);
+    if (valid && rank == 0) s.wtab[w][e] = (uint16_t)__popcll(peers);
+    __syncthreads();
+
+    int run = 0;
+    if (tid < E) {
+        for (int v = 0; v < kLayoutWaves; ++v) {
+            const int c = s.wtab[v][tid];
+            s.wtab[v][tid] = (uint16_t)run;
+            run += c;
+        }
+    }
+    __syncthreads();
+
+    if (p < n) {
+        int row = -1;
+        if (valid) {
+            row = s.cursor[e] + (int)s.wtab[w][e] + rank;
+            if (src_pair && row < n) src_pair[row] = (int32_t)p;
+        }
+        row_of_pair[p] = row;
+    }
+    __syncthreads();
+
+    if (tid < E) {
+        s.cursor[tid] += run;
+        for (int v = 0; v < kLayoutWaves; ++v) s.wtab[v][tid] = 0;
+    }
+    __syncthreads();
+}
+
+// Exclusive scan of one value per thread over the whole workgroup; *total
+// receives the sum.  Contains barriers: all threads must call it.
+__device__ int block_exclusive_scan(int v, LayoutSmem& s, int* total)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, w = tid / kWave;
+    int x = v;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+    }
+    if (lane == kWave - 1) s.wsum[w] = x;
+    __syncthreads();
+    if (w == 0) {
+        int t = lane < kLayoutWaves ? s.wsum[lane] : 0;
+        for (int d = 1; d < kLayoutWaves; d <<= 1) {
+            const int y = __shfl_up(t, d, kWave);
+            if (lane >= d) t += y;
+        }
+        if (lane < kLayoutWaves) s.wsum[lane] = t;   // inclusive prefix of wave sums
+    }
+    __syncthreads();
+    const int before = (w > 0) ? s.wsum[w - 1] : 0;
+    *total = s.wsum[kLayoutWaves - 1];
+    __syncthreads();
+    return before + x - v;
+}
+
+// From per-expert counts (one per thread, tid < E): write expert_count,
+// expert_offset, part_count, part_offset and status; leave the exclusive
+// offsets in s.cursor and N in s.total.
+__device__ void finish_counts(int count, int E, int P, uint32_t bad, LayoutSmem& s,
+                              int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+                              int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
+                              uint32_t* __restrict__ status)
+{
+    const int tid = threadIdx.x;
+    int N = 0;
+    const int off = block_exclusive_scan(tid < E ? count : 0, s, &N);
+    if (tid < E) {
+        s.cursor[tid] = off;
+        expert_count[tid] = count;
+        expert_offset[tid] = off;
+    }
+    if (tid == 0) {
+        expert_offset[E] = N;
+        s.total = N;
+        *status = bad ? 1u : 0u;
+    }
+    __syncthreads();
+    const int L = E / P;
+    if (tid < P) {
+        const int lo = s.cursor[tid * L];
+        const int hi = (tid + 1 < P) ? s.cursor[(tid + 1) * L] : N;
+        part_offset[tid] = lo;
+        part_count[tid] = hi - lo;
+    }
+    if (tid == 0) part_offset[P] = N;
+}
+
+// ---------------------------------------------------------------------------
+// Small batches (T*K <= kSmallMaxPairs): one workgroup does everything.
+__global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
+    const int32_t* __restrict__ idx, int64_t n, int E, int P,
+    int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
+    int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair,
+    uint32_t* __restrict__ status)
+{
+    __shared__ LayoutSmem s;
+    const int tid = threadIdx.x;
+    const int nbits = id_bits(E);
+    zero_smem(s, E);
+    __syncthreads();
+
+    // pass 1: histogram (order-free sums; one LDS atomic per peer group)
+    for (int64_t base = 0; base < n; base += kLayoutThreads) {
+        const int64_t p = base + tid;
+        const int e = (p < n) ? idx[p] : -1;
+        const bool valid = (e >= 0) && (e < E);
+        if (p < n && e >= E) s.bad = 1u;
+        const uint64_t peers = match_peers(e, valid, nbits);
+        if (valid && lanes_below(peers) == 0) atomicAdd(&s.hist[e], (int)__popcll(peers));
+    }
+    __syncthreads();
+
+    finish_counts(tid < E ? s.hist[tid] : 0, E, P, s.bad, s, expert_count, expert_offset,
+                  part_count, part_offset, status);
+    __syncthreads();
+
+    // pass 2: deterministic slots
+    for (int64_t base = 0; base < n; base += kLayoutThreads)
+        rank_round(idx, base, n, E, nbits, s, row_of_pair, src_pair);
+
+    for (int64_t r = (int64_t)s.total + tid; r < n; r += kLayoutThreads) src_pair[r] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// Large batches, step 1: one workgroup per chunk of kChunkPairs entries.
+// Writes the in-chunk rank into row_of_pair (-1 when masked), the chunk's
+// histogram into ws_hist[chunk][E] and a bad-id flag into ws_bad[chunk].
+__global__ __launch_bounds__(kLayoutThreads) void layout_chunk_kernel(
+    const int32_t* __restrict__ idx, int64_t n, int E,
+    int32_t* __restrict__ row_of_pair, int32_t* __restrict__ ws_hist,
+    uint32_t* __restrict__ ws_bad)
+{
+    __shared__ LayoutSmem s;
+    const int tid = threadIdx.x;
+    const int chunk = blockIdx.x;
+    const int nbits = id_bits(E);
+    zero_smem(s, E);
+    __syncthreads();
+    const int64_t c0 = (int64_t)chunk * kChunkPairs;
+    const int64_t c1 = (c0 + kChunkPairs < n) ? c0 + kChunkPairs : n;
+    for (int64_t base = c0; base < c1; base += kLayoutThreads)
+        rank_round(idx, base, c1, E, nbits, s, row_of_pair, nullptr);
+    if (tid < E) ws_hist[(int64_t)chunk * E + tid] = s.cursor[tid];
+    if (tid == 0) ws_bad[chunk] = s.bad;
+}
+
+// Large batches, step 2: one workgroup.  Totals per expert over chunks, the
+// exclusive scans and partition sums, then each chunk's base row per expert
+// (offset[e] + rows of expert e in earlier chunks) written back over ws_hist.
+constexpr int kScanBatch = 16;
+
+__global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(
+    int nchunks, int E, int P, int32_t* __restrict__ ws_hist,
+    const uint32_t* __restrict__ ws_bad,
+    int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
+    uint32_t* __restrict__ status)
+{
+    __shared__ LayoutSmem s;
+    const int tid = threadIdx.x;
+    if (tid == 0) s.bad = 0u;
+    __syncthreads();
+    uint32_t b = 0;
+    for (int c = tid; c < nchunks; c += kLayoutThreads) b |= ws_bad[c];
+    if (b) s.bad = 1u;
+
+    // exclusive prefix over chunks, per expert (loads batched so they overlap)
+    int run = 0;
+    if (tid < E) {
+        for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+            int h[kScanBatch];
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j)
+                h[j] = (c0 + j < nchunks) ? ws_hist[(int64_t)(c0 + j) * E + tid] : 0;
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j) {
+                if (c0 + j < nchunks) ws_hist[(int64_t)(c0 + j) * E + tid] = run;
+                run += h[j];
+            }
+        }
+    }
+    __syncthreads();
+    finish_counts(run, E, P, s.bad, s, expert_count, expert_offset, part_count, part_offset,
+                  status);
+    __syncthreads();
+    if (tid < E) {
+        const int off = s.cursor[tid];
+        for (int c = 0; c < nchunks; ++c) ws_hist[(int64_t)c * E + tid] += off;
+    }
+}
+
+// Large batches, step 3: row = chunk base of the entry's expert + in-chunk
+// rank; src_pair is the inverse map, -1 past N.
+__global__ __launch_bounds__(256) void layout_finalize_kernel(
+    const int32_t* __restrict__ idx, int64_t n, int E,
+    const int32_t* __restrict__ ws_base, const int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t p = g; p < n; p += stride) {
+        const int e = idx[p];
+        if (e >= 0 && e < E) {
+            const int row = ws_base[(p / kChunkPairs) * E + e] + row_of_pair[p];
+            row_of_pair[p] = row;
+            if (row >= 0 && row < n) src_pair[row] = (int32_t)p;
+        }
+    }
+    const int64_t N = expert_offset[E];
+    for (int64_t r = N + g; r < n; r += stride) src_pair[r] = -1;
+}
+
+int64_t num_chunks(int64_t n) { return (n + kChunkPairs - 1) / kChunkPairs; }
+
+}  // namespace
+
+size_t layout_workspace_bytes(int T, int K, int E)
+{
+    const int64_t n = (int64_t)T * K;
+    if (n <= kSmallMaxPairs) return 0;
+    const int64_t c = num_chunks(n);
+    const size_t hist = (size_t)c * E * sizeof(int32_t);
+    const size_t hist_padded = (hist + 255) & ~(size_t)255;
+    return hist_padded + (size_t)c * sizeof(uint32_t);
+}
+
+hipError_t launch_layout(const int32_t* idx, int T, int K, int E, int P,
+                         int32_t* expert_count, int32_t* expert_offset,
+                         int32_t* part_count, int32_t* part_offset,
+                         int32_t* row_of_pair, int32_t* src_pair, uint32_t* status,
+                         void* ws, hipStream_t stream)
+{
+    const int64_t n = (int64_t)T * K;
+    if (n <= kSmallMaxPairs) {
+        hipLaunchKernelGGL(layout_single_kernel, dim3(1), dim3(kLayoutThreads), 0, stream,
+                           idx, n, E, P, expert_count, expert_offset, part_count, part_offset,
+                           row_of_pair, src_pair, status);
+        return hipGetLastError();
+    }
+    const int64_t c = num_chunks(n);
+    const size_t hist = (size_t)c * E * sizeof(int32_t);
+    int32_t* ws_hist = (int32_t*)ws;
+    uint32_t* ws_bad = (uint32_t*)((char*)ws + ((hist + 255) & ~(size_t)255));
+    hipLaunchKernelGGL(layout_chunk_kernel, dim3((unsigned)c), dim3(kLayoutThreads), 0, stream,
+                       idx, n, E, row_of_pair, ws_hist, ws_bad);
+    hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kLayoutThreads), 0, stream,
+                       (int)c, E, P, ws_hist, ws_bad, expert_count, expert_offset, part_count,
+                       part_offset, status);
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(layout_finalize_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048)),
+                       dim3(256), 0, stream, idx, n, E, ws_hist, expert_offset, row_of_pair,
+                       src_pair);
+    return hipGetLastError();
+}
+
+}  // namespace ep

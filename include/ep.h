@@ -1,0 +1,189 @@
+/*
+ * ep.h -- C ABI of the MI355X (gfx950) MoE expert-parallel low-latency
+ * layout / dispatch / combine library (libep_mi355x.so).
+ *
+ * One GPU's share of the expert-parallel traffic: the P destination "ranks"
+ * of an EP group are P contiguous partitions of the receive buffers in this
+ * GPU's HBM.  The method:
+ *   - layout: count tokens per expert and per destination before any
+ *     payload moves, then give every (token, k) entry a slot.  The sources
+ *     show the cost of learning a destination's batch size by waiting on
+ *     per-expert completion counters (UCCL PR #749 "[EP] Low-latency mode
+ *     batch tokens per destination", review comment); here the counts come
+ *     from a histogram and an exclusive scan, and slots are deterministic;
+ *   - dispatch: each token's hidden vector, quantised to fp8 with one scale
+ *     per 128 columns, is written to the receive row of each of its top-k
+ *     experts (DeepEP PR #693 "Pipeline direct NVLink dispatch with
+ *     triple-buffered prefetch", Summary: a token carries hidden data, scale
+ *     factors and routing); a bf16 passthrough mode copies the row as is;
+ *   - combine: each token gathers its top-k expert outputs, reads straight
+ *     from the caller's buffer (MoRI PR #614 "perf(ep): InterNodeV1LL
+ *     low-token latency on MI300X + CX7", zero-copy combine paragraph), and
+ *     reduces them in fp32 with the top-k weights, written out as bf16.
+ *
+ * Conventions (all entry points):
+ *   - Device pointers unless stated.  The caller owns every buffer; the
+ *     library allocates nothing, keeps no pointer after a call returns and
+ *     holds no global state, so calls on different streams are independent.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work; none synchronises the host.  Buffers must stay
+ *     alive until the stream has run the work.
+ *   - Return 0 on success.  A negative code means a host-side check failed
+ *     and NOTHING was enqueued: EP_EINVAL (bad argument), EP_ENOTSUP
+ *     (unsupported payload), EP_EHIP (a HIP launch failed; see
+ *     ep_last_hip_error()).
+ *   - Every call can be captured into a HIP graph: no call allocates,
+ *     memsets or synchronises; counters the kernels need are cleared by
+ *     the kernels themselves.
+ *
+ * Notation: T tokens, H hidden size, K top-k (1..16), E experts (1..1024),
+ * P partitions (E % P == 0), L = E / P experts per partition, expert e
+ * belongs to partition e / L (UCCL PR #749 review excerpt: a rank owns a
+ * contiguous block of experts).  A "pair" is a (t, k) entry, flat index
+ * t*K + k.  N = number of valid pairs (0 <= id < E).
+ */
+#ifndef EP_MI355X_H
+#define EP_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EP_OK 0
+#define EP_EINVAL (-1)
+#define EP_ENOTSUP (-2)
+#define EP_EHIP (-3)
+
+#define EP_PAYLOAD_FP8_E4M3FN 0   /* OCP e4m3fn bytes + fp32 scale per 128 columns */
+#define EP_PAYLOAD_BF16 1         /* bf16 passthrough, no scales */
+
+#define EP_MAX_TOPK 16
+#define EP_MAX_EXPERTS 1024
+
+/* status word bit set by ep_layout when some id >= E was seen (that entry is
+ * then treated as masked). */
+#define EP_STATUS_BAD_EXPERT_ID 1u
+
+/*
+ * Size in bytes of the workspace ep_layout needs for T tokens, top-K, E
+ * experts.  Host-only.  0 means no workspace is needed (small batches).
+ * Returns 0 as well for arguments ep_layout would reject.
+ */
+size_t ep_layout_workspace_bytes(int T, int K, int E);
+
+/*
+ * Layout: per-expert and per-destination counts, their exclusive scans and
+ * the slot of every pair.
+ *
+ *   topk_idx      int32 [T, K] row-major.  Negative = masked entry (the
+ *                 sentinel of MoRI PR #614, routing-scan paragraph); an id
+ *                 >= E sets EP_STATUS_BAD_EXPERT_ID in *status and is masked.
+ *   expert_count  int32 [E]    out: pairs routed to each expert.
+ *   expert_offset int32 [E+1]  out: exclusive scan, expert_offset[E] = N.
+ *   part_count    int32 [P]    out: pairs per destination partition (the
+ *                              batch size a sender needs, UCCL PR #749).
+ *   part_offset   int32 [P+1]  out: part_offset[p] = expert_offset[p*L],
+ *                              part_offset[P] = N.
+ *   row_of_pair   int32 [T*K]  out: receive row of pair t*K+k, -1 if masked.
+ *                              Rows of expert e are expert_offset[e] ..
+ *                              expert_offset[e+1]-1 in ascending (t, k)
+ *                              order, so the layout is deterministic and
+ *                              partition p owns rows part_offset[p] ..
+ *                              part_offset[p+1]-1.
+ *   src_pair      int32 [T*K]  out: src_pair[row] = t*K+k for row < N, -1
+ *                              for row in [N, T*K).
+ *   status        uint32 [1]   out: cleared, then EP_STATUS_* bits.
+ *   ws, ws_bytes  workspace of at least ep_layout_workspace_bytes(T,K,E)
+ *                 bytes, 16-byte aligned (may be NULL when that is 0).
+ *                 Contents need no initialisation and are scratch after the
+ *                 call; one workspace must not be shared by calls that can
+ *                 run concurrently.
+ * Errors: EP_EINVAL for T < 0, K outside 1..16, E outside 1..1024, P < 1,
+ * E % P != 0, T*K >= 2^31, NULL or misaligned (4 B; ws 16 B) pointers where
+ * T > 0 needs them (expert_count, expert_offset, part_count, part_offset and
+ * status are always needed), or ws_bytes too small.
+ */
+int ep_layout(const int32_t* topk_idx, int T, int K, int E, int P,
+              int32_t* expert_count, int32_t* expert_offset,
+              int32_t* part_count, int32_t* part_offset,
+              int32_t* row_of_pair, int32_t* src_pair, uint32_t* status,
+              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dispatch: scatter each token's hidden vector into the receive rows of its
+ * valid pairs.
+ *
+ *   x            bf16 bits [T, H], 16-byte aligned.
+ *   row_of_pair  int32 [T*K] from ep_layout.
+ *   payload      EP_PAYLOAD_FP8_E4M3FN: for every token and 128-column block,
+ *                amax = max |x| (NaN ignored), scale = amax / 448 (IEEE fp32
+ *                division), byte = e4m3fn(x / scale) (IEEE fp32 division,
+ *                round to nearest even, saturating at +-448, NaN -> 0x7F|sign,
+ *                sign kept on zero); amax = 0 gives scale 0 and zero bytes.
+ *                recv_x is uint8 [T*K, H] and recv_scales fp32 [T*K, H/128],
+ *                both row-major; H % 128 == 0.
+ *                EP_PAYLOAD_BF16: the row is copied verbatim, recv_x is bf16
+ *                [T*K, H], recv_scales is ignored (may be NULL); H % 8 == 0.
+ *   Only rows named by row_of_pair are written; every other row (masked
+ *   entries, rows >= N) is left untouched.
+ * Errors: EP_EINVAL for T < 0, H <= 0, the H divisibility above, K outside
+ * 1..16, T*K >= 2^31, NULL or misaligned pointers (x, recv_x 16 B;
+ * row_of_pair, recv_scales 4 B) when T > 0; EP_ENOTSUP for another payload.
+ */
+int ep_dispatch(const uint16_t* x, int T, int H, int K,
+                const int32_t* row_of_pair, int payload,
+                void* recv_x, float* recv_scales, void* stream);
+
+/*
+ * Combine: out[t, c] = bf16_rne(acc), acc = 0.0f, then for k = 0..K-1 with
+ * r = row_of_pair[t*K+k] >= 0: acc = fmaf(topk_w[t*K+k], y[r, c], acc)
+ * (fp32, fixed k order; masked entries are skipped, weights used as given).
+ * A token with every entry masked gives +0.  bf16 rounding is to nearest
+ * even; NaN stays NaN.
+ *
+ *   expert_out  bf16 bits y [T*K, H] in the receive-row layout of
+ *               ep_dispatch (read in place, no staging copy), 16-B aligned.
+ *   topk_w      fp32 [T, K].   out  bf16 bits [T, H], 16-B aligned.
+ * Errors: EP_EINVAL for T < 0, H <= 0 or H % 8 != 0, K outside 1..16,
+ * T*K >= 2^31, NULL or misaligned pointers when T > 0.
+ */
+int ep_combine(const uint16_t* expert_out, const int32_t* row_of_pair,
+               const float* topk_w, int T, int H, int K,
+               uint16_t* out, void* stream);
+
+/*
+ * HIP graph capture for the small-token regime, where host enqueue paces the
+ * GPU (MoRI PR #614, view-cache paragraph: at 4 tokens most of a round's
+ * wall time was host work, and stable buffers are what make the op
+ * capturable).  Between ep_graph_begin(stream) and ep_graph_end(stream, &g)
+ * every ep_* call (and any other work) enqueued on `stream` is recorded, not
+ * run; `stream` must not be the null stream.  ep_graph_launch replays the
+ * recorded work on any stream with the pointers and sizes it was recorded
+ * with.  ep_graph_destroy frees the graph (host call; the graph must not be
+ * running).  Return codes as above; *graph is set only on success.
+ */
+int ep_graph_begin(void* stream);
+int ep_graph_end(void* stream, void** graph);
+int ep_graph_launch(void* graph, void* stream);
+int ep_graph_destroy(void* graph);
+
+/*
+ * Encode n fp32 values with the same e4m3fn encoder the fp8 dispatch uses
+ * (round to nearest even, saturating, NaN -> 0x7F|sign).  in: fp32 [n],
+ * out: uint8 [n], both device pointers (4 B / 1 B aligned).  For checking
+ * the encoder against the format definition over whole ranges of inputs.
+ */
+int ep_e4m3fn_encode(const float* in, int64_t n, uint8_t* out, void* stream);
+
+/* Message for a return code; static storage. */
+const char* ep_strerror(int code);
+/* hipError_t of the last failed launch in the calling thread (0 if none). */
+int ep_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EP_MI355X_H */

@@ -1,0 +1,96 @@
+"""Runs the HIP path and the oracle on the same seeded inputs, for the tests.
+
+GPU side: the C-ABI library through its thin Python binding.  Oracle side:
+oracle/ (CPU).  The two share nothing but the inputs from workloads/.
+"""
+import numpy as np
+import torch
+
+import oracle
+
+POISON_BYTE = 0xA5
+POISON_F32_BITS = 0x7FA5A5A5          # a NaN pattern no kernel writes
+
+
+def gpu_lib():
+    import combine_ep_layout_05_amd as ep
+    return ep
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def run_gpu(wl, d, stream=None, poison=True):
+    """Layout + dispatch + combine on the GPU; returns numpy copies of every output."""
+    ep = gpu_lib()
+    buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    if poison:
+        buf.recv_x.view(torch.uint8).fill_(POISON_BYTE)
+        if buf.recv_scales is not None:
+            buf.recv_scales.view(torch.int32).fill_(POISON_F32_BITS)
+        buf.row_of_pair.fill_(-7)
+        buf.src_pair.fill_(-7)
+        buf.out.view(torch.int16).fill_(0x5A5A)
+    idx = to_dev(d["idx"])
+    x = to_dev(d["x"].view(np.int16), torch.bfloat16)
+    y = to_dev(d["y"].view(np.int16), torch.bfloat16)
+    w = to_dev(d["w"])
+    buf.layout(idx, stream)
+    buf.dispatch(x, stream)
+    buf.combine(y, w, stream)
+    torch.cuda.synchronize()
+    return collect(buf)
+
+
+def collect(buf):
+    res = {k: getattr(buf, k).cpu().numpy() for k in
+           ("expert_count", "expert_offset", "part_count", "part_offset", "row_of_pair", "src_pair")}
+    res["status"] = buf.status.cpu().numpy().view(np.uint32)
+    res["recv_x"] = buf.recv_x.view(torch.uint8).cpu().numpy() if buf.payload == "fp8" else \
+        buf.recv_x.view(torch.int16).cpu().numpy().view(np.uint16)
+    if buf.recv_scales is not None:
+        res["recv_scales"] = buf.recv_scales.cpu().numpy()
+    res["out"] = buf.out.view(torch.int16).cpu().numpy().view(np.uint16)
+    return res
+
+
+def run_oracle(wl, d):
+    lo = oracle.layout(d["idx"], wl.E, wl.P)
+    res = dict(lo)
+    if wl.payload == "fp8":
+        rx, rs = oracle.dispatch_fp8(d["x"], lo["row_of_pair"], wl.K)
+        res["recv_x"], res["recv_scales"] = rx, rs
+    else:
+        res["recv_x"] = oracle.dispatch_bf16(d["x"], lo["row_of_pair"], wl.K)
+    res["out"] = oracle.combine(d["y"], lo["row_of_pair"], d["w"], wl.T, wl.H, wl.K)
+    return res
+
+
+def compare(wl, got, ref, check_poison=True):
+    """Bit-exact for layout, fp8 bytes, scales, bf16 rows; combine within 1 bf16 ulp.
+    Returns the number of combine outputs that differ at all (expected 0)."""
+    from tests.helpers import bf16_ulp_distance
+    for k in ("expert_count", "expert_offset", "part_count", "part_offset", "row_of_pair",
+              "src_pair"):
+        np.testing.assert_array_equal(got[k], ref[k], err_msg="%s: %s" % (wl.name, k))
+    assert int(got["status"][0]) == int(ref["status"][0]), (wl.name, "status")
+    N = int(ref["expert_offset"][wl.E])
+    gx, rx = got["recv_x"], ref["recv_x"]
+    bad = np.nonzero((gx[:N] != rx[:N]).any(axis=1))[0]
+    assert bad.size == 0, "%s: recv_x rows differ, first row %d" % (wl.name, bad[0])
+    if wl.payload == "fp8":
+        gs = got["recv_scales"][:N].view(np.uint32)
+        rs = ref["recv_scales"][:N].view(np.uint32)
+        np.testing.assert_array_equal(gs, rs, err_msg="%s: recv_scales" % wl.name)
+    if check_poison:
+        tail = gx[N:].view(np.uint8)
+        assert np.all(tail == POISON_BYTE), "%s: rows >= N were written" % wl.name
+        if wl.payload == "fp8":
+            assert np.all(got["recv_scales"][N:].view(np.uint32) == POISON_F32_BITS)
+    dist = bf16_ulp_distance(got["out"], ref["out"])
+    assert dist.max(initial=0) <= 1, "%s: combine off by %d ulp" % (wl.name, dist.max())
+    return int(np.count_nonzero(dist))

@@ -1,0 +1,71 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ep_[a-z0-9_]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch  # noqa: F401  (the HIP runtime is loaded through torch first)
+    import combine_ep_layout_05_amd as ep
+    return ctypes.CDLL(ep.library_path())
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("ep_layout", "ep_dispatch", "ep_combine", "ep_layout_workspace_bytes",
+              "ep_strerror", "ep_last_hip_error", "ep_graph_begin", "ep_graph_end",
+              "ep_graph_launch", "ep_graph_destroy", "ep_e4m3fn_encode"):
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_host_side_validation(lib):
+    P = ctypes.c_void_p
+    L = lib
+    L.ep_layout.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [P] * 7 + [
+        P, ctypes.c_size_t, P]
+    L.ep_dispatch.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, P, P]
+    L.ep_combine.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+    L.ep_layout_workspace_bytes.restype = ctypes.c_size_t
+    L.ep_strerror.restype = ctypes.c_char_p
+    fake = P(0x10000)          # never dereferenced: every case below fails a host check first
+    odd = P(0x10004)
+    ws = [fake] * 7
+    # E % P != 0, K out of range, E too large, T < 0
+    assert L.ep_layout(fake, 4, 8, 30, 8, *ws, None, 0, None) == -1
+    assert L.ep_layout(fake, 4, 17, 32, 8, *ws, None, 0, None) == -1
+    assert L.ep_layout(fake, 4, 8, 2048, 8, *ws, None, 0, None) == -1
+    assert L.ep_layout(fake, -1, 8, 32, 8, *ws, None, 0, None) == -1
+    # null outputs, and a large batch without its workspace
+    assert L.ep_layout(fake, 4, 8, 32, 8, None, *ws[1:], None, 0, None) == -1
+    assert L.ep_layout_workspace_bytes(4096, 8, 256) > 0
+    assert L.ep_layout(fake, 4096, 8, 256, 8, *ws, None, 0, None) == -1
+    # dispatch: bad payload, H not a multiple of 128 for fp8, misaligned x
+    assert L.ep_dispatch(fake, 4, 1024, 8, fake, 7, fake, fake, None) == -2
+    assert L.ep_dispatch(fake, 4, 1000, 8, fake, 0, fake, fake, None) == -1
+    assert L.ep_dispatch(odd, 4, 1024, 8, fake, 0, fake, fake, None) == -1
+    # combine: H % 8 != 0, null out
+    assert L.ep_combine(fake, fake, fake, 4, 1001, 8, fake, None) == -1
+    assert L.ep_combine(fake, fake, fake, 4, 1024, 8, None, None) == -1
+    # empty batches are accepted without launching anything
+    assert L.ep_dispatch(None, 0, 1024, 8, None, 0, None, None, None) == 0
+    assert L.ep_combine(None, None, None, 0, 1024, 8, None, None) == 0
+    assert b"invalid" in L.ep_strerror(-1)
