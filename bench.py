@@ -66,12 +66,16 @@ class Path:
         self.N = self.d["N"]
 
     def enqueue(self, phase="step"):
+        """step: ep_layout_dispatch (one launch for small batches) + ep_combine;
+        step3: ep_layout + ep_dispatch + ep_combine; or a single phase."""
         s, b = self.stream, self.buf
-        if phase in ("step", "layout"):
+        if phase in ("step", "layout_dispatch"):
+            b.layout_dispatch(self.idx, self.x, s)
+        if phase in ("step3", "layout"):
             b.layout(self.idx, s)
-        if phase in ("step", "dispatch"):
+        if phase in ("step3", "dispatch"):
             b.dispatch(self.x, s)
-        if phase in ("step", "combine"):
+        if phase in ("step", "step3", "combine"):
             b.combine(self.y, self.w, s)
 
     def capture(self, phase="step", reps=1):
@@ -96,16 +100,16 @@ class Path:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / launches      # us per launch
 
-    def time_eager(self, iters, warmup=3):
+    def time_eager(self, iters, warmup=3, phase="step"):
         torch = self.torch
         for _ in range(warmup):
-            self.enqueue()
+            self.enqueue(phase)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(self.stream)
         for _ in range(iters):
-            self.enqueue()
+            self.enqueue(phase)
         e1.record(self.stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / iters
@@ -141,12 +145,12 @@ def cpu_baseline(wl, d, N, min_seconds):
             "sample": "%d full steps (layout+dispatch+combine) of %s, %.1f ms/step" % (n, wl.name, per * 1e3)}
 
 
-def measure(wl, steps, warmup, graph=True):
+def measure(wl, steps, warmup, graph=True, phase="step"):
     p = Path(wl)
     b = algo_bytes(wl, p.N)
     torch = p.torch
     if graph:
-        g = p.capture("step")
+        g = p.capture(phase)
         for _ in range(warmup):
             g.launch(p.stream)
         torch.cuda.synchronize()
@@ -159,7 +163,7 @@ def measure(wl, steps, warmup, graph=True):
         us = e0.elapsed_time(e1) * 1e3 / steps
         g.destroy()
     else:
-        us = p.time_eager(steps, warmup)
+        us = p.time_eager(steps, warmup, phase)
     return p, b, us
 
 
@@ -170,10 +174,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="ll_128x7168")
     ap.add_argument("--eager", action="store_true", help="time host-launched steps, no graph")
+    ap.add_argument("--unfused", action="store_true",
+                    help="step = ep_layout + ep_dispatch + ep_combine (default: ep_layout_dispatch + ep_combine)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-targets", action="store_true")
-    ap.add_argument("--only", choices=["layout", "dispatch", "combine", "step"],
+    ap.add_argument("--only", choices=["layout", "dispatch", "combine", "layout_dispatch", "step",
+                                       "step3"],
                     help="profiling mode: launch only this phase (eagerly) steps times, print nothing else")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="profiling mode: first run one device copy of this many MiB (counter calibration)")
@@ -199,7 +206,7 @@ def main():
             print("calib copy %d bytes" % n, flush=True)
         if args.only:
             p = Path(wl)
-            p.enqueue("step")
+            p.enqueue("step3")
             torch.cuda.synchronize()
             for _ in range(args.warmup + args.steps):
                 p.enqueue(args.only)
@@ -207,10 +214,13 @@ def main():
             print("profiled %s x%d on %s" % (args.only, args.warmup + args.steps, wl.name), flush=True)
         return
 
-    p, b, us = measure(wl, args.steps, args.warmup, graph=not args.eager)
-    eager_us = p.time_eager(200)
-    phases = {ph: p.phase_us(ph) for ph in ("layout", "dispatch", "combine")}
-    dom = max(("dispatch", "combine"), key=lambda ph: phases[ph])
+    step = "step3" if args.unfused else "step"
+    p, b, us = measure(wl, args.steps, args.warmup, graph=not args.eager, phase=step)
+    eager_us = p.time_eager(200, phase=step)
+    phases = {ph: p.phase_us(ph) for ph in ("layout_dispatch", "layout", "dispatch", "combine")}
+    b["layout_dispatch"] = b["dispatch"]
+    cand = ("dispatch", "combine") if args.unfused else ("layout_dispatch", "combine")
+    dom = max(cand, key=lambda ph: phases[ph])
     achieved = b[dom] / (phases[dom] * 1e-6) / 1e9
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -237,6 +247,8 @@ def main():
         "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.H, "experts": wl.E,
                    "partitions": wl.P, "topk": wl.K, "valid_pairs": p.N,
                    "timing": "eager" if args.eager else "hipgraph replay of one step",
+                   "step": "ep_layout + ep_dispatch + ep_combine" if args.unfused
+                   else "ep_layout_dispatch + ep_combine",
                    "parallelism": "single GPU (partitions stand in for EP ranks)"},
         "bytes_per_step": b["step"],
         "phases_us": {k: round(v, 3) for k, v in phases.items()},
@@ -256,6 +268,8 @@ def main():
         tg["bw_4096x7168_zipf_target_frac"] = 0.60
         tg["bw_4096x7168_zipf_phases_us"] = {ph: round(pb.phase_us(ph, reps=10, launches=3), 2)
                                             for ph in ("layout", "dispatch", "combine")}
+        tg["sweep_4x6144_unfused_us_per_step_graph"] = round(
+            measure(WORKLOADS["sweep_4x6144"], 2000, 50, phase="step3")[2], 3)
         del pb
         res["targets"] = tg
 

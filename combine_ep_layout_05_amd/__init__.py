@@ -39,6 +39,8 @@ _SIGS = {
     "ep_layout": ([_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "ep_dispatch": ([_P, _I, _I, _I, _P, _I, _P, _P, _P], _I),
     "ep_combine": ([_P, _P, _P, _I, _I, _I, _P, _P], _I),
+    "ep_layout_dispatch": ([_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                            _P, _P, _P], _I),
     "ep_graph_begin": ([_P], _I),
     "ep_graph_end": ([_P, ctypes.POINTER(_P)], _I),
     "ep_graph_launch": ([_P, _P], _I),
@@ -120,6 +122,22 @@ def ep_dispatch(x, K, row_of_pair, payload, recv_x, recv_scales=None, stream=Non
                                            _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
 
 
+def ep_layout_dispatch(topk_idx, x, E, P, payload, expert_count, expert_offset, part_count,
+                       part_offset, row_of_pair, src_pair, status, ws, recv_x, recv_scales=None,
+                       stream=None):
+    """ep_layout followed by ep_dispatch, as one launch for small batches."""
+    _dt(topk_idx, torch.int32)
+    _dt(x, torch.bfloat16, torch.int16, torch.uint16)
+    payload = PAYLOADS.get(payload, payload)
+    T, K = topk_idx.shape
+    H = x.shape[1]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("ep_layout_dispatch", _lib.ep_layout_dispatch(
+        _ptr(topk_idx), _ptr(x), T, H, K, E, P, payload, _ptr(expert_count), _ptr(expert_offset),
+        _ptr(part_count), _ptr(part_offset), _ptr(row_of_pair), _ptr(src_pair), _ptr(status),
+        _ptr(ws), ws_bytes, _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
+
+
 def ep_combine(expert_out, row_of_pair, topk_w, out, stream=None):
     """expert_out bf16 [T*K, H] (receive-row layout), topk_w fp32 [T, K] -> out bf16 [T, H]."""
     _dt(expert_out, torch.bfloat16, torch.int16, torch.uint16)
@@ -199,6 +217,11 @@ class EpBuffers:
     def layout(self, topk_idx, stream=None):
         ep_layout(topk_idx, self.E, self.P, self.expert_count, self.expert_offset, self.part_count,
                   self.part_offset, self.row_of_pair, self.src_pair, self.status, self.ws, stream)
+
+    def layout_dispatch(self, topk_idx, x, stream=None):
+        ep_layout_dispatch(topk_idx, x, self.E, self.P, self.payload, self.expert_count,
+                           self.expert_offset, self.part_count, self.part_offset, self.row_of_pair,
+                           self.src_pair, self.status, self.ws, self.recv_x, self.recv_scales, stream)
 
     def dispatch(self, x, stream=None):
         ep_dispatch(x, self.K, self.row_of_pair, self.payload, self.recv_x, self.recv_scales, stream)

@@ -70,6 +70,41 @@ int ep_dispatch(const uint16_t* x, int T, int H, int K, const int32_t* row_of_pa
                                         (hipStream_t)stream));
 }
 
+int ep_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
+                       int P, int payload, int32_t* expert_count, int32_t* expert_offset,
+                       int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
+                       int32_t* src_pair, uint32_t* status, void* ws, size_t ws_bytes,
+                       void* recv_x, float* recv_scales, void* stream)
+{
+    if (payload != EP_PAYLOAD_FP8_E4M3FN && payload != EP_PAYLOAD_BF16) return EP_ENOTSUP;
+    if (!routing_ok(T, K) || E < 1 || E > EP_MAX_EXPERTS || P < 1 || E % P != 0 || H <= 0)
+        return EP_EINVAL;
+    if (payload == EP_PAYLOAD_FP8_E4M3FN && H % ep::kScaleBlock != 0) return EP_EINVAL;
+    if (payload == EP_PAYLOAD_BF16 && H % ep::kColsPerLane != 0) return EP_EINVAL;
+    if (!ptr_ok(expert_count, 4) || !ptr_ok(expert_offset, 4) || !ptr_ok(part_count, 4) ||
+        !ptr_ok(part_offset, 4) || !ptr_ok(status, 4))
+        return EP_EINVAL;
+    if (T > 0) {
+        if (!ptr_ok(topk_idx, 4) || !ptr_ok(row_of_pair, 4) || !ptr_ok(src_pair, 4) ||
+            !ptr_ok(x, 16) || !ptr_ok(recv_x, 16))
+            return EP_EINVAL;
+        if (payload == EP_PAYLOAD_FP8_E4M3FN && !ptr_ok(recv_scales, 4)) return EP_EINVAL;
+    }
+    const size_t need = ep::layout_workspace_bytes(T, K, E);
+    if (need > 0 && (ws_bytes < need || !ptr_ok(ws, 16))) return EP_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (T > 0 && ep::fused_layout_dispatch_fits(T, K))
+        return from_hip(ep::launch_layout_dispatch(topk_idx, x, T, H, K, E, P, payload, expert_count,
+                                                   expert_offset, part_count, part_offset,
+                                                   row_of_pair, src_pair, status, recv_x,
+                                                   recv_scales, s));
+    int rc = from_hip(ep::launch_layout(topk_idx, T, K, E, P, expert_count, expert_offset,
+                                        part_count, part_offset, row_of_pair, src_pair, status,
+                                        ws, s));
+    if (rc != EP_OK || T == 0) return rc;
+    return from_hip(ep::launch_dispatch(x, T, H, K, row_of_pair, payload, recv_x, recv_scales, s));
+}
+
 int ep_combine(const uint16_t* expert_out, const int32_t* row_of_pair, const float* topk_w, int T,
                int H, int K, uint16_t* out, void* stream)
 {

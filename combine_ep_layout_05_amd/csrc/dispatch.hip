@@ -36,6 +36,38 @@
 namespace ep {
 namespace {
 
+// Quantise (fp8) or copy (bf16) one item and write it to the token's valid
+// rows.  `myrow` holds, in lane k < K, the receive row of the token's pair k.
+// Called by all 64 lanes of the wave (the fp8 amax uses DPP row exchanges).
+template <int kPayload>
+__device__ __forceinline__ void scatter_item(uint4 v, int myrow, int col0, int lane, int H, int K,
+                                             int n_rows, uint8_t* __restrict__ recv_x,
+                                             float* __restrict__ recv_scales)
+{
+    const bool active = col0 < H;
+    if constexpr (kPayload == 0) {
+        const int nb = H / kScaleBlock;
+        float scale;
+        const uint2 q = quantise_e4m3fn_block8(v, scale);
+        for (int k = 0; k < K; ++k) {
+            const int r = read_lane(myrow, k);
+            if (r < 0 || r >= n_rows) continue;     // masked (or not a receive row)
+            if (active) {
+                *reinterpret_cast<uint2*>(recv_x + (int64_t)r * H + col0) = q;
+                if ((lane % kLanesPerScaleBlock) == 0)
+                    recv_scales[(int64_t)r * nb + col0 / kScaleBlock] = scale;
+            }
+        }
+    } else {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(recv_x);
+        for (int k = 0; k < K; ++k) {
+            const int r = read_lane(myrow, k);
+            if (r < 0 || r >= n_rows) continue;
+            if (active) *reinterpret_cast<uint4*>(dst + (int64_t)r * H + col0) = v;
+        }
+    }
+}
+
 template <int kPayload>
 __global__ __launch_bounds__(kMoveThreads) void dispatch_kernel(
     const uint16_t* __restrict__ x, int H, int K, const int32_t* __restrict__ row_of_pair,
@@ -44,7 +76,6 @@ __global__ __launch_bounds__(kMoveThreads) void dispatch_kernel(
 {
     const int lane = threadIdx.x % kWave;
     const int stride = gridDim.x * kMoveWaves;
-    const int nb = H / kScaleBlock;
     int item = blockIdx.x * kMoveWaves + wave_uniform(threadIdx.x / kWave);
     if (item >= n_items) return;
 
@@ -67,33 +98,167 @@ __global__ __launch_bounds__(kMoveThreads) void dispatch_kernel(
         uint4 nv = make_uint4(0, 0, 0, 0);
         if (next < n_items) load_item(next, nrow, nv, ncol0);
 
-        const bool active = col0 < H;
-        if constexpr (kPayload == 0) {
-            float scale;
-            const uint2 q = quantise_e4m3fn_block8(v, scale);
-            for (int k = 0; k < K; ++k) {
-                const int r = read_lane(myrow, k);
-                if (r < 0 || r >= n_rows) continue;     // masked (or not a receive row)
-                if (active) {
-                    *reinterpret_cast<uint2*>(recv_x + (int64_t)r * H + col0) = q;
-                    if ((lane % kLanesPerScaleBlock) == 0)
-                        recv_scales[(int64_t)r * nb + col0 / kScaleBlock] = scale;
-                }
-            }
-        } else {
-            uint16_t* dst = reinterpret_cast<uint16_t*>(recv_x);
-            for (int k = 0; k < K; ++k) {
-                const int r = read_lane(myrow, k);
-                if (r < 0 || r >= n_rows) continue;
-                if (active) *reinterpret_cast<uint4*>(dst + (int64_t)r * H + col0) = v;
-            }
-        }
+        scatter_item<kPayload>(v, myrow, col0, lane, H, K, n_rows, recv_x, recv_scales);
 
         if (next >= n_items) break;
         item = next;
         myrow = nrow;
         v = nv;
         col0 = ncol0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Layout fused into the dispatch, for small batches (T*K <= kFusedMaxPairs).
+//
+// At a few tokens the step is paced by launches, not bytes (MoRI PR #614,
+// view-cache paragraph: latency flat over hidden 1024..6144 and over 4/8/16
+// tokens).  Here every dispatch workgroup derives, from all T*K ids (at most
+// 8 KB, read from L2), exactly the layout values it needs, so no separate
+// layout launch precedes the dispatch:
+//   - the per-expert totals (LDS atomics: integer sums, order-free) and their
+//     exclusive scan -> expert offsets;
+//   - per expert, the number of entries before this workgroup's first token;
+//   - the slots of its own tokens' entries: offset + entries before + rank
+//     among the workgroup's own entries (ballot match-any in one wave).
+// The results are identical to ep_layout's: workgroup 0 writes the counts,
+// offsets, partition sums and status; the workgroup holding a token's first
+// 512-column step writes that token's row_of_pair and src_pair entries.
+struct FusedSmem {
+    int32_t ids[kFusedMaxPairs];
+    int32_t cnt[kMaxExperts];
+    int32_t off[kMaxExperts];
+    int32_t before[kMaxExperts];
+    int32_t rows[kMoveWaves * kMaxTopK];
+    int32_t wsum[kMoveWaves];
+    uint32_t bad;
+};
+
+template <int kPayload>
+__global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, int n, int H, int K, int E,
+    int P, int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
+    int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair,
+    uint32_t* __restrict__ status, uint8_t* __restrict__ recv_x, float* __restrict__ recv_scales,
+    int steps_per_token, int n_items)
+{
+    __shared__ FusedSmem s;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int w = wave_uniform(tid / kWave);
+    const int item0 = blockIdx.x * kMoveWaves;
+    const int item = item0 + w;
+    const int last = (item0 + kMoveWaves - 1 < n_items) ? item0 + kMoveWaves - 1 : n_items - 1;
+    const int t_lo = item0 / steps_per_token;
+    const int t_hi = last / steps_per_token;
+    const int p_lo = t_lo * K;
+
+    // this wave's x vector is independent of the layout: load it first
+    int t = 0, col0 = H;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (item < n_items) {
+        t = item / steps_per_token;
+        col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
+        if (col0 < H) v = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + col0);
+    }
+
+    for (int e = tid; e < E; e += kMoveThreads) { s.cnt[e] = 0; s.before[e] = 0; }
+    if (tid == 0) s.bad = 0u;
+    for (int p = tid; p < n; p += kMoveThreads) s.ids[p] = idx[p];
+    __syncthreads();
+
+    for (int p = tid; p < n; p += kMoveThreads) {
+        const int e = s.ids[p];
+        if (e >= E) s.bad = 1u;
+        else if (e >= 0) {
+            atomicAdd(&s.cnt[e], 1);
+            if (p < p_lo) atomicAdd(&s.before[e], 1);
+        }
+    }
+    __syncthreads();
+
+    // exclusive scan of the counts: 4 consecutive experts per thread
+    constexpr int kPer = kMaxExperts / kMoveThreads;
+    static_assert(kPer * kMoveThreads == kMaxExperts, "experts split evenly over threads");
+    int c[kPer], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int e = tid * kPer + j;
+        c[j] = (e < E) ? s.cnt[e] : 0;
+        sum += c[j];
+    }
+    int incl = sum;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += y;
+    }
+    if (lane == kWave - 1) s.wsum[w] = incl;
+    __syncthreads();
+    int before_wave = 0, N = 0;
+    for (int u = 0; u < kMoveWaves; ++u) {
+        if (u < w) before_wave += s.wsum[u];
+        N += s.wsum[u];
+    }
+    int run = before_wave + incl - sum;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int e = tid * kPer + j;
+        if (e < E) s.off[e] = run;
+        run += c[j];
+    }
+    __syncthreads();
+
+    // slots of this workgroup's own entries (at most 4 tokens x 16 = one wave)
+    const int nq = (t_hi - t_lo + 1) * K;
+    if (w == 0) {
+        const int p = p_lo + lane;
+        const int e = (lane < nq) ? s.ids[p] : -1;
+        const bool valid = (e >= 0) && (e < E);
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < 10; ++b) {            // ids < kMaxExperts = 2^10
+            const bool bit = (e >> b) & 1;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        if (lane < nq) s.rows[lane] = valid ? s.off[e] + s.before[e] + lanes_below(peers) : -1;
+    }
+    __syncthreads();
+
+    // layout outputs
+    if (blockIdx.x == 0) {
+        for (int e = tid; e < E; e += kMoveThreads) {
+            expert_count[e] = s.cnt[e];
+            expert_offset[e] = s.off[e];
+        }
+        const int L = E / P;
+        for (int q = tid; q < P; q += kMoveThreads) {
+            const int lo = s.off[q * L];
+            const int hi = (q + 1 < P) ? s.off[(q + 1) * L] : N;
+            part_offset[q] = lo;
+            part_count[q] = hi - lo;
+        }
+        if (tid == 0) {
+            expert_offset[E] = N;
+            part_offset[P] = N;
+            *status = s.bad ? 1u : 0u;
+        }
+    }
+    if (tid < nq) {
+        const int tt = t_lo + tid / K;
+        if (tt * steps_per_token >= item0) {     // this workgroup holds the token's first step
+            const int p = p_lo + tid;
+            const int r = s.rows[tid];
+            row_of_pair[p] = r;
+            if (r >= 0 && r < n) src_pair[r] = p;
+        }
+    }
+    for (int r = N + blockIdx.x * kMoveThreads + tid; r < n; r += gridDim.x * kMoveThreads)
+        src_pair[r] = -1;
+
+    if (item < n_items) {
+        const int myrow = (lane < K) ? s.rows[(t - t_lo) * K + lane] : -1;
+        scatter_item<kPayload>(v, myrow, col0, lane, H, K, n, recv_x, recv_scales);
     }
 }
 
@@ -124,6 +289,33 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, const int32_t
     else
         hipLaunchKernelGGL(dispatch_kernel<1>, dim3((unsigned)blocks), dim3(kMoveThreads), 0, stream,
                            x, H, K, row_of_pair, (uint8_t*)recv_x, nullptr, steps, (int)items, T * K);
+    return hipGetLastError();
+}
+
+bool fused_layout_dispatch_fits(int T, int K) { return (int64_t)T * K <= kFusedMaxPairs; }
+
+hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
+                                  int E, int P, int payload, int32_t* expert_count,
+                                  int32_t* expert_offset, int32_t* part_count,
+                                  int32_t* part_offset, int32_t* row_of_pair, int32_t* src_pair,
+                                  uint32_t* status, void* recv_x, float* recv_scales,
+                                  hipStream_t stream)
+{
+    const int steps = (H + kStepCols - 1) / kStepCols;
+    const int64_t items = (int64_t)T * steps;
+    const int n = T * K;
+    const int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
+    if (T == 0 || blocks > kMaxGridBlocks) return hipErrorInvalidValue;
+    if (payload == 0)
+        hipLaunchKernelGGL(layout_dispatch_kernel<0>, dim3((unsigned)blocks), dim3(kMoveThreads), 0,
+                           stream, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
+                           part_count, part_offset, row_of_pair, src_pair, status,
+                           (uint8_t*)recv_x, recv_scales, steps, (int)items);
+    else
+        hipLaunchKernelGGL(layout_dispatch_kernel<1>, dim3((unsigned)blocks), dim3(kMoveThreads), 0,
+                           stream, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
+                           part_count, part_offset, row_of_pair, src_pair, status,
+                           (uint8_t*)recv_x, nullptr, steps, (int)items);
     return hipGetLastError();
 }
 

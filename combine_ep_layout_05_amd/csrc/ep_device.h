@@ -22,11 +22,14 @@ constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kMaxExperts = 1024;          // one expert column per thread
 constexpr int kSmallMaxPairs = 4096;       // single-workgroup layout up to this
 constexpr int kChunkPairs = 2048;          // pairs per workgroup above it
+constexpr int kMaxChunksTwoPass = 256;     // above: a separate scan launch
 static_assert(kMaxExperts <= kLayoutThreads, "scan assigns one expert per thread");
 static_assert(kChunkPairs % kLayoutThreads == 0, "a chunk is whole rounds");
 static_assert(kLayoutWaves * kWave <= 0xFFFF, "per-wave counts fit in uint16");
 
 // ---- dispatch / combine ---------------------------------------------------
+constexpr int kMaxTopK = 16;
+constexpr int kFusedMaxPairs = 2048;       // layout fused into dispatch up to this T*K
 constexpr int kMoveThreads = 256;          // 4 waves per workgroup
 constexpr int kMoveWaves = kMoveThreads / kWave;
 constexpr int kColsPerLane = 8;            // 16 B of bf16 per lane per step
@@ -34,6 +37,8 @@ constexpr int kStepCols = kWave * kColsPerLane;   // 512 columns per wave step
 constexpr int kScaleBlock = 128;           // columns per fp8 scale
 constexpr int kLanesPerScaleBlock = kScaleBlock / kColsPerLane;   // 16 = one DPP row
 static_assert(kLanesPerScaleBlock == 16, "a scale block must be one 16-lane DPP row");
+static_assert(kMoveWaves * kMaxTopK <= kWave, "a workgroup's own entries fit in one wave");
+static_assert(kMaxExperts <= 1024, "fused slot ranks compare 10 id bits");
 
 // Bits of v strictly below this lane set in `mask` (wave64).
 __device__ __forceinline__ int lanes_below(uint64_t mask)

@@ -21,6 +21,15 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K,
                            const int32_t* row_of_pair, int payload,
                            void* recv_x, float* recv_scales, hipStream_t stream);
 
+bool fused_layout_dispatch_fits(int T, int K);
+
+hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
+                                  int E, int P, int payload, int32_t* expert_count,
+                                  int32_t* expert_offset, int32_t* part_count,
+                                  int32_t* part_offset, int32_t* row_of_pair, int32_t* src_pair,
+                                  uint32_t* status, void* recv_x, float* recv_scales,
+                                  hipStream_t stream);
+
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of_pair,
                           const float* topk_w, int T, int H, int K,
                           uint16_t* out, hipStream_t stream);

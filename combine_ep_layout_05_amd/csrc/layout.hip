@@ -77,9 +77,9 @@ __device__ __forceinline__ void zero_smem(LayoutSmem& s, int E)
 // flat entry array (entries >= n are padding).  On entry s.cursor[e] is the
 // first free row of expert e; on exit it has moved past this round's entries.
 // Writes row_of_pair for every real entry (-1 when masked) and src_pair for
-// valid ones when src_pair is non-null.
+// valid ones when src_pair is non-null (rows are below n_rows = T*K).
 __device__ void rank_round(const int32_t* __restrict__ idx, int64_t base, int64_t n,
-                           int E, int nbits, LayoutSmem& s,
+                           int64_t n_rows, int E, int nbits, LayoutSmem& s,
                            int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair)
 {
     const int tid = threadIdx.x;
@@ -108,7 +108,7 @@ __device__ void rank_round(const int32_t* __restrict__ idx, int64_t base, int64_
         int row = -1;
         if (valid) {
             row = s.cursor[e] + (int)s.wtab[w][e] + rank;
-            if (src_pair && row < n) src_pair[row] = (int32_t)p;
+            if (src_pair && row < n_rows) src_pair[row] = (int32_t)p;
         }
         row_of_pair[p] = row;
     }
@@ -152,7 +152,7 @@ __device__ int block_exclusive_scan(int v, LayoutSmem& s, int* total)
 // From per-expert counts (one per thread, tid < E): write expert_count,
 // expert_offset, part_count, part_offset and status; leave the exclusive
 // offsets in s.cursor and N in s.total.
-__device__ void finish_counts(int count, int E, int P, uint32_t bad, LayoutSmem& s,
+__device__ void finish_counts(int count, int E, int P, uint32_t bad, LayoutSmem& s, bool write_out,
                               int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
                               int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
                               uint32_t* __restrict__ status)
@@ -160,25 +160,27 @@ __device__ void finish_counts(int count, int E, int P, uint32_t bad, LayoutSmem&
     const int tid = threadIdx.x;
     int N = 0;
     const int off = block_exclusive_scan(tid < E ? count : 0, s, &N);
-    if (tid < E) {
-        s.cursor[tid] = off;
-        expert_count[tid] = count;
-        expert_offset[tid] = off;
-    }
-    if (tid == 0) {
-        expert_offset[E] = N;
-        s.total = N;
-        *status = bad ? 1u : 0u;
+    if (tid < E) s.cursor[tid] = off;
+    if (tid == 0) s.total = N;
+    if (write_out) {
+        if (tid < E) {
+            expert_count[tid] = count;
+            expert_offset[tid] = off;
+        }
+        if (tid == 0) {
+            expert_offset[E] = N;
+            *status = bad ? 1u : 0u;
+        }
     }
     __syncthreads();
     const int L = E / P;
-    if (tid < P) {
+    if (write_out && tid < P) {
         const int lo = s.cursor[tid * L];
         const int hi = (tid + 1 < P) ? s.cursor[(tid + 1) * L] : N;
         part_offset[tid] = lo;
         part_count[tid] = hi - lo;
     }
-    if (tid == 0) part_offset[P] = N;
+    if (write_out && tid == 0) part_offset[P] = N;
 }
 
 // ---------------------------------------------------------------------------
@@ -207,43 +209,53 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
     }
     __syncthreads();
 
-    finish_counts(tid < E ? s.hist[tid] : 0, E, P, s.bad, s, expert_count, expert_offset,
+    finish_counts(tid < E ? s.hist[tid] : 0, E, P, s.bad, s, true, expert_count, expert_offset,
                   part_count, part_offset, status);
     __syncthreads();
 
     // pass 2: deterministic slots
     for (int64_t base = 0; base < n; base += kLayoutThreads)
-        rank_round(idx, base, n, E, nbits, s, row_of_pair, src_pair);
+        rank_round(idx, base, n, n, E, nbits, s, row_of_pair, src_pair);
 
     for (int64_t r = (int64_t)s.total + tid; r < n; r += kLayoutThreads) src_pair[r] = -1;
 }
 
 // ---------------------------------------------------------------------------
-// Large batches, step 1: one workgroup per chunk of kChunkPairs entries.
-// Writes the in-chunk rank into row_of_pair (-1 when masked), the chunk's
-// histogram into ws_hist[chunk][E] and a bad-id flag into ws_bad[chunk].
-__global__ __launch_bounds__(kLayoutThreads) void layout_chunk_kernel(
-    const int32_t* __restrict__ idx, int64_t n, int E,
-    int32_t* __restrict__ row_of_pair, int32_t* __restrict__ ws_hist,
+// Large batches, pass 1: one workgroup per chunk of kChunkPairs entries
+// writes the chunk's histogram into ws_hist[chunk][E] and a bad-id flag into
+// ws_bad[chunk] (ballot-aggregated LDS atomics: a hot expert costs one atomic
+// per wave, not one per entry).
+__global__ __launch_bounds__(kLayoutThreads) void layout_hist_kernel(
+    const int32_t* __restrict__ idx, int64_t n, int E, int32_t* __restrict__ ws_hist,
     uint32_t* __restrict__ ws_bad)
 {
-    __shared__ LayoutSmem s;
+    __shared__ int32_t hist[kMaxExperts];
+    __shared__ uint32_t bad;
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
     const int nbits = id_bits(E);
-    zero_smem(s, E);
+    if (tid < E) hist[tid] = 0;
+    if (tid == 0) bad = 0u;
     __syncthreads();
     const int64_t c0 = (int64_t)chunk * kChunkPairs;
     const int64_t c1 = (c0 + kChunkPairs < n) ? c0 + kChunkPairs : n;
-    for (int64_t base = c0; base < c1; base += kLayoutThreads)
-        rank_round(idx, base, c1, E, nbits, s, row_of_pair, nullptr);
-    if (tid < E) ws_hist[(int64_t)chunk * E + tid] = s.cursor[tid];
-    if (tid == 0) ws_bad[chunk] = s.bad;
+    for (int64_t base = c0; base < c1; base += kLayoutThreads) {
+        const int64_t p = base + tid;
+        const int e = (p < c1) ? idx[p] : -1;
+        const bool valid = (e >= 0) && (e < E);
+        if (p < c1 && e >= E) bad = 1u;
+        const uint64_t peers = match_peers(e, valid, nbits);
+        if (valid && lanes_below(peers) == 0) atomicAdd(&hist[e], (int)__popcll(peers));
+    }
+    __syncthreads();
+    if (tid < E) ws_hist[(int64_t)chunk * E + tid] = hist[tid];
+    if (tid == 0) ws_bad[chunk] = bad;
 }
 
-// Large batches, step 2: one workgroup.  Totals per expert over chunks, the
-// exclusive scans and partition sums, then each chunk's base row per expert
-// (offset[e] + rows of expert e in earlier chunks) written back over ws_hist.
+// Large batches with many chunks, pass 2: one workgroup turns the chunk
+// histograms into totals, the scans and partition sums, and each chunk's base
+// row per expert (offset[e] + rows of expert e in earlier chunks), written
+// back over ws_hist.
 constexpr int kScanBatch = 16;
 
 __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(
@@ -277,7 +289,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(
         }
     }
     __syncthreads();
-    finish_counts(run, E, P, s.bad, s, expert_count, expert_offset, part_count, part_offset,
+    finish_counts(run, E, P, s.bad, s, true, expert_count, expert_offset, part_count, part_offset,
                   status);
     __syncthreads();
     if (tid < E) {
@@ -286,25 +298,65 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(
     }
 }
 
-// Large batches, step 3: row = chunk base of the entry's expert + in-chunk
-// rank; src_pair is the inverse map, -1 past N.
-__global__ __launch_bounds__(256) void layout_finalize_kernel(
-    const int32_t* __restrict__ idx, int64_t n, int E,
-    const int32_t* __restrict__ ws_base, const int32_t* __restrict__ expert_offset,
-    int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair)
+// Large batches, last pass: one workgroup per chunk ranks its entries.
+// With bases_ready == 0 (few chunks) every workgroup first derives, from all
+// chunk histograms, the per-expert totals (-> scans; workgroup 0 also writes
+// the count outputs) and the rows of each expert taken by earlier chunks --
+// reading C*E integers from L2 is cheaper than another launch.  With
+// bases_ready == 1 the scan kernel has already put the bases in ws_hist.
+__global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
+    const int32_t* __restrict__ idx, int64_t n, int E, int P, int nchunks, int bases_ready,
+    const int32_t* __restrict__ ws_hist, const uint32_t* __restrict__ ws_bad,
+    int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
+    int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair,
+    uint32_t* __restrict__ status)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (int64_t p = g; p < n; p += stride) {
-        const int e = idx[p];
-        if (e >= 0 && e < E) {
-            const int row = ws_base[(p / kChunkPairs) * E + e] + row_of_pair[p];
-            row_of_pair[p] = row;
-            if (row >= 0 && row < n) src_pair[row] = (int32_t)p;
+    __shared__ LayoutSmem s;
+    const int tid = threadIdx.x;
+    const int chunk = blockIdx.x;
+    const int nbits = id_bits(E);
+    zero_smem(s, E);
+    __syncthreads();
+
+    if (!bases_ready) {
+        // groups of E threads split the chunks; partial sums meet in LDS
+        const int groups = kLayoutThreads / E;
+        const int g = tid / E, e = tid - g * E;
+        if (g < groups) {
+            int tot = 0, bef = 0;
+            for (int c = g; c < nchunks; c += groups) {
+                const int h = ws_hist[(int64_t)c * E + e];
+                tot += h;
+                if (c < chunk) bef += h;
+            }
+            atomicAdd(&s.hist[e], tot);
+            atomicAdd(&s.cursor[e], bef);
         }
+        uint32_t b = 0;
+        for (int c = tid; c < nchunks; c += kLayoutThreads) b |= ws_bad[c];
+        if (b) s.bad = 1u;
+        __syncthreads();
+        const int before = (tid < E) ? s.cursor[tid] : 0;
+        __syncthreads();
+        finish_counts(tid < E ? s.hist[tid] : 0, E, P, s.bad, s, chunk == 0, expert_count,
+                      expert_offset, part_count, part_offset, status);
+        __syncthreads();                     // partition sums above read s.cursor
+        if (tid < E) s.cursor[tid] += before;
+    } else {
+        if (tid < E) s.cursor[tid] = ws_hist[(int64_t)chunk * E + tid];
+        if (tid == 0) s.total = expert_offset[E];
     }
-    const int64_t N = expert_offset[E];
-    for (int64_t r = N + g; r < n; r += stride) src_pair[r] = -1;
+    __syncthreads();
+
+    const int64_t c0 = (int64_t)chunk * kChunkPairs;
+    const int64_t c1 = (c0 + kChunkPairs < n) ? c0 + kChunkPairs : n;
+    for (int64_t base = c0; base < c1; base += kLayoutThreads)
+        rank_round(idx, base, c1, n, E, nbits, s, row_of_pair, src_pair);
+
+    const int64_t stride = (int64_t)gridDim.x * kLayoutThreads;
+    for (int64_t r = (int64_t)s.total + (int64_t)chunk * kLayoutThreads + tid; r < n; r += stride)
+        src_pair[r] = -1;
 }
 
 int64_t num_chunks(int64_t n) { return (n + kChunkPairs - 1) / kChunkPairs; }
@@ -338,15 +390,16 @@ hipError_t launch_layout(const int32_t* idx, int T, int K, int E, int P,
     const size_t hist = (size_t)c * E * sizeof(int32_t);
     int32_t* ws_hist = (int32_t*)ws;
     uint32_t* ws_bad = (uint32_t*)((char*)ws + ((hist + 255) & ~(size_t)255));
-    hipLaunchKernelGGL(layout_chunk_kernel, dim3((unsigned)c), dim3(kLayoutThreads), 0, stream,
-                       idx, n, E, row_of_pair, ws_hist, ws_bad);
-    hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kLayoutThreads), 0, stream,
-                       (int)c, E, P, ws_hist, ws_bad, expert_count, expert_offset, part_count,
-                       part_offset, status);
-    const int64_t blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(layout_finalize_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048)),
-                       dim3(256), 0, stream, idx, n, E, ws_hist, expert_offset, row_of_pair,
-                       src_pair);
+    hipLaunchKernelGGL(layout_hist_kernel, dim3((unsigned)c), dim3(kLayoutThreads), 0, stream,
+                       idx, n, E, ws_hist, ws_bad);
+    const int bases_ready = c > kMaxChunksTwoPass ? 1 : 0;
+    if (bases_ready)
+        hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kLayoutThreads), 0, stream,
+                           (int)c, E, P, ws_hist, ws_bad, expert_count, expert_offset, part_count,
+                           part_offset, status);
+    hipLaunchKernelGGL(layout_rank_kernel, dim3((unsigned)c), dim3(kLayoutThreads), 0, stream,
+                       idx, n, E, P, (int)c, bases_ready, ws_hist, ws_bad, expert_count,
+                       expert_offset, part_count, part_offset, row_of_pair, src_pair, status);
     return hipGetLastError();
 }
 

@@ -138,6 +138,22 @@ int ep_dispatch(const uint16_t* x, int T, int H, int K,
                 void* recv_x, float* recv_scales, void* stream);
 
 /*
+ * Layout and dispatch in one call: the same results as ep_layout followed by
+ * ep_dispatch (every output of both, bit for bit), with the same arguments
+ * and errors as those two calls together.  For small batches (T*K <= 2048)
+ * it is ONE kernel launch: each dispatch workgroup derives the layout values
+ * it needs from the T*K ids, so no separate layout launch precedes it -- at
+ * a few tokens the step is paced by launches, not by bytes (MoRI PR #614,
+ * view-cache paragraph).  Larger batches run the layout and dispatch kernels
+ * back to back.
+ */
+int ep_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
+                       int P, int payload, int32_t* expert_count, int32_t* expert_offset,
+                       int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
+                       int32_t* src_pair, uint32_t* status, void* ws, size_t ws_bytes,
+                       void* recv_x, float* recv_scales, void* stream);
+
+/*
  * Combine: out[t, c] = bf16_rne(acc), acc = 0.0f, then for k = 0..K-1 with
  * r = row_of_pair[t*K+k] >= 0: acc = fmaf(topk_w[t*K+k], y[r, c], acc)
  * (fp32, fixed k order; masked entries are skipped, weights used as given).

@@ -24,8 +24,9 @@ def to_dev(a, dtype=None):
     return t.cuda()
 
 
-def run_gpu(wl, d, stream=None, poison=True):
-    """Layout + dispatch + combine on the GPU; returns numpy copies of every output."""
+def run_gpu(wl, d, stream=None, poison=True, fused=False):
+    """Layout + dispatch + combine on the GPU; returns numpy copies of every output.
+    fused=True runs ep_layout_dispatch instead of ep_layout then ep_dispatch."""
     ep = gpu_lib()
     buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
     if poison:
@@ -39,8 +40,11 @@ def run_gpu(wl, d, stream=None, poison=True):
     x = to_dev(d["x"].view(np.int16), torch.bfloat16)
     y = to_dev(d["y"].view(np.int16), torch.bfloat16)
     w = to_dev(d["w"])
-    buf.layout(idx, stream)
-    buf.dispatch(x, stream)
+    if fused:
+        buf.layout_dispatch(idx, x, stream)
+    else:
+        buf.layout(idx, stream)
+        buf.dispatch(x, stream)
     buf.combine(y, w, stream)
     torch.cuda.synchronize()
     return collect(buf)

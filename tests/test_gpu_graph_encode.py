@@ -13,8 +13,9 @@ from workloads import WORKLOADS, generate
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name", ["sweep_4x6144", "ll_128x7168", "bw_4096x7168_zipf"])
-def test_graph_replay_matches_eager(name):
+def test_graph_replay_matches_eager(name, fused):
     """A captured layout -> dispatch -> combine step replays bit-exactly to the
     eager result, replay after replay, with unrelated eager work and
     synchronisations in between (the check MoRI PR #614 runs for its
@@ -41,8 +42,11 @@ def test_graph_replay_matches_eager(name):
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         ep.ep_graph_begin(s)
-        buf.layout(idx, s)
-        buf.dispatch(x, s)
+        if fused:
+            buf.layout_dispatch(idx, x, s)
+        else:
+            buf.layout(idx, s)
+            buf.dispatch(x, s)
         buf.combine(y, w, s)
         g = ep.ep_graph_end(s)
     for rep in range(4):

@@ -20,12 +20,12 @@ SMALL = ["tiny_4x1024", "ll_128x7168", "sweep_4x6144", "sweep_8x6144", "sweep_16
 LARGE = ["bw_4096x7168_zipf", "masked_16384x4096_bf16"]
 
 
-def _case(wl, seed=None, d=None):
-    print("case %s T=%d H=%d E=%d P=%d K=%d %s seed=%s" % (wl.name, wl.T, wl.H, wl.E, wl.P, wl.K,
-                                                           wl.payload, seed), flush=True)
+def _case(wl, seed=None, d=None, fused=False):
+    print("case %s T=%d H=%d E=%d P=%d K=%d %s seed=%s fused=%s" % (
+        wl.name, wl.T, wl.H, wl.E, wl.P, wl.K, wl.payload, seed, fused), flush=True)
     sys.stdout.flush()
     d = generate(wl, seed=seed) if d is None else d
-    got = run_gpu(wl, d)
+    got = run_gpu(wl, d, fused=fused)
     ref = run_oracle(wl, d)
     ndiff = compare(wl, got, ref)
     assert ndiff == 0, "%s: %d combine outputs differ by 1 ulp" % (wl.name, ndiff)
@@ -45,6 +45,44 @@ def test_large_workloads(name):
     _case(wl, wl.seed)
 
 
+@pytest.mark.parametrize("name", SMALL + LARGE)
+def test_fused_layout_dispatch(name):
+    """ep_layout_dispatch: one launch up to 2048 entries, layout + dispatch
+    kernels above; same results as the separate calls, hence as the oracle."""
+    wl = WORKLOADS[name]
+    _case(wl, wl.seed + 1, fused=True)
+
+
+FUSED_EDGE = {
+    "T1": dict(T=1),
+    "K16": dict(K=16, E=64, P=8),
+    "E1024": dict(E=1024, P=8, T=64),
+    "H128_many_tokens_per_wg": dict(H=128, T=200),        # 1 step/token: 4 tokens per workgroup
+    "H640": dict(H=640, T=33),
+    "at_limit_2048": dict(T=256, H=256),                  # T*K = 2048: fused
+    "over_limit_2056": dict(T=257, H=256),                # T*K = 2056: layout + dispatch
+    "bf16_payload": dict(payload="bf16", T=50, H=512),
+}
+
+
+@pytest.mark.parametrize("edge", list(FUSED_EDGE))
+def test_fused_edge_shapes(edge):
+    wl = WORKLOADS["tiny_4x1024"].with_(name="fused_" + edge, **FUSED_EDGE[edge])
+    _case(wl, 78, fused=True)
+
+
+def test_fused_masked_duplicate_and_bad_ids():
+    wl = WORKLOADS["tiny_4x1024"].with_(name="fused_ids", T=40, H=256, E=16, P=4, K=6)
+    d = generate(wl, seed=6)
+    rng = np.random.default_rng(6)
+    idx = rng.integers(-3, 20, size=(wl.T, wl.K)).astype(np.int32)
+    idx[3] = 7
+    idx[4] = -1
+    d["idx"] = idx
+    got, ref, _ = _case(wl, d=d, fused=True)
+    assert int(got["status"][0]) == 1
+
+
 EDGE = {
     "T1": dict(T=1),
     "K1": dict(K=1),
@@ -56,6 +94,7 @@ EDGE = {
     "E1024": dict(E=1024, P=8, T=64),
     "just_over_single_wg": dict(T=513, H=256),        # 4104 pairs -> chunked path, ragged chunk
     "chunked_ragged": dict(T=700, H=384, E=96, P=4),
+    "many_chunks_scan_pass": dict(T=70000, H=128, E=64, P=8),   # > 256 chunks: scan launch
 }
 
 
