@@ -123,6 +123,26 @@ class Path:
         return us
 
 
+def recorded_traffic(phase, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    readings (profiles/traffic.txt), or None when there is no reading for this
+    kernel and workload or the kernel's sources changed since it was taken."""
+    from combine_ep_layout_05_amd import build as B
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        f = line.split()
+        kv = dict(x.split("=", 1) for x in f[2:])
+        if f[0] == phase and f[1] == workload:
+            if kv.get("source_digest") != B.source_digest(phase):
+                return None
+            return int(float(kv["traffic_bytes"]))
+    return None
+
+
 def cpu_baseline(wl, d, N, min_seconds):
     """The oracle as it stands (single-threaded C), full steps of the same
     workload on the host, repeated until min_seconds have elapsed."""
@@ -145,26 +165,37 @@ def cpu_baseline(wl, d, N, min_seconds):
             "sample": "%d full steps (layout+dispatch+combine) of %s, %.1f ms/step" % (n, wl.name, per * 1e3)}
 
 
-def measure(wl, steps, warmup, graph=True, phase="step"):
+STEPS_PER_GRAPH = 50
+
+
+def time_steps(p, steps, warmup, mode, phase="step"):
+    """us per step.  mode "graph": graphs of STEPS_PER_GRAPH whole steps
+    (device time per step; one graph launch per STEPS_PER_GRAPH steps);
+    "graph1": one graph launch per step (adds the host's graph-launch cost);
+    "eager": every call enqueued from the host."""
+    torch = p.torch
+    if mode == "eager":
+        return p.time_eager(steps, warmup, phase)
+    per = min(STEPS_PER_GRAPH, steps) if mode == "graph" else 1
+    g = p.capture(phase, per)
+    launches = max(1, steps // per)
+    for _ in range(max(1, warmup // per)):
+        g.launch(p.stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(p.stream)
+    for _ in range(launches):
+        g.launch(p.stream)
+    e1.record(p.stream)
+    torch.cuda.synchronize()
+    g.destroy()
+    return e0.elapsed_time(e1) * 1e3 / (launches * per)
+
+
+def measure(wl, steps, warmup, mode="graph", phase="step"):
     p = Path(wl)
     b = algo_bytes(wl, p.N)
-    torch = p.torch
-    if graph:
-        g = p.capture(phase)
-        for _ in range(warmup):
-            g.launch(p.stream)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(p.stream)
-        for _ in range(steps):
-            g.launch(p.stream)
-        e1.record(p.stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
-        g.destroy()
-    else:
-        us = p.time_eager(steps, warmup, phase)
-    return p, b, us
+    return p, b, time_steps(p, steps, warmup, mode, phase)
 
 
 def main():
@@ -215,15 +246,18 @@ def main():
         return
 
     step = "step3" if args.unfused else "step"
-    p, b, us = measure(wl, args.steps, args.warmup, graph=not args.eager, phase=step)
-    eager_us = p.time_eager(200, phase=step)
+    mode = "eager" if args.eager else "graph"
+    p, b, us = measure(wl, args.steps, args.warmup, mode=mode, phase=step)
+    eager_us = time_steps(p, 500, 20, "eager", step)
+    graph1_us = time_steps(p, 1000, 20, "graph1", step)
     phases = {ph: p.phase_us(ph) for ph in ("layout_dispatch", "layout", "dispatch", "combine")}
     b["layout_dispatch"] = b["dispatch"]
     cand = ("dispatch", "combine") if args.unfused else ("layout_dispatch", "combine")
     dom = max(cand, key=lambda ph: phases[ph])
     achieved = b[dom] / (phases[dom] * 1e-6) / 1e9
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic(dom, wl.name),
             "bytes_per_launch": b[dom], "us_per_launch": round(phases[dom], 3)}
     value = b["step"] / (us * 1e-6) / 1e9
 
@@ -246,13 +280,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.H, "experts": wl.E,
                    "partitions": wl.P, "topk": wl.K, "valid_pairs": p.N,
-                   "timing": "eager" if args.eager else "hipgraph replay of one step",
+                   "timing": "eager host launches" if args.eager else
+                   "HIP graphs of %d whole steps, replayed" % STEPS_PER_GRAPH,
                    "step": "ep_layout + ep_dispatch + ep_combine" if args.unfused
                    else "ep_layout_dispatch + ep_combine",
                    "parallelism": "single GPU (partitions stand in for EP ranks)"},
         "bytes_per_step": b["step"],
         "phases_us": {k: round(v, 3) for k, v in phases.items()},
         "eager_us_per_step": round(eager_us, 3),
+        "graph1_us_per_step": round(graph1_us, 3),
         "roofline": roof,
     }
 
@@ -260,9 +296,14 @@ def main():
         tg = {}
         pw, bw_, us4 = measure(WORKLOADS["sweep_4x6144"], 2000, 50)
         tg["sweep_4x6144_us_per_step_graph"] = round(us4, 3)
+        tg["sweep_4x6144_us_per_step_graph1"] = round(time_steps(pw, 1000, 20, "graph1"), 3)
+        tg["sweep_4x6144_us_per_step_eager"] = round(time_steps(pw, 500, 20, "eager"), 3)
         tg["sweep_4x6144_target_us"] = 15.0
+        for tt in (8, 16):
+            tg["sweep_%dx6144_us_per_step_graph" % tt] = round(
+                measure(WORKLOADS["sweep_%dx6144" % tt], 2000, 50)[2], 3)
         del pw
-        pb, bb, usb = measure(WORKLOADS["bw_4096x7168_zipf"], 50, 5)
+        pb, bb, usb = measure(WORKLOADS["bw_4096x7168_zipf"], 100, 10)
         tg["bw_4096x7168_zipf_us_per_step"] = round(usb, 2)
         tg["bw_4096x7168_zipf_hbm_frac"] = round(bb["step"] / (usb * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
         tg["bw_4096x7168_zipf_target_frac"] = 0.60
@@ -270,6 +311,10 @@ def main():
                                             for ph in ("layout", "dispatch", "combine")}
         tg["sweep_4x6144_unfused_us_per_step_graph"] = round(
             measure(WORKLOADS["sweep_4x6144"], 2000, 50, phase="step3")[2], 3)
+        pm, bm, usm = measure(WORKLOADS["masked_16384x4096_bf16"], 20, 2)
+        tg["masked_16384x4096_bf16_us_per_step"] = round(usm, 2)
+        tg["masked_16384x4096_bf16_hbm_frac"] = round(bm["step"] / (usm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        del pm
         del pb
         res["targets"] = tg
 

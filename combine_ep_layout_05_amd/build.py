@@ -18,7 +18,7 @@ FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-Wl,-soname,libep_mi355x.so",
     "-I", os.path.join(ROOT, "include"),
 ]
 
@@ -46,3 +46,35 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+
+
+# sources each kernel family is compiled from (shared headers included)
+KERNEL_SOURCES = {
+    "layout": ["layout.hip", "ep_device.h"],
+    "dispatch": ["dispatch.hip", "ep_numerics.h", "ep_device.h"],
+    "layout_dispatch": ["dispatch.hip", "ep_numerics.h", "ep_device.h"],
+    "combine": ["combine.hip", "ep_numerics.h", "ep_device.h"],
+}
+
+
+def source_digest(kernel=None) -> str:
+    """sha256 of the HIP sources a kernel is built from (all sources when
+    kernel is None) and the code-generation flags, with comments and
+    whitespace removed: it changes when the compiled code can change, not when
+    a comment does.  Recorded next to rocprofv3 counter readings so that a
+    reading is only reused for the kernel code it was taken from."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    h.update(" ".join(f for f in FLAGS if f.startswith(("-O", "--offload", "-f", "-m", "-std"))).encode())
+    if kernel is None:
+        files = sorted(sources() + glob.glob(os.path.join(CSRC, "*.h")))
+    else:
+        files = [os.path.join(CSRC, n) for n in KERNEL_SOURCES[kernel]]
+    for p in files:
+        text = open(p).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = re.sub(r"\s+", " ", text)
+        h.update(os.path.basename(p).encode() + b"\0" + text.encode())
+    return h.hexdigest()

@@ -23,7 +23,7 @@
 namespace ep {
 namespace {
 
-template <int kMaxK>
+template <int kMaxK, bool kStream>
 __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
     const uint16_t* __restrict__ y, const int32_t* __restrict__ row_of_pair,
     const float* __restrict__ topk_w, int H, int K, uint16_t* __restrict__ out,
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
             v[k] = make_uint4(0, 0, 0, 0);
             if (k < K) {
                 const int r = read_lane(myrow, k);
-                if (r >= 0 && active) v[k] = *reinterpret_cast<const uint4*>(y + (int64_t)r * H + col0);
+                if (r >= 0 && active) v[k] = load16<kStream>(y + (int64_t)r * H + col0);
             }
         }
         float acc[8];
@@ -75,12 +75,27 @@ __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
             o.y = pack2_bf16(acc[2], acc[3]);
             o.z = pack2_bf16(acc[4], acc[5]);
             o.w = pack2_bf16(acc[6], acc[7]);
-            *reinterpret_cast<uint4*>(out + (int64_t)t * H + col0) = o;
+            store16<kStream>(out + (int64_t)t * H + col0, o);
         }
     }
 }
 
 constexpr int64_t kMaxGridBlocks = 1 << 20;
+
+// Streaming (nontemporal) expert-output reads and output writes once the
+// gathered rows exceed what the caches can usefully hold: measured on MI355X
+// at 4096 x 7168 top-8 right after a dispatch, the combine went 132 -> 96 us
+// because its once-read rows no longer evict the dispatch's fresh lines.
+// EP_FORCE_POLICY (build option for A/B runs): 1 = cached accesses everywhere,
+// 2 = streaming combine only, 3 = streaming dispatch and combine.
+bool combine_streams(int T, int H, int K)
+{
+#if defined(EP_FORCE_POLICY)
+    if (EP_FORCE_POLICY == 1) return false;
+    if (EP_FORCE_POLICY >= 2) return true;
+#endif
+    return (int64_t)T * K * H * 2 >= kStreamMinBytes;
+}
 
 }  // namespace
 
@@ -93,12 +108,11 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* row_of_pair, const f
     if (items + kMaxGridBlocks * kMoveWaves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
     if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
-    if (K <= 8)
-        hipLaunchKernelGGL(combine_kernel<8>, dim3((unsigned)blocks), dim3(kMoveThreads), 0, stream,
-                           y, row_of_pair, topk_w, H, K, out, steps, (int)items, T * K);
-    else
-        hipLaunchKernelGGL(combine_kernel<16>, dim3((unsigned)blocks), dim3(kMoveThreads), 0, stream,
-                           y, row_of_pair, topk_w, H, K, out, steps, (int)items, T * K);
+    const bool stream_policy = combine_streams(T, H, K);
+    auto k = K <= 8 ? (stream_policy ? combine_kernel<8, true> : combine_kernel<8, false>)
+                    : (stream_policy ? combine_kernel<16, true> : combine_kernel<16, false>);
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kMoveThreads), 0, stream, y, row_of_pair,
+                       topk_w, H, K, out, steps, (int)items, T * K);
     return hipGetLastError();
 }
 

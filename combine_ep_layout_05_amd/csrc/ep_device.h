@@ -31,6 +31,9 @@ static_assert(kLayoutWaves * kWave <= 0xFFFF, "per-wave counts fit in uint16");
 constexpr int kMaxTopK = 16;
 constexpr int kFusedMaxPairs = 2048;       // layout fused into dispatch up to this T*K
 constexpr int kMoveThreads = 256;          // 4 waves per workgroup
+// payload bytes of one call above which dispatch/combine use streaming
+// (nontemporal) accesses; below it the working set stays cache resident
+constexpr int64_t kStreamMinBytes = (int64_t)64 << 20;
 constexpr int kMoveWaves = kMoveThreads / kWave;
 constexpr int kColsPerLane = 8;            // 16 B of bf16 per lane per step
 constexpr int kStepCols = kWave * kColsPerLane;   // 512 columns per wave step
@@ -45,6 +48,39 @@ __device__ __forceinline__ int lanes_below(uint64_t mask)
 {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// 16- and 8-byte global accesses with a cache policy.  kStream = true marks
+// data touched once (nontemporal: the access does not displace reusable lines
+// in L2 / the memory-side cache).  At large batches the combine streams far
+// more than the caches hold, and keeping its reads and writes from evicting
+// the dispatch's freshly written rows measured faster on MI355X.
+typedef unsigned int ep_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int ep_u32x2 __attribute__((ext_vector_type(2)));
+
+template <bool kStream>
+__device__ __forceinline__ uint4 load16(const void* p)
+{
+    ep_u32x4 v;
+    if constexpr (kStream) v = __builtin_nontemporal_load(reinterpret_cast<const ep_u32x4*>(p));
+    else v = *reinterpret_cast<const ep_u32x4*>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <bool kStream>
+__device__ __forceinline__ void store16(void* p, uint4 u)
+{
+    ep_u32x4 v = {u.x, u.y, u.z, u.w};
+    if constexpr (kStream) __builtin_nontemporal_store(v, reinterpret_cast<ep_u32x4*>(p));
+    else *reinterpret_cast<ep_u32x4*>(p) = v;
+}
+
+template <bool kStream>
+__device__ __forceinline__ void store8(void* p, uint2 u)
+{
+    ep_u32x2 v = {u.x, u.y};
+    if constexpr (kStream) __builtin_nontemporal_store(v, reinterpret_cast<ep_u32x2*>(p));
+    else *reinterpret_cast<ep_u32x2*>(p) = v;
 }
 
 __device__ __forceinline__ int wave_uniform(int v)
