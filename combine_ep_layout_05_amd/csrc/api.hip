@@ -5,7 +5,7 @@
 // call leaves the stream untouched (configuration errors are refused early
 // and loudly, as the tuning CLI of MoRI PR #614 "perf(ep): InterNodeV1LL
 // low-token latency on MI300X + CX7" does for its environment knobs).
-#include "../../include/ep.h"
+#include "ep.h"
 #include "ep_device.h"
 #include "ep_launch.h"
 

@@ -36,19 +36,18 @@
 namespace ep {
 namespace {
 
-// Quantise (fp8) or copy (bf16) one item and write it to the token's valid
-// rows.  `myrow` holds, in lane k < K, the receive row of the token's pair k.
-// Called by all 64 lanes of the wave (the fp8 amax uses DPP row exchanges).
+// Write one item to the token's valid rows: the fp8 bytes q and the block
+// scale (kPayload 0) or the bf16 vector v unchanged (kPayload 1).  `myrow`
+// holds, in lane k < K, the receive row of the token's pair k.
 template <int kPayload, bool kStream>
-__device__ __forceinline__ void scatter_item(uint4 v, int myrow, int col0, int lane, int H, int K,
-                                             int n_rows, uint8_t* __restrict__ recv_x,
-                                             float* __restrict__ recv_scales)
+__device__ __forceinline__ void store_item(uint4 v, uint2 q, float scale, int myrow, int col0,
+                                           int lane, int H, int K, int n_rows,
+                                           uint8_t* __restrict__ recv_x,
+                                           float* __restrict__ recv_scales)
 {
     const bool active = col0 < H;
     if constexpr (kPayload == 0) {
         const int nb = H / kScaleBlock;
-        float scale;
-        const uint2 q = quantise_e4m3fn_block8(v, scale);
         for (int k = 0; k < K; ++k) {
             const int r = read_lane(myrow, k);
             if (r < 0 || r >= n_rows) continue;     // masked (or not a receive row)
@@ -66,6 +65,16 @@ __device__ __forceinline__ void scatter_item(uint4 v, int myrow, int col0, int l
             if (active) store16<kStream>(dst + (int64_t)r * H + col0, v);
         }
     }
+}
+
+// Quantise (fp8) one item; must be called by all 64 lanes of the wave (the
+// 128-column amax uses DPP row exchanges).  bf16 needs no work.
+template <int kPayload>
+__device__ __forceinline__ uint2 prepare_item(uint4 v, float& scale)
+{
+    scale = 0.0f;
+    if constexpr (kPayload == 0) return quantise_e4m3fn_block8(v, scale);
+    return make_uint2(0u, 0u);
 }
 
 template <int kPayload, bool kStream>
@@ -98,7 +107,10 @@ __global__ __launch_bounds__(kMoveThreads) void dispatch_kernel(
         uint4 nv = make_uint4(0, 0, 0, 0);
         if (next < n_items) load_item(next, nrow, nv, ncol0);
 
-        scatter_item<kPayload, kStream>(v, myrow, col0, lane, H, K, n_rows, recv_x, recv_scales);
+        float scale;
+        const uint2 q = prepare_item<kPayload>(v, scale);
+        store_item<kPayload, kStream>(v, q, scale, myrow, col0, lane, H, K, n_rows, recv_x,
+                                      recv_scales);
 
         if (next >= n_items) break;
         item = next;
@@ -111,19 +123,23 @@ __global__ __launch_bounds__(kMoveThreads) void dispatch_kernel(
 // ---------------------------------------------------------------------------
 // Layout fused into the dispatch, for small batches (T*K <= kFusedMaxPairs).
 //
-// At a few tokens the step is paced by launches, not bytes (MoRI PR #614,
-// view-cache paragraph: latency flat over hidden 1024..6144 and over 4/8/16
-// tokens).  Here every dispatch workgroup derives, from all T*K ids (at most
-// 8 KB, read from L2), exactly the layout values it needs, so no separate
-// layout launch precedes the dispatch:
+// At a few tokens the step is paced by launches and latency, not bytes (MoRI
+// PR #614, view-cache paragraph: latency flat over hidden 1024..6144 and over
+// 4/8/16 tokens).  Here every dispatch workgroup derives, from all T*K ids (at
+// most 8 KB, read from L2), exactly the layout values it needs, so no
+// separate layout launch precedes the dispatch:
 //   - the per-expert totals (LDS atomics: integer sums, order-free) and their
-//     exclusive scan -> expert offsets;
+//     exclusive scan -> expert offsets (4 experts per thread, DPP wave scan);
 //   - per expert, the number of entries before this workgroup's first token;
 //   - the slots of its own tokens' entries: offset + entries before + rank
 //     among the workgroup's own entries (ballot match-any in one wave).
-// The results are identical to ep_layout's: workgroup 0 writes the counts,
-// offsets, partition sums and status; the workgroup holding a token's first
-// 512-column step writes that token's row_of_pair and src_pair entries.
+// The x vectors are loaded first and quantised while the histogram atomics
+// drain, and the layout outputs are written after the payload stores, so
+// neither sits on the path from the ids to the receive rows.  Workgroup 0
+// writes the counts, offsets, partition sums and status; the workgroup
+// holding a token's first 512-column step writes that token's row_of_pair
+// and src_pair entries.  Every output equals ep_layout's followed by
+// ep_dispatch's.
 struct FusedSmem {
     int32_t ids[kFusedMaxPairs];
     int32_t cnt[kMaxExperts];
@@ -133,6 +149,21 @@ struct FusedSmem {
     int32_t wsum[kMoveWaves];
     uint32_t bad;
 };
+
+constexpr int kFusedIdsPerThread = kFusedMaxPairs / kMoveThreads;   // 8
+static_assert(kFusedIdsPerThread * kMoveThreads == kFusedMaxPairs, "ids split evenly");
+
+// Inclusive scan over the 64 lanes (DPP; lanes without a source add 0).
+__device__ __forceinline__ int wave_inclusive_scan(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+    return v;
+}
 
 template <int kPayload>
 __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
@@ -153,8 +184,9 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
     const int t_lo = item0 / steps_per_token;
     const int t_hi = last / steps_per_token;
     const int p_lo = t_lo * K;
+    const int nq = (t_hi - t_lo + 1) * K;         // <= kMoveWaves * kMaxTopK = 64
 
-    // this wave's x vector is independent of the layout: load it first
+    // every load is independent: x vector and all ids together
     int t = 0, col0 = H;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (item < n_items) {
@@ -162,19 +194,49 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
         col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
         if (col0 < H) v = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + col0);
     }
-
+    int ids[kFusedIdsPerThread];
+#pragma unroll
+    for (int j = 0; j < kFusedIdsPerThread; ++j) {
+        const int p = j * kMoveThreads + tid;
+        ids[j] = (p < n) ? idx[p] : -1;
+    }
     for (int e = tid; e < E; e += kMoveThreads) { s.cnt[e] = 0; s.before[e] = 0; }
     if (tid == 0) s.bad = 0u;
-    for (int p = tid; p < n; p += kMoveThreads) s.ids[p] = idx[p];
+#pragma unroll
+    for (int j = 0; j < kFusedIdsPerThread; ++j) {
+        const int p = j * kMoveThreads + tid;
+        if (p < n) s.ids[p] = ids[j];
+    }
     __syncthreads();
 
-    for (int p = tid; p < n; p += kMoveThreads) {
-        const int e = s.ids[p];
-        if (e >= E) s.bad = 1u;
-        else if (e >= 0) {
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < kFusedIdsPerThread; ++j) {
+        const int p = j * kMoveThreads + tid;
+        const int e = ids[j];
+        bad |= (e >= E);
+        if (e >= 0 && e < E) {
             atomicAdd(&s.cnt[e], 1);
             if (p < p_lo) atomicAdd(&s.before[e], 1);
         }
+    }
+    if (bad) s.bad = 1u;
+    // while the atomics drain: quantise this wave's item, and (wave 0) find the
+    // peers of the workgroup's own entries
+    float scale = 0.0f;
+    uint2 q = make_uint2(0u, 0u);
+    if (item < n_items) q = prepare_item<kPayload>(v, scale);
+    const int me = (w == 0 && lane < nq) ? s.ids[p_lo + lane] : -1;
+    const bool mvalid = (me >= 0) && (me < E);
+    int rank = 0;
+    if (w == 0) {
+        uint64_t peers = __ballot(mvalid);
+        for (int b = 0; b < 10; ++b) {            // ids < kMaxExperts = 2^10
+            const bool bit = (me >> b) & 1;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        rank = lanes_below(peers);
     }
     __syncthreads();
 
@@ -188,14 +250,11 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
         c[j] = (e < E) ? s.cnt[e] : 0;
         sum += c[j];
     }
-    int incl = sum;
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(incl, d, kWave);
-        if (lane >= d) incl += y;
-    }
+    const int incl = wave_inclusive_scan(sum);
     if (lane == kWave - 1) s.wsum[w] = incl;
     __syncthreads();
     int before_wave = 0, N = 0;
+#pragma unroll
     for (int u = 0; u < kMoveWaves; ++u) {
         if (u < w) before_wave += s.wsum[u];
         N += s.wsum[u];
@@ -209,41 +268,15 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
     }
     __syncthreads();
 
-    // slots of this workgroup's own entries (at most 4 tokens x 16 = one wave)
-    const int nq = (t_hi - t_lo + 1) * K;
-    if (w == 0) {
-        const int p = p_lo + lane;
-        const int e = (lane < nq) ? s.ids[p] : -1;
-        const bool valid = (e >= 0) && (e < E);
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < 10; ++b) {            // ids < kMaxExperts = 2^10
-            const bool bit = (e >> b) & 1;
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
-        }
-        if (lane < nq) s.rows[lane] = valid ? s.off[e] + s.before[e] + lanes_below(peers) : -1;
-    }
+    if (w == 0 && lane < nq) s.rows[lane] = mvalid ? s.off[me] + s.before[me] + rank : -1;
     __syncthreads();
 
-    // layout outputs
-    if (blockIdx.x == 0) {
-        for (int e = tid; e < E; e += kMoveThreads) {
-            expert_count[e] = s.cnt[e];
-            expert_offset[e] = s.off[e];
-        }
-        const int L = E / P;
-        for (int q = tid; q < P; q += kMoveThreads) {
-            const int lo = s.off[q * L];
-            const int hi = (q + 1 < P) ? s.off[(q + 1) * L] : N;
-            part_offset[q] = lo;
-            part_count[q] = hi - lo;
-        }
-        if (tid == 0) {
-            expert_offset[E] = N;
-            part_offset[P] = N;
-            *status = s.bad ? 1u : 0u;
-        }
+    if (item < n_items) {
+        const int myrow = (lane < K) ? s.rows[(t - t_lo) * K + lane] : -1;
+        store_item<kPayload, false>(v, q, scale, myrow, col0, lane, H, K, n, recv_x, recv_scales);
     }
+
+    // layout outputs, after the payload stores
     if (tid < nq) {
         const int tt = t_lo + tid / K;
         if (tt * steps_per_token >= item0) {     // this workgroup holds the token's first step
@@ -253,13 +286,30 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
             if (r >= 0 && r < n) src_pair[r] = p;
         }
     }
+    if (blockIdx.x == 0) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int e = tid * kPer + j;
+            if (e < E) {
+                expert_count[e] = c[j];
+                expert_offset[e] = s.off[e];
+            }
+        }
+        const int L = E / P;
+        for (int p = tid; p < P; p += kMoveThreads) {
+            const int lo = s.off[p * L];
+            const int hi = (p + 1 < P) ? s.off[(p + 1) * L] : N;
+            part_offset[p] = lo;
+            part_count[p] = hi - lo;
+        }
+        if (tid == 0) {
+            expert_offset[E] = N;
+            part_offset[P] = N;
+            *status = s.bad ? 1u : 0u;
+        }
+    }
     for (int r = N + blockIdx.x * kMoveThreads + tid; r < n; r += gridDim.x * kMoveThreads)
         src_pair[r] = -1;
-
-    if (item < n_items) {
-        const int myrow = (lane < K) ? s.rows[(t - t_lo) * K + lane] : -1;
-        scatter_item<kPayload, false>(v, myrow, col0, lane, H, K, n, recv_x, recv_scales);
-    }
 }
 
 __global__ __launch_bounds__(256) void e4m3fn_encode_kernel(const float* __restrict__ in, int64_t n,
@@ -317,7 +367,7 @@ hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, in
     const int64_t items = (int64_t)T * steps;
     const int n = T * K;
     const int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
-    if (T == 0 || blocks > kMaxGridBlocks) return hipErrorInvalidValue;
+    if (T == 0 || n > kFusedMaxPairs || blocks > kMaxGridBlocks) return hipErrorInvalidValue;
     if (payload == 0)
         hipLaunchKernelGGL(layout_dispatch_kernel<0>, dim3((unsigned)blocks), dim3(kMoveThreads), 0,
                            stream, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,

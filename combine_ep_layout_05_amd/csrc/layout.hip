@@ -78,7 +78,7 @@ __device__ __forceinline__ void zero_smem(LayoutSmem& s, int E)
 // first free row of expert e; on exit it has moved past this round's entries.
 // Writes row_of_pair for every real entry (-1 when masked) and src_pair for
 // valid ones when src_pair is non-null (rows are below n_rows = T*K).
-__device__ void rank_round(const int32_t* __restrict__ idx, int64_t base, int64_t n,
+__device__ __forceinline__ void rank_round(const int32_t* __restrict__ idx, int64_t base, int64_t n,
                            int64_t n_rows, int E, int nbits, LayoutSmem& s,
                            int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair)
 {
@@ -123,7 +123,7 @@ __device__ void rank_round(const int32_t* __restrict__ idx, int64_t base, int64_
 
 // Exclusive scan of one value per thread over the whole workgroup; *total
 // receives the sum.  Contains barriers: all threads must call it.
-__device__ int block_exclusive_scan(int v, LayoutSmem& s, int* total)
+__device__ __forceinline__ int block_exclusive_scan(int v, LayoutSmem& s, int* total)
 {
     const int tid = threadIdx.x;
     const int lane = tid % kWave, w = tid / kWave;
@@ -152,7 +152,7 @@ __device__ int block_exclusive_scan(int v, LayoutSmem& s, int* total)
 // From per-expert counts (one per thread, tid < E): write expert_count,
 // expert_offset, part_count, part_offset and status; leave the exclusive
 // offsets in s.cursor and N in s.total.
-__device__ void finish_counts(int count, int E, int P, uint32_t bad, LayoutSmem& s, bool write_out,
+__device__ __forceinline__ void finish_counts(int count, int E, int P, uint32_t bad, LayoutSmem& s, bool write_out,
                               int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
                               int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
                               uint32_t* __restrict__ status)
