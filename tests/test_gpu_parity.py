@@ -150,3 +150,23 @@ def test_deterministic_repeat():
     b = run_gpu(wl, d)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_fp8_quotient_sweep():
+    """Blocks whose amax sweeps the whole bf16 range (including scales below
+    2^-90, which take the IEEE-division path, mixed with the shortcut path
+    inside the same wave), with every other element a random bf16 of at most
+    that magnitude: fp8 bytes and scales bit-exact against the oracle."""
+    T, H, K, E, P = 2048, 2048, 1, 8, 1
+    wl = WORKLOADS["tiny_4x1024"].with_(name="fp8_quotient_sweep", T=T, H=H, K=K, E=E, P=P)
+    rng = np.random.default_rng(2024)
+    nblk = T * H // 128
+    amax_code = (1 + (np.arange(nblk, dtype=np.int64) * 997) % 0x7F7F).astype(np.uint16)
+    codes = (rng.random((nblk, 128)) * (amax_code[:, None].astype(np.float64) + 1)).astype(np.uint32)
+    codes = np.minimum(codes, amax_code[:, None]).astype(np.uint16)
+    codes[:, 0] = amax_code
+    signs = (rng.random((nblk, 128)) < 0.5).astype(np.uint16) << 15
+    x = (codes | signs).reshape(T, H)
+    d = dict(idx=(np.arange(T, dtype=np.int32) % E).reshape(T, 1), w=np.ones((T, 1), np.float32),
+             x=x, y=np.zeros((T, H), np.uint16), N=T)
+    _case(wl, d=d)

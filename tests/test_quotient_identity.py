@@ -1,0 +1,34 @@
+"""The fp8 dispatch kernel divides by the block scale with a reciprocal and one
+remainder-correction step instead of an IEEE division per element.  This
+checks, exhaustively over every bf16 input pair, that the shortcut yields the
+same e4m3fn byte as the IEEE-rounded quotient the method specifies (the GPU
+parity tests then compare the kernel itself against the oracle)."""
+import os
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+@pytest.fixture(scope="module")
+def checker(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("qid") / "quotient_identity")
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math",
+                    os.path.join(HERE, "quotient_identity.c"),
+                    os.path.join(ROOT, "oracle", "ep_oracle.c"), "-o", exe, "-lm"], check=True)
+    return exe
+
+
+@pytest.mark.slow
+def test_all_positive_pairs(checker):
+    r = subprocess.run([checker, "1", "0"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout
+    assert "differing bytes 0" in r.stdout
+
+
+def test_negative_pairs_strided(checker):
+    r = subprocess.run([checker, "37", "1"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout
+    assert "differing bytes 0" in r.stdout
