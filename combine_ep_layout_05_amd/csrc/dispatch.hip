@@ -153,18 +153,6 @@ struct FusedSmem {
 constexpr int kFusedIdsPerThread = kFusedMaxPairs / kMoveThreads;   // 8
 static_assert(kFusedIdsPerThread * kMoveThreads == kFusedMaxPairs, "ids split evenly");
 
-// Inclusive scan over the 64 lanes (DPP; lanes without a source add 0).
-__device__ __forceinline__ int wave_inclusive_scan(int v)
-{
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
-    return v;
-}
-
 template <int kPayload>
 __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, int n, int H, int K, int E,

@@ -83,6 +83,20 @@ __device__ __forceinline__ void store8(void* p, uint2 u)
     else *reinterpret_cast<ep_u32x2*>(p) = v;
 }
 
+// Inclusive prefix sum over the 64 lanes (DPP: row_shr 1/2/4/8 within each
+// 16-lane row, then row_bcast 15 / 31 carry the row totals; lanes without a
+// source add 0).
+__device__ __forceinline__ int wave_inclusive_scan(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+    return v;
+}
+
 __device__ __forceinline__ int wave_uniform(int v)
 {
     return __builtin_amdgcn_readfirstlane(v);

@@ -24,8 +24,11 @@
 //     into an exclusive prefix over waves;
 //   - across rounds: a running per-expert cursor in LDS;
 //   - across workgroups (large batches): per-chunk histograms in the
-//     workspace, scanned over chunks by a second kernel, and a third kernel
-//     adds the chunk base to the in-chunk rank.
+//     workspace; each ranking workgroup derives its chunk's per-expert bases
+//     from all chunk histograms (a separate scan launch only above 256
+//     chunks).
+// Every id is loaded once, up front, and the match-any peers found while
+// building the histogram are reused for the ranks.  Scans use DPP wave scans.
 // No atomic's return value ever decides a slot, so the result is the same on
 // every run.  LDS atomics are used only for order-free histogram sums.
 #include "ep_device.h"
@@ -33,6 +36,9 @@
 
 namespace ep {
 namespace {
+
+constexpr int kSmallRounds = kSmallMaxPairs / kLayoutThreads;   // 4
+constexpr int kChunkRounds = kChunkPairs / kLayoutThreads;      // 2
 
 struct LayoutSmem {
     int32_t hist[kMaxExperts];
@@ -73,23 +79,30 @@ __device__ __forceinline__ void zero_smem(LayoutSmem& s, int E)
     if (tid == 0) s.bad = 0u;
 }
 
-// Rank one round of kLayoutThreads pairs [base, base + kLayoutThreads) of the
-// flat entry array (entries >= n are padding).  On entry s.cursor[e] is the
-// first free row of expert e; on exit it has moved past this round's entries.
+// Histogram contribution of one round: the lowest lane of each peer group adds
+// the group's size (order-free integer sums).  Returns the peers for reuse by
+// rank_round.  All threads call it.
+__device__ __forceinline__ uint64_t hist_round(int e, int E, int nbits, int32_t* hist)
+{
+    const bool valid = (e >= 0) && (e < E);
+    const uint64_t peers = match_peers(e, valid, nbits);
+    if (valid && lanes_below(peers) == 0) atomicAdd(&hist[e], (int)__popcll(peers));
+    return peers;
+}
+
+// Rank one round: entry p (this thread's, `real` when p < n) with expert id e
+// and its in-wave peers.  On entry s.cursor[e] is the first free row of
+// expert e; unless `last`, it has moved past this round's entries on exit.
 // Writes row_of_pair for every real entry (-1 when masked) and src_pair for
 // valid ones when src_pair is non-null (rows are below n_rows = T*K).
-__device__ __forceinline__ void rank_round(const int32_t* __restrict__ idx, int64_t base, int64_t n,
-                           int64_t n_rows, int E, int nbits, LayoutSmem& s,
-                           int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair)
+__device__ __forceinline__ void rank_round(int e, int64_t p, bool real, uint64_t peers,
+                                           int64_t n_rows, int E, bool last, LayoutSmem& s,
+                                           int32_t* __restrict__ row_of_pair,
+                                           int32_t* __restrict__ src_pair)
 {
     const int tid = threadIdx.x;
     const int w = tid / kWave;
-    const int64_t p = base + tid;
-    const int e = (p < n) ? idx[p] : -1;
-    const bool valid = (e >= 0) && (e < E);
-    if (p < n && e >= E) s.bad = 1u;           // benign race: every writer stores 1
-
-    const uint64_t peers = match_peers(e, valid, nbits);
+    const bool valid = real && (e >= 0) && (e < E);
     const int rank = lanes_below(peers);
     if (valid && rank == 0) s.wtab[w][e] = (uint16_t)__popcll(peers);
     __syncthreads();
@@ -104,7 +117,7 @@ __device__ __forceinline__ void rank_round(const int32_t* __restrict__ idx, int6
     }
     __syncthreads();
 
-    if (p < n) {
+    if (real) {
         int row = -1;
         if (valid) {
             row = s.cursor[e] + (int)s.wtab[w][e] + rank;
@@ -112,6 +125,7 @@ __device__ __forceinline__ void rank_round(const int32_t* __restrict__ idx, int6
         }
         row_of_pair[p] = row;
     }
+    if (last) return;
     __syncthreads();
 
     if (tid < E) {
@@ -127,19 +141,11 @@ __device__ __forceinline__ int block_exclusive_scan(int v, LayoutSmem& s, int* t
 {
     const int tid = threadIdx.x;
     const int lane = tid % kWave, w = tid / kWave;
-    int x = v;
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(x, d, kWave);
-        if (lane >= d) x += y;
-    }
+    const int x = wave_inclusive_scan(v);
     if (lane == kWave - 1) s.wsum[w] = x;
     __syncthreads();
     if (w == 0) {
-        int t = lane < kLayoutWaves ? s.wsum[lane] : 0;
-        for (int d = 1; d < kLayoutWaves; d <<= 1) {
-            const int y = __shfl_up(t, d, kWave);
-            if (lane >= d) t += y;
-        }
+        const int t = wave_inclusive_scan(lane < kLayoutWaves ? s.wsum[lane] : 0);
         if (lane < kLayoutWaves) s.wsum[lane] = t;   // inclusive prefix of wave sums
     }
     __syncthreads();
@@ -195,18 +201,28 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
     __shared__ LayoutSmem s;
     const int tid = threadIdx.x;
     const int nbits = id_bits(E);
+    const int rounds = (int)((n + kLayoutThreads - 1) / kLayoutThreads);
+    int ids[kSmallRounds];
+#pragma unroll
+    for (int r = 0; r < kSmallRounds; ++r) {
+        const int64_t p = (int64_t)r * kLayoutThreads + tid;
+        ids[r] = (p < n) ? idx[p] : -1;
+    }
     zero_smem(s, E);
     __syncthreads();
 
-    // pass 1: histogram (order-free sums; one LDS atomic per peer group)
-    for (int64_t base = 0; base < n; base += kLayoutThreads) {
-        const int64_t p = base + tid;
-        const int e = (p < n) ? idx[p] : -1;
-        const bool valid = (e >= 0) && (e < E);
-        if (p < n && e >= E) s.bad = 1u;
-        const uint64_t peers = match_peers(e, valid, nbits);
-        if (valid && lanes_below(peers) == 0) atomicAdd(&s.hist[e], (int)__popcll(peers));
+    // pass 1: histogram
+    uint64_t peers[kSmallRounds];
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < kSmallRounds; ++r) {
+        peers[r] = 0ull;
+        if (r < rounds) {
+            bad |= ids[r] >= E;
+            peers[r] = hist_round(ids[r], E, nbits, s.hist);
+        }
     }
+    if (bad) s.bad = 1u;
     __syncthreads();
 
     finish_counts(tid < E ? s.hist[tid] : 0, E, P, s.bad, s, true, expert_count, expert_offset,
@@ -214,8 +230,13 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
     __syncthreads();
 
     // pass 2: deterministic slots
-    for (int64_t base = 0; base < n; base += kLayoutThreads)
-        rank_round(idx, base, n, n, E, nbits, s, row_of_pair, src_pair);
+#pragma unroll
+    for (int r = 0; r < kSmallRounds; ++r) {
+        if (r < rounds) {
+            const int64_t p = (int64_t)r * kLayoutThreads + tid;
+            rank_round(ids[r], p, p < n, peers[r], n, E, r == rounds - 1, s, row_of_pair, src_pair);
+        }
+    }
 
     for (int64_t r = (int64_t)s.total + tid; r < n; r += kLayoutThreads) src_pair[r] = -1;
 }
@@ -234,19 +255,24 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_hist_kernel(
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
     const int nbits = id_bits(E);
+    const int64_t c0 = (int64_t)chunk * kChunkPairs;
+    const int64_t c1 = (c0 + kChunkPairs < n) ? c0 + kChunkPairs : n;
+    int ids[kChunkRounds];
+#pragma unroll
+    for (int r = 0; r < kChunkRounds; ++r) {
+        const int64_t p = c0 + (int64_t)r * kLayoutThreads + tid;
+        ids[r] = (p < c1) ? idx[p] : -1;
+    }
     if (tid < E) hist[tid] = 0;
     if (tid == 0) bad = 0u;
     __syncthreads();
-    const int64_t c0 = (int64_t)chunk * kChunkPairs;
-    const int64_t c1 = (c0 + kChunkPairs < n) ? c0 + kChunkPairs : n;
-    for (int64_t base = c0; base < c1; base += kLayoutThreads) {
-        const int64_t p = base + tid;
-        const int e = (p < c1) ? idx[p] : -1;
-        const bool valid = (e >= 0) && (e < E);
-        if (p < c1 && e >= E) bad = 1u;
-        const uint64_t peers = match_peers(e, valid, nbits);
-        if (valid && lanes_below(peers) == 0) atomicAdd(&hist[e], (int)__popcll(peers));
+    bool b = false;
+#pragma unroll
+    for (int r = 0; r < kChunkRounds; ++r) {
+        b |= ids[r] >= E;
+        (void)hist_round(ids[r], E, nbits, hist);
     }
+    if (b) bad = 1u;
     __syncthreads();
     if (tid < E) ws_hist[(int64_t)chunk * E + tid] = hist[tid];
     if (tid == 0) ws_bad[chunk] = bad;
@@ -316,6 +342,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
     const int nbits = id_bits(E);
+    const int64_t c0 = (int64_t)chunk * kChunkPairs;
+    const int64_t c1 = (c0 + kChunkPairs < n) ? c0 + kChunkPairs : n;
+    int ids[kChunkRounds];
+#pragma unroll
+    for (int r = 0; r < kChunkRounds; ++r) {
+        const int64_t p = c0 + (int64_t)r * kLayoutThreads + tid;
+        ids[r] = (p < c1) ? idx[p] : -1;
+    }
     zero_smem(s, E);
     __syncthreads();
 
@@ -349,10 +383,17 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     }
     __syncthreads();
 
-    const int64_t c0 = (int64_t)chunk * kChunkPairs;
-    const int64_t c1 = (c0 + kChunkPairs < n) ? c0 + kChunkPairs : n;
-    for (int64_t base = c0; base < c1; base += kLayoutThreads)
-        rank_round(idx, base, c1, n, E, nbits, s, row_of_pair, src_pair);
+    const int rounds = (int)((c1 - c0 + kLayoutThreads - 1) / kLayoutThreads);
+#pragma unroll
+    for (int r = 0; r < kChunkRounds; ++r) {
+        if (r < rounds) {
+            const int64_t p = c0 + (int64_t)r * kLayoutThreads + tid;
+            const bool valid = ids[r] >= 0 && ids[r] < E;
+            const uint64_t peers = match_peers(ids[r], valid, nbits);
+            rank_round(ids[r], p, p < c1, peers, n, E, r == rounds - 1, s, row_of_pair,
+                       src_pair);
+        }
+    }
 
     const int64_t stride = (int64_t)gridDim.x * kLayoutThreads;
     for (int64_t r = (int64_t)s.total + (int64_t)chunk * kLayoutThreads + tid; r < n; r += stride)
