@@ -21,7 +21,7 @@ constexpr int kLayoutThreads = 1024;       // one pair per thread per round
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kMaxExperts = 1024;          // one expert column per thread
 constexpr int kSmallMaxPairs = 4096;       // single-workgroup layout up to this
-constexpr int kChunkPairs = 2048;          // pairs per workgroup above it
+constexpr int kChunkPairs = 1024;          // pairs per workgroup above it
 constexpr int kMaxChunksTwoPass = 256;     // above: a separate scan launch
 static_assert(kMaxExperts <= kLayoutThreads, "scan assigns one expert per thread");
 static_assert(kChunkPairs % kLayoutThreads == 0, "a chunk is whole rounds");
