@@ -192,6 +192,32 @@ def time_steps(p, steps, warmup, mode, phase="step"):
     return e0.elapsed_time(e1) * 1e3 / (launches * per)
 
 
+def single_step_us(p, reps, flush_bytes=0, phase="step"):
+    """Median device time of one step (a one-step graph between two events),
+    each step preceded -- outside the events -- by a write of flush_bytes that
+    evicts the step's data from L2 and the memory-side cache (cold), or by
+    nothing (warm).  The flush keeps the GPU busy while the host enqueues the
+    events and the graph, so no host time is inside the events."""
+    torch = p.torch
+    g = p.capture(phase, 1)
+    flush = torch.empty(max(flush_bytes, 1), dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for i in range(reps + 2):
+        if flush_bytes:
+            with torch.cuda.stream(p.stream):
+                flush.fill_(i & 0xFF)
+        e0.record(p.stream)
+        g.launch(p.stream)
+        e1.record(p.stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(e0.elapsed_time(e1) * 1e3)
+    g.destroy()
+    del flush
+    return float(np.median(times))
+
+
 def measure(wl, steps, warmup, mode="graph", phase="step"):
     p = Path(wl)
     b = algo_bytes(wl, p.N)
@@ -250,6 +276,8 @@ def main():
     p, b, us = measure(wl, args.steps, args.warmup, mode=mode, phase=step)
     eager_us = time_steps(p, 500, 20, "eager", step)
     graph1_us = time_steps(p, 1000, 20, "graph1", step)
+    warm1_us = single_step_us(p, 50, 0, step)
+    cold1_us = single_step_us(p, 50, 512 << 20, step)
     phases = {ph: p.phase_us(ph) for ph in ("layout_dispatch", "layout", "dispatch", "combine")}
     b["layout_dispatch"] = b["dispatch"]
     cand = ("dispatch", "combine") if args.unfused else ("layout_dispatch", "combine")
@@ -289,6 +317,7 @@ def main():
         "phases_us": {k: round(v, 3) for k, v in phases.items()},
         "eager_us_per_step": round(eager_us, 3),
         "graph1_us_per_step": round(graph1_us, 3),
+        "single_step_us": {"warm": round(warm1_us, 3), "cold_after_512MB_write": round(cold1_us, 3)},
         "roofline": roof,
     }
 

@@ -19,14 +19,23 @@ import numpy as np
 from . import build as _build
 
 _lib = None
+_lib_path = None
+
+
+def use_library(path=None):
+    """Load the oracle from another build of ep_oracle.c (tests that plant a
+    mistake in a copy of the oracle use this); None restores the default."""
+    global _lib, _lib_path
+    _lib, _lib_path = None, path
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = _lib_path or _build.LIB
+        if _lib_path is None and not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64 = ctypes.c_int, ctypes.c_int64
         L.oracle_layout.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P]

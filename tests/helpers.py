@@ -23,7 +23,8 @@ def table_encode_e4m3fn(v32: np.ndarray) -> np.ndarray:
     """Nearest representable E4M3 value by search over the value table; ties go
     to the even code; |v| >= 448 saturates to 0x7E; NaN -> 0x7F; sign kept."""
     v = np.asarray(v32, dtype=np.float32)
-    a = np.abs(v.astype(np.float64))
+    with np.errstate(invalid="ignore"):
+        a = np.abs(v.astype(np.float64))
     sign = np.signbit(v).astype(np.uint8) << 7
     i = np.searchsorted(E4M3_VALUES, a)            # first value >= a
     hi = np.clip(i, 0, 126)
@@ -110,3 +111,29 @@ def brute_layout(idx: np.ndarray, E: int, P: int):
     return dict(expert_count=count, expert_offset=offset, part_count=part_count,
                 part_offset=part_offset, row_of_pair=row_of_pair, src_pair=src_pair,
                 status=np.array([status]))
+
+
+# ------------------------------------------------------- vectorised exact fmaf
+def fmaf_exact_np(a, b, c) -> np.ndarray:
+    """fp32 fma(a, b, c) with one rounding, vectorised: a*b is exact in fp64
+    (24 + 24 bits), p + c is held exactly as a double-double (TwoSum), and the
+    pair is rounded to fp32.  Rounding hi alone is correct unless hi is exactly
+    an fp32 rounding midpoint, where the sign of lo decides."""
+    a = np.asarray(a, np.float32).astype(np.float64)
+    b = np.asarray(b, np.float32).astype(np.float64)
+    c = np.asarray(c, np.float32).astype(np.float64)
+    p = a * b
+    hi = p + c
+    bb = hi - p
+    lo = (p - (hi - bb)) + (c - bb)
+    r = hi.astype(np.float32)
+    up = np.nextafter(r, np.float32(np.inf))
+    dn = np.nextafter(r, np.float32(-np.inf))
+    rd = r.astype(np.float64)
+    mid_up = (rd + up.astype(np.float64)) * 0.5      # exact: fp32 neighbours fit in fp64
+    mid_dn = (rd + dn.astype(np.float64)) * 0.5
+    # hi sits on the midpoint above r (rounded down to even r) and lo > 0: round up
+    r = np.where((hi == mid_up) & (lo > 0), up, r)
+    # hi sits on the midpoint below r (rounded up to even r) and lo < 0: round down
+    r = np.where((hi == mid_dn) & (lo < 0), dn, r)
+    return r.astype(np.float32)

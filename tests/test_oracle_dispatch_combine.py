@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from tests.helpers import (bf16_to_f32, bf16_ulp_distance, decode_e4m3fn, exact_fmaf,
-                           table_encode_e4m3fn)
+                           fmaf_exact_np, table_encode_e4m3fn)
 from workloads import WORKLOADS, generate
 from workloads.gen import to_bf16_bits
 
@@ -141,6 +141,44 @@ def test_combine_exact_rational_small():
             want = to_bf16_bits(np.array([acc], np.float32))[0]
             assert got[t, c] == want, (t, c)
     assert np.all(got[4] == 0)                            # all masked -> +0
+
+
+def test_vectorised_fmaf_matches_exact_rationals():
+    """The numpy fmaf used below, against exact rational arithmetic, on random
+    operands and on operands built to land on fp32 rounding midpoints."""
+    rng = np.random.default_rng(17)
+    a = rng.standard_normal(3000).astype(np.float32)
+    b = rng.standard_normal(3000).astype(np.float32)
+    c = rng.standard_normal(3000).astype(np.float32) * np.float32(4.0)
+    # midpoint cases: a*b exactly half an ulp of c plus/minus a tiny excess
+    c2 = np.float32(1.0) + np.arange(1, 1001, dtype=np.float32) * np.float32(2.0 ** -20)
+    a2 = np.full(1000, 2.0 ** -24, np.float32)
+    b2 = np.where(np.arange(1000) % 3 == 0, 1.0, np.where(np.arange(1000) % 3 == 1, 1.0 + 2.0 ** -23,
+                                                          1.0 - 2.0 ** -24)).astype(np.float32)
+    a, b, c = np.concatenate([a, a2, -a2]), np.concatenate([b, b2, b2]), np.concatenate([c, c2, c2])
+    got = fmaf_exact_np(a, b, c)
+    for i in range(a.size):
+        assert got[i] == exact_fmaf(a[i], b[i], c[i]), i
+
+
+@pytest.mark.parametrize("name", ["ll_128x7168", "tiny_4x1024"])
+def test_combine_bit_exact_at_full_size(name):
+    """Bit-exact pin at full size: the fmaf chain in k order from +0 (masked
+    entries skipped), evaluated with the vectorised exact fmaf, then torch's
+    bf16 rounding."""
+    wl = WORKLOADS[name]
+    d = generate(wl)
+    lo = oracle.layout(d["idx"], wl.E, wl.P)
+    got = oracle.combine(d["y"], lo["row_of_pair"], d["w"], wl.T, wl.H, wl.K)
+    rop = lo["row_of_pair"].reshape(wl.T, wl.K)
+    yf = bf16_to_f32(d["y"])
+    acc = np.zeros((wl.T, wl.H), np.float32)
+    for k in range(wl.K):
+        r = rop[:, k]
+        valid = r >= 0
+        upd = fmaf_exact_np(np.broadcast_to(d["w"][:, k:k + 1], acc.shape), yf[np.maximum(r, 0)], acc)
+        acc = np.where(valid[:, None], upd, acc)
+    np.testing.assert_array_equal(got, to_bf16_bits(acc))
 
 
 def test_combine_fp64_bound_full_size():
