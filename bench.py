@@ -100,6 +100,22 @@ class Path:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / launches      # us per launch
 
+    def time_eager_bound(self, iters, warmup=3):
+        """Eager steps through a BoundStep (arguments marshalled once)."""
+        torch = self.torch
+        bs = self.ep.BoundStep(self.buf, self.idx, self.x, self.y, self.w, self.stream)
+        for _ in range(warmup):
+            bs.step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(iters):
+            bs.step()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / iters
+
     def time_eager(self, iters, warmup=3, phase="step"):
         torch = self.torch
         for _ in range(warmup):
@@ -192,28 +208,29 @@ def time_steps(p, steps, warmup, mode, phase="step"):
     return e0.elapsed_time(e1) * 1e3 / (launches * per)
 
 
-def single_step_us(p, reps, flush_bytes=0, phase="step"):
-    """Median device time of one step (a one-step graph between two events),
-    each step preceded -- outside the events -- by a write of flush_bytes that
-    evicts the step's data from L2 and the memory-side cache (cold), or by
-    nothing (warm).  The flush keeps the GPU busy while the host enqueues the
-    events and the graph, so no host time is inside the events."""
+def single_step_us(p, reps, flush_bytes=0):
+    """Median device time of one step (a BoundStep's two launches between two
+    events), each step preceded -- outside the events -- by a write of
+    flush_bytes that evicts the step's data from L2 and the memory-side cache
+    (cold), or by nothing (warm); then a bounded GPU spin keeps the GPU busy
+    while the host enqueues the events and the step, so no host time is inside
+    the events."""
     torch = p.torch
-    g = p.capture(phase, 1)
+    bs = p.ep.BoundStep(p.buf, p.idx, p.x, p.y, p.w, p.stream)
     flush = torch.empty(max(flush_bytes, 1), dtype=torch.uint8, device="cuda")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     times = []
     for i in range(reps + 2):
-        if flush_bytes:
-            with torch.cuda.stream(p.stream):
+        with torch.cuda.stream(p.stream):
+            if flush_bytes:
                 flush.fill_(i & 0xFF)
+            torch.cuda._sleep(200000)       # bounded spin: the GPU stays busy while the host enqueues
         e0.record(p.stream)
-        g.launch(p.stream)
+        bs.step()
         e1.record(p.stream)
         torch.cuda.synchronize()
         if i >= 2:
             times.append(e0.elapsed_time(e1) * 1e3)
-    g.destroy()
     del flush
     return float(np.median(times))
 
@@ -275,9 +292,10 @@ def main():
     mode = "eager" if args.eager else "graph"
     p, b, us = measure(wl, args.steps, args.warmup, mode=mode, phase=step)
     eager_us = time_steps(p, 500, 20, "eager", step)
+    eager_bound_us = p.time_eager_bound(500, 20) if step == "step" else None
     graph1_us = time_steps(p, 1000, 20, "graph1", step)
-    warm1_us = single_step_us(p, 50, 0, step)
-    cold1_us = single_step_us(p, 50, 512 << 20, step)
+    warm1_us = single_step_us(p, 50, 0)
+    cold1_us = single_step_us(p, 50, 512 << 20)
     phases = {ph: p.phase_us(ph) for ph in ("layout_dispatch", "layout", "dispatch", "combine")}
     b["layout_dispatch"] = b["dispatch"]
     cand = ("dispatch", "combine") if args.unfused else ("layout_dispatch", "combine")
@@ -316,6 +334,7 @@ def main():
         "bytes_per_step": b["step"],
         "phases_us": {k: round(v, 3) for k, v in phases.items()},
         "eager_us_per_step": round(eager_us, 3),
+        "eager_bound_us_per_step": None if eager_bound_us is None else round(eager_bound_us, 3),
         "graph1_us_per_step": round(graph1_us, 3),
         "single_step_us": {"warm": round(warm1_us, 3), "cold_after_512MB_write": round(cold1_us, 3)},
         "roofline": roof,
@@ -327,6 +346,7 @@ def main():
         tg["sweep_4x6144_us_per_step_graph"] = round(us4, 3)
         tg["sweep_4x6144_us_per_step_graph1"] = round(time_steps(pw, 1000, 20, "graph1"), 3)
         tg["sweep_4x6144_us_per_step_eager"] = round(time_steps(pw, 500, 20, "eager"), 3)
+        tg["sweep_4x6144_us_per_step_eager_bound"] = round(pw.time_eager_bound(500, 20), 3)
         tg["sweep_4x6144_target_us"] = 15.0
         for tt in (8, 16):
             tg["sweep_%dx6144_us_per_step_graph" % tt] = round(

@@ -229,3 +229,52 @@ class EpBuffers:
     def combine(self, expert_out, topk_w, stream=None):
         ep_combine(expert_out, self.row_of_pair, topk_w, self.out, stream)
         return self.out
+
+
+class BoundStep:
+    """ep_layout_dispatch + ep_combine with every argument marshalled once.
+
+    For a serving loop whose buffers never move: the pointers, sizes and stream
+    are converted to ctypes values at bind time, so each call is a single
+    foreign call with no per-call tensor inspection (the host-side cost that
+    paces the GPU at a few tokens; MoRI PR #614, view-cache paragraph).  The
+    library still checks every argument on each call.
+    """
+
+    def __init__(self, buf, topk_idx, x, expert_out, topk_w, stream=None):
+        _dt(topk_idx, torch.int32)
+        _dt(x, torch.bfloat16, torch.int16, torch.uint16)
+        _dt(expert_out, torch.bfloat16, torch.int16, torch.uint16)
+        _dt(topk_w, torch.float32)
+        T, K = topk_idx.shape
+        if (T, K) != (buf.T, buf.K) or tuple(x.shape) != (buf.T, buf.H) or \
+                tuple(topk_w.shape) != (buf.T, buf.K) or tuple(expert_out.shape) != (buf.T * buf.K, buf.H):
+            raise ValueError("tensor shapes do not match the buffers")
+        self._keep = (buf, topk_idx, x, expert_out, topk_w, stream)   # keep the memory alive
+        s = _stream(stream)
+        ws_bytes = buf.ws.numel()
+        self._ld = (_ptr(topk_idx), _ptr(x), T, buf.H, K, buf.E, buf.P, PAYLOADS[buf.payload],
+                    _ptr(buf.expert_count), _ptr(buf.expert_offset), _ptr(buf.part_count),
+                    _ptr(buf.part_offset), _ptr(buf.row_of_pair), _ptr(buf.src_pair),
+                    _ptr(buf.status), _ptr(buf.ws), ws_bytes, _ptr(buf.recv_x),
+                    _ptr(buf.recv_scales), s)
+        self._cb = (_ptr(expert_out), _ptr(buf.row_of_pair), _ptr(topk_w), T, buf.H, K,
+                    _ptr(buf.out), s)
+        self._f_ld, self._f_cb = _lib.ep_layout_dispatch, _lib.ep_combine
+
+    def layout_dispatch(self):
+        rc = self._f_ld(*self._ld)
+        if rc:
+            raise EpError("ep_layout_dispatch", rc)
+
+    def combine(self):
+        rc = self._f_cb(*self._cb)
+        if rc:
+            raise EpError("ep_combine", rc)
+
+    def step(self):
+        rc = self._f_ld(*self._ld)
+        if rc == 0:
+            rc = self._f_cb(*self._cb)
+        if rc:
+            raise EpError("ep_layout_dispatch/ep_combine", rc)

@@ -170,3 +170,24 @@ def test_fp8_quotient_sweep():
     d = dict(idx=(np.arange(T, dtype=np.int32) % E).reshape(T, 1), w=np.ones((T, 1), np.float32),
              x=x, y=np.zeros((T, H), np.uint16), N=T)
     _case(wl, d=d)
+
+
+def test_bound_step_matches_oracle():
+    """BoundStep (arguments marshalled once) gives the same outputs as the
+    oracle, call after call."""
+    import torch
+    import combine_ep_layout_05_amd as ep
+    from tests.pathrun import collect, to_dev
+    wl = WORKLOADS["ll_128x7168"]
+    d = generate(wl, seed=wl.seed + 7)
+    buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    idx, w = to_dev(d["idx"]), to_dev(d["w"])
+    x = to_dev(d["x"].view(np.int16), torch.bfloat16)
+    y = to_dev(d["y"].view(np.int16), torch.bfloat16)
+    bs = ep.BoundStep(buf, idx, x, y, w)
+    ref = run_oracle(wl, d)
+    for _ in range(3):
+        buf.out.zero_()
+        bs.step()
+        torch.cuda.synchronize()
+        assert compare(wl, collect(buf), ref, check_poison=False) == 0
