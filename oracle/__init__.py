@@ -50,6 +50,12 @@ def lib():
         L.oracle_e4m3fn_encode_array.restype = None
         L.oracle_bf16_rne_array.argtypes = [P, i64, P]
         L.oracle_bf16_rne_array.restype = None
+        L.oracle_dedup_layout.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P]
+        L.oracle_dedup_layout.restype = i32
+        L.oracle_combine_partial.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P]
+        L.oracle_combine_partial.restype = i32
+        L.oracle_combine_reduce.argtypes = [P, P, i32, i32, i32, P]
+        L.oracle_combine_reduce.restype = i32
         L.oracle_e4m3fn_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3fn_decode.restype = ctypes.c_float
         _lib = L
@@ -157,4 +163,46 @@ def bf16_rne(values_f32):
     v = _c(values_f32, np.float32).reshape(-1)
     out = np.empty(v.shape, np.uint16)
     lib().oracle_bf16_rne_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def dedup_layout(topk_idx, E, P):
+    """Per-destination deduplicated layout (one row per (token, partition))."""
+    idx = _c(topk_idx, np.int32)
+    T, K = idx.shape
+    out = dict(tp_row=np.zeros(T * P, np.int32), part_tokens=np.zeros(P, np.int32),
+               part_token_offset=np.zeros(P + 1, np.int32), tp_src=np.zeros(T * P, np.int32),
+               kmask=np.zeros(T * P, np.uint32), status=np.zeros(1, np.uint32))
+    rc = lib().oracle_dedup_layout(_ptr(idx), T, K, E, P,
+                                   *[_ptr(out[k]) for k in ("tp_row", "part_tokens", "part_token_offset",
+                                                            "tp_src", "kmask", "status")])
+    if rc != 0:
+        raise OracleError("oracle_dedup_layout rejected T=%d K=%d E=%d P=%d" % (T, K, E, P))
+    return out
+
+
+def combine_partial(y_bf16, row_of_pair, topk_w, tp_row, kmask, T, H, K, P, rows=None):
+    """Level 1 of the two-level combine: bf16 partial per (token, partition) row."""
+    y = _c(y_bf16, np.uint16)
+    rop = _c(row_of_pair, np.int32).reshape(-1)
+    w = _c(topk_w, np.float32).reshape(-1)
+    tr = _c(tp_row, np.int32).reshape(-1)
+    km = _c(kmask, np.uint32).reshape(-1)
+    rows = T * P if rows is None else rows
+    part = np.zeros((rows, H), np.uint16)
+    rc = lib().oracle_combine_partial(_ptr(y), _ptr(rop), _ptr(w), _ptr(tr), _ptr(km), T, H, K, P,
+                                      _ptr(part))
+    if rc != 0:
+        raise OracleError("oracle_combine_partial rejected")
+    return part
+
+
+def combine_reduce(partial_bf16, tp_row, T, H, P):
+    """Level 2: fp32 sum of a token's partials in partition order -> bf16."""
+    part = _c(partial_bf16, np.uint16)
+    tr = _c(tp_row, np.int32).reshape(-1)
+    out = np.zeros((T, H), np.uint16)
+    rc = lib().oracle_combine_reduce(_ptr(part), _ptr(tr), T, H, P, _ptr(out))
+    if rc != 0:
+        raise OracleError("oracle_combine_reduce rejected")
     return out

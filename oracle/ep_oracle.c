@@ -297,3 +297,109 @@ int oracle_combine(const uint16_t* y, const int32_t* row_of_pair, const float* w
 {
     return oracle_combine_range(y, row_of_pair, w, T, H, K, 0, T, out);
 }
+
+/*
+ * Per-destination deduplicated layout (a token travels once to each partition
+ * that holds any of its valid experts; UCCL PR #749: tokens batched per
+ * destination; MoRI PR #614, DispatchIntraNode paragraph: the dispatch
+ * de-duplicates a token's copies per destination).
+ *
+ *  kmask[t*P+p]        = bit k set iff idx[t,k] is a valid id in partition p
+ *  present(t,p)        = kmask[t*P+p] != 0
+ *  part_tokens[p]      = #{t : present(t,p)}
+ *  part_token_off[0]=0, part_token_off[p+1] = part_token_off[p] + part_tokens[p]; M = part_token_off[P]
+ *  tp_row[t*P+p]       = part_token_off[p] + #{t' < t : present(t',p)}, or -1
+ *  tp_src[row]         = t*P+p for row < M, -1 for row in [M, T*P)
+ *  status bit 0        = some id >= E
+ */
+int oracle_dedup_layout(const int32_t* idx, int T, int K, int E, int P,
+                        int32_t* tp_row, int32_t* part_tokens, int32_t* part_token_off,
+                        int32_t* tp_src, uint32_t* kmask, uint32_t* status)
+{
+    if (check_routing(T, K, E, P) != ORACLE_OK || P > 16)
+        return ORACLE_EINVAL;
+    const int L = E / P;
+    uint32_t st = 0;
+    for (int64_t i = 0; i < (int64_t)T * P; ++i) kmask[i] = 0;
+    for (int t = 0; t < T; ++t)
+        for (int k = 0; k < K; ++k) {
+            int32_t e = idx[(int64_t)t * K + k];
+            if (e < 0) continue;
+            if (e >= E) { st |= 1u; continue; }
+            kmask[(int64_t)t * P + e / L] |= 1u << k;
+        }
+    for (int p = 0; p < P; ++p) {
+        int32_t c = 0;
+        for (int t = 0; t < T; ++t) c += kmask[(int64_t)t * P + p] != 0;
+        part_tokens[p] = c;
+    }
+    part_token_off[0] = 0;
+    for (int p = 0; p < P; ++p) part_token_off[p + 1] = part_token_off[p] + part_tokens[p];
+    const int64_t M = part_token_off[P];
+    for (int p = 0; p < P; ++p) {
+        int32_t cursor = part_token_off[p];
+        for (int t = 0; t < T; ++t) {
+            int64_t i = (int64_t)t * P + p;
+            if (kmask[i] == 0) { tp_row[i] = -1; continue; }
+            tp_row[i] = cursor;
+            tp_src[cursor] = (int32_t)i;
+            ++cursor;
+        }
+    }
+    for (int64_t r = M; r < (int64_t)T * P; ++r) tp_src[r] = -1;
+    *status = st;
+    return ORACLE_OK;
+}
+
+/*
+ * Two-level combine, level 1 (at the destination): for every present (t,p),
+ * acc = 0.0f, then acc = fmaf(w[t,k], y[row_of_pair[t,k], c], acc) for the k
+ * of kmask[t*P+p] in ascending order; partial[tp_row[t,p], c] = bf16_rne(acc).
+ * y is in the pair-row layout of the plain dispatch.
+ */
+int oracle_combine_partial(const uint16_t* y, const int32_t* row_of_pair, const float* w,
+                           const int32_t* tp_row, const uint32_t* kmask,
+                           int T, int H, int K, int P, uint16_t* partial)
+{
+    if (T < 0 || H <= 0 || K < 1 || K > 16 || P < 1 || P > 16)
+        return ORACLE_EINVAL;
+    for (int t = 0; t < T; ++t)
+        for (int p = 0; p < P; ++p) {
+            int64_t i = (int64_t)t * P + p;
+            int32_t dst = tp_row[i];
+            if (dst < 0) continue;
+            for (int c = 0; c < H; ++c) {
+                float acc = 0.0f;
+                for (int k = 0; k < K; ++k) {
+                    if (!(kmask[i] >> k & 1u)) continue;
+                    int32_t r = row_of_pair[(int64_t)t * K + k];
+                    acc = fmaf(w[(int64_t)t * K + k], oracle_bf16_to_f32(y[(int64_t)r * H + c]), acc);
+                }
+                partial[(int64_t)dst * H + c] = oracle_bf16_rne(acc);
+            }
+        }
+    return ORACLE_OK;
+}
+
+/*
+ * Two-level combine, level 2 (at the source): acc = 0.0f, then
+ * acc = acc + partial[tp_row[t,p], c] for p ascending over present (t,p)
+ * (fp32 adds); out[t,c] = bf16_rne(acc).  A token present nowhere gives +0.
+ */
+int oracle_combine_reduce(const uint16_t* partial, const int32_t* tp_row, int T, int H, int P,
+                          uint16_t* out)
+{
+    if (T < 0 || H <= 0 || P < 1 || P > 16)
+        return ORACLE_EINVAL;
+    for (int t = 0; t < T; ++t)
+        for (int c = 0; c < H; ++c) {
+            float acc = 0.0f;
+            for (int p = 0; p < P; ++p) {
+                int32_t r = tp_row[(int64_t)t * P + p];
+                if (r < 0) continue;
+                acc = acc + oracle_bf16_to_f32(partial[(int64_t)r * H + c]);
+            }
+            out[(int64_t)t * H + c] = oracle_bf16_rne(acc);
+        }
+    return ORACLE_OK;
+}

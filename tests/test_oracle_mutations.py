@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 from oracle import build as obuild
+from tests import test_oracle_dedup as tdd
 from tests import test_oracle_dispatch_combine as tdc
 from tests import test_oracle_layout as tlay
 from tests import test_oracle_numerics as tnum
@@ -27,7 +28,8 @@ MUTANTS = [
     ("bf16 ties rounded up", "if (discarded > 0x8000u || (discarded == 0x8000u && (hi & 1u)))",
      "if (discarded >= 0x8000u)"),
     ("bf16 truncation", "        hi = (uint16_t)(hi + 1u);", "        hi = hi;"),
-    ("bad id does not set status", "if (e >= E) { st |= 1u; continue; }", "if (e >= E) { continue; }"),
+    ("bad id does not set status", "if (e >= E) { st |= 1u; continue; }\n        expert_count[e] += 1;",
+     "if (e >= E) { continue; }\n        expert_count[e] += 1;"),
     ("partition offset one expert late", "part_offset[p] = expert_offset[p * L];",
      "part_offset[p] = expert_offset[p * L + (p * L + 1 <= E ? 1 : 0)];"),
     ("slots filled from the back of each expert", "int32_t r = cursor[e]++;",
@@ -42,9 +44,21 @@ MUTANTS = [
      "oracle_e4m3fn_encode(oracle_bf16_to_f32(xb[j]) * (1.0f / scale));"),
     ("combine in reverse k order", "            for (int k = 0; k < K; ++k) {\n                int32_t r = row_of_pair[(int64_t)t * K + k];\n                if (r < 0) continue;\n                acc = fmaf",
      "            for (int k = K - 1; k >= 0; --k) {\n                int32_t r = row_of_pair[(int64_t)t * K + k];\n                if (r < 0) continue;\n                acc = fmaf"),
-    ("combine multiply then add", "acc = fmaf(w[(int64_t)t * K + k], oracle_bf16_to_f32(y[(int64_t)r * H + c]), acc);",
-     "acc = w[(int64_t)t * K + k] * oracle_bf16_to_f32(y[(int64_t)r * H + c]) + acc;"),
-    ("combine uses weight k=0 for every k", "acc = fmaf(w[(int64_t)t * K + k],", "acc = fmaf(w[(int64_t)t * K],"),
+    ("combine multiply then add",
+     "acc = fmaf(w[(int64_t)t * K + k], oracle_bf16_to_f32(y[(int64_t)r * H + c]), acc);\n            }\n            out[",
+     "acc = w[(int64_t)t * K + k] * oracle_bf16_to_f32(y[(int64_t)r * H + c]) + acc;\n            }\n            out["),
+    ("combine uses weight k=0 for every k",
+     "acc = fmaf(w[(int64_t)t * K + k], oracle_bf16_to_f32(y[(int64_t)r * H + c]), acc);\n            }\n            out[",
+     "acc = fmaf(w[(int64_t)t * K], oracle_bf16_to_f32(y[(int64_t)r * H + c]), acc);\n            }\n            out["),
+    ("dedup mask records k+1", "kmask[(int64_t)t * P + e / L] |= 1u << k;",
+     "kmask[(int64_t)t * P + e / L] |= 1u << ((k + 1) % K);"),
+    ("dedup rows token-descending", "        for (int t = 0; t < T; ++t) {\n            int64_t i = (int64_t)t * P + p;",
+     "        for (int t = T - 1; t >= 0; --t) {\n            int64_t i = (int64_t)t * P + p;"),
+    ("dedup level 2 sums in reverse partition order", "            for (int p = 0; p < P; ++p) {\n                int32_t r = tp_row[(int64_t)t * P + p];",
+     "            for (int p = P - 1; p >= 0; --p) {\n                int32_t r = tp_row[(int64_t)t * P + p];"),
+    ("dedup level 1 multiply then add",
+     "                    acc = fmaf(w[(int64_t)t * K + k], oracle_bf16_to_f32(y[(int64_t)r * H + c]), acc);\n                }\n                partial",
+     "                    acc = w[(int64_t)t * K + k] * oracle_bf16_to_f32(y[(int64_t)r * H + c]) + acc;\n                }\n                partial"),
 ]
 
 BATTERY = [
@@ -66,16 +80,23 @@ BATTERY = [
     tdc.test_combine_exact_rational_small,
     tdc.test_identity_experts_return_dequantised_input,
     tdc.test_k1_unit_weight_returns_y_and_bf16_identity,
+    tdd.test_hand_worked_example,
+    tdd.test_brute_force_random_small_cases,
+    lambda: tdd.test_two_level_combine_exact("ll_128x7168"),
+    tdd.test_single_partition_tokens_equal_plain_combine,
+    tdd.test_reduce_order_hand_worked,
 ]
 
 
-def run_battery():
+def run_battery(stop_at_first=True):
     failed = 0
     for fn in BATTERY:
         try:
             fn()
         except Exception:
             failed += 1
+            if stop_at_first:
+                break
     return failed
 
 
@@ -95,7 +116,7 @@ def source():
 def test_unmodified_oracle_passes_battery(source, tmp_path):
     oracle.use_library(build_variant(source, str(tmp_path / "orig.so")))
     try:
-        assert run_battery() == 0
+        assert run_battery(stop_at_first=False) == 0
     finally:
         oracle.use_library(None)
 
