@@ -46,6 +46,10 @@ _SIGS = {
     "ep_graph_launch": ([_P, _P], _I),
     "ep_graph_destroy": ([_P], _I),
     "ep_e4m3fn_encode": ([_P, _I64, _P, _P], _I),
+    "ep_dedup_layout_workspace_bytes": ([_I, _I, _I, _I], _SZ),
+    "ep_dedup_layout": ([_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "ep_combine_partial": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
+    "ep_combine_reduce": ([_P, _P, _I, _I, _I, _P, _P], _I),
     "ep_strerror": ([_I], ctypes.c_char_p),
     "ep_last_hip_error": ([], _I),
 }
@@ -157,6 +161,50 @@ def ep_e4m3fn_encode(values_f32, out_u8, stream=None):
                                                      _ptr(out_u8), _stream(stream)))
 
 
+def ep_dedup_layout_workspace_bytes(T: int, K: int, E: int, P: int) -> int:
+    return int(_lib.ep_dedup_layout_workspace_bytes(T, K, E, P))
+
+
+def ep_dedup_layout(topk_idx, E, P, tp_row, part_tokens, part_token_offset, tp_src, kmask,
+                    status, ws=None, stream=None):
+    """topk_idx int32 [T, K] -> per-destination (dedup) layout (see include/ep.h)."""
+    _dt(topk_idx, torch.int32)
+    for t in (tp_row, part_tokens, part_token_offset, tp_src):
+        _dt(t, torch.int32)
+    _dt(kmask, torch.int32, torch.uint32)
+    _dt(status, torch.int32, torch.uint32)
+    T, K = topk_idx.shape
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("ep_dedup_layout", _lib.ep_dedup_layout(
+        _ptr(topk_idx), T, K, E, P, _ptr(tp_row), _ptr(part_tokens), _ptr(part_token_offset),
+        _ptr(tp_src), _ptr(kmask), _ptr(status), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def ep_combine_partial(expert_out, row_of_pair, topk_w, tp_row, kmask, P, partial, stream=None):
+    """Level 1: expert_out bf16 [T*K, H] -> partial bf16 [T*P, H] (rows of present couples)."""
+    _dt(expert_out, torch.bfloat16, torch.int16, torch.uint16)
+    _dt(partial, torch.bfloat16, torch.int16, torch.uint16)
+    _dt(topk_w, torch.float32)
+    _dt(row_of_pair, torch.int32)
+    _dt(tp_row, torch.int32)
+    _dt(kmask, torch.int32, torch.uint32)
+    T, K = topk_w.shape
+    H = partial.shape[1]
+    _check("ep_combine_partial", _lib.ep_combine_partial(
+        _ptr(expert_out), _ptr(row_of_pair), _ptr(topk_w), _ptr(tp_row), _ptr(kmask), T, H, K, P,
+        _ptr(partial), _stream(stream)))
+
+
+def ep_combine_reduce(partial, tp_row, T, P, out, stream=None):
+    """Level 2: partial bf16 [T*P, H] -> out bf16 [T, H] (partition-order fp32 sum)."""
+    _dt(partial, torch.bfloat16, torch.int16, torch.uint16)
+    _dt(out, torch.bfloat16, torch.int16, torch.uint16)
+    _dt(tp_row, torch.int32)
+    H = out.shape[1]
+    _check("ep_combine_reduce", _lib.ep_combine_reduce(_ptr(partial), _ptr(tp_row), T, H, P,
+                                                       _ptr(out), _stream(stream)))
+
+
 class EpGraph:
     """A recorded sequence of ep_* calls (HIP graph), replayed with ep_graph_launch."""
 
@@ -228,6 +276,52 @@ class EpBuffers:
 
     def combine(self, expert_out, topk_w, stream=None):
         ep_combine(expert_out, self.row_of_pair, topk_w, self.out, stream)
+        return self.out
+
+
+class EpDedupBuffers:
+    """Persistent device buffers of the per-destination (dedup) path for one
+    shape: the dedup layout, the dedup receive rows (one per present (token,
+    partition) couple), the partial rows and the output."""
+
+    def __init__(self, T, H, K, E, P, payload="fp8", device="cuda"):
+        self.T, self.H, self.K, self.E, self.P = T, H, K, E, P
+        self.payload = payload
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.tp_row = torch.empty(T * P, **i32)
+        self.part_tokens = torch.empty(P, **i32)
+        self.part_token_offset = torch.empty(P + 1, **i32)
+        self.tp_src = torch.empty(T * P, **i32)
+        self.kmask = torch.empty(T * P, **i32)
+        self.status = torch.empty(1, **i32)
+        wsb = ep_dedup_layout_workspace_bytes(T, K, E, P)
+        self.ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        if payload == "fp8":
+            self.recv_x = torch.empty((T * P, H), dtype=torch.uint8, device=dev)
+            self.recv_scales = torch.empty((T * P, H // 128), dtype=torch.float32, device=dev)
+        else:
+            self.recv_x = torch.empty((T * P, H), dtype=torch.bfloat16, device=dev)
+            self.recv_scales = None
+        self.partial = torch.empty((T * P, H), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def layout(self, topk_idx, stream=None):
+        ep_dedup_layout(topk_idx, self.E, self.P, self.tp_row, self.part_tokens,
+                        self.part_token_offset, self.tp_src, self.kmask, self.status, self.ws,
+                        stream)
+
+    def dispatch(self, x, stream=None):
+        """One copy of each token per partition it reaches (ep_dispatch, K = P, tp_row)."""
+        ep_dispatch(x, self.P, self.tp_row, self.payload, self.recv_x, self.recv_scales, stream)
+
+    def combine_partial(self, expert_out, row_of_pair, topk_w, stream=None):
+        ep_combine_partial(expert_out, row_of_pair, topk_w, self.tp_row, self.kmask, self.P,
+                           self.partial, stream)
+        return self.partial
+
+    def combine_reduce(self, stream=None):
+        ep_combine_reduce(self.partial, self.tp_row, self.T, self.P, self.out, stream)
         return self.out
 
 

@@ -28,6 +28,11 @@ bool routing_ok(int T, int K)
     return T >= 0 && K >= 1 && K <= EP_MAX_TOPK && (int64_t)T * K < ((int64_t)1 << 31);
 }
 
+bool dedup_ok(int T, int P)
+{
+    return T >= 0 && P >= 1 && P <= EP_MAX_DEDUP_PARTITIONS && (int64_t)T * P < ((int64_t)1 << 31);
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,6 +119,53 @@ int ep_combine(const uint16_t* expert_out, const int32_t* row_of_pair, const flo
         return EP_EINVAL;
     return from_hip(ep::launch_combine(expert_out, row_of_pair, topk_w, T, H, K, out,
                                        (hipStream_t)stream));
+}
+
+size_t ep_dedup_layout_workspace_bytes(int T, int K, int E, int P)
+{
+    if (!routing_ok(T, K) || !dedup_ok(T, P) || E < 1 || E > EP_MAX_EXPERTS || E % P != 0) return 0;
+    return ep::dedup_layout_workspace_bytes(T, P);
+}
+
+int ep_dedup_layout(const int32_t* topk_idx, int T, int K, int E, int P, int32_t* tp_row,
+                    int32_t* part_tokens, int32_t* part_token_offset, int32_t* tp_src,
+                    uint32_t* kmask, uint32_t* status, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!routing_ok(T, K) || !dedup_ok(T, P) || E < 1 || E > EP_MAX_EXPERTS || E % P != 0)
+        return EP_EINVAL;
+    if (!ptr_ok(part_tokens, 4) || !ptr_ok(part_token_offset, 4) || !ptr_ok(status, 4))
+        return EP_EINVAL;
+    if (T > 0 && (!ptr_ok(topk_idx, 4) || !ptr_ok(tp_row, 4) || !ptr_ok(tp_src, 4) ||
+                  !ptr_ok(kmask, 4)))
+        return EP_EINVAL;
+    const size_t need = ep::dedup_layout_workspace_bytes(T, P);
+    if (need > 0 && (ws_bytes < need || !ptr_ok(ws, 16))) return EP_EINVAL;
+    return from_hip(ep::launch_dedup_layout(topk_idx, T, K, E, P, tp_row, part_tokens,
+                                            part_token_offset, tp_src, kmask, status, ws,
+                                            (hipStream_t)stream));
+}
+
+int ep_combine_partial(const uint16_t* expert_out, const int32_t* row_of_pair,
+                       const float* topk_w, const int32_t* tp_row, const uint32_t* kmask, int T,
+                       int H, int K, int P, uint16_t* partial, void* stream)
+{
+    if (!routing_ok(T, K) || !dedup_ok(T, P) || H <= 0 || H % ep::kColsPerLane != 0)
+        return EP_EINVAL;
+    if (T == 0) return EP_OK;
+    if (!ptr_ok(expert_out, 16) || !ptr_ok(row_of_pair, 4) || !ptr_ok(topk_w, 4) ||
+        !ptr_ok(tp_row, 4) || !ptr_ok(kmask, 4) || !ptr_ok(partial, 16))
+        return EP_EINVAL;
+    return from_hip(ep::launch_combine_partial(expert_out, row_of_pair, topk_w, tp_row, kmask, T, H,
+                                               K, P, partial, (hipStream_t)stream));
+}
+
+int ep_combine_reduce(const uint16_t* partial, const int32_t* tp_row, int T, int H, int P,
+                      uint16_t* out, void* stream)
+{
+    if (!dedup_ok(T, P) || H <= 0 || H % ep::kColsPerLane != 0) return EP_EINVAL;
+    if (T == 0) return EP_OK;
+    if (!ptr_ok(partial, 16) || !ptr_ok(tp_row, 4) || !ptr_ok(out, 16)) return EP_EINVAL;
+    return from_hip(ep::launch_combine_reduce(partial, tp_row, T, H, P, out, (hipStream_t)stream));
 }
 
 int ep_e4m3fn_encode(const float* in, int64_t n, uint8_t* out, void* stream)

@@ -16,6 +16,16 @@
 // its K 16-byte loads (one per expert row, each wave-wide load a contiguous
 // 1 KB) before the first FMA so the K rows are in flight together, then
 // accumulates in k order and stores 16 bytes of bf16.
+//
+// The same kernel runs the two levels of the per-destination (dedup) combine
+// (UCCL PR #749: tokens batched per destination; MoRI PR #614,
+// DispatchIntraNode paragraph: one copy of a token per destination):
+//   partial: one item per (token, partition) couple that has a row; it sums,
+//            in k order, only the top-k entries whose bit is set in that
+//            couple's mask and writes the bf16 partial to the couple's row;
+//   reduce:  one item per token; it adds the token's partial rows in
+//            partition order (weight 1: fmaf(1, v, acc) is the correctly
+//            rounded acc + v) and writes the bf16 result.
 #include "ep_device.h"
 #include "ep_launch.h"
 #include "ep_numerics.h"
@@ -23,22 +33,39 @@
 namespace ep {
 namespace {
 
-template <int kMaxK, bool kStream>
+enum CombineMode { kPlain = 0, kPartial = 1, kReduce = 2 };
+
+// Plain and reduce: an item is (token t, column step); its K source rows are
+// row_of_pair[t*K ..] (tp_row with K = P for reduce) and it writes out row t.
+// Partial: an item is (couple j = t*P + p, column step); it writes row
+// tp_row[j] of `out` (skipped when -1) from the entries in kmask[j].
+template <int kMaxK, bool kStream, int kMode>
 __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
     const uint16_t* __restrict__ y, const int32_t* __restrict__ row_of_pair,
     const float* __restrict__ topk_w, int H, int K, uint16_t* __restrict__ out,
-    int steps_per_token, int n_items, int n_rows)
+    int steps_per_token, int n_items, int n_rows,
+    const int32_t* __restrict__ tp_row, const uint32_t* __restrict__ kmask, int P, int out_rows)
 {
     const int lane = threadIdx.x % kWave;
     const int stride = gridDim.x * kMoveWaves;
     for (int item = blockIdx.x * kMoveWaves + wave_uniform(threadIdx.x / kWave); item < n_items;
          item += stride) {                   // n_items + stride < 2^31 (checked by the launcher)
-        const int t = item / steps_per_token;
-        const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
+        const int u = item / steps_per_token;
+        const int col0 = (item - u * steps_per_token) * kStepCols + lane * kColsPerLane;
+        int t = u, orow = u;
+        uint32_t use = ~0u;
+        if constexpr (kMode == kPartial) {
+            t = u / P;
+            orow = tp_row[u];
+            if (orow < 0 || orow >= out_rows) continue;   // no copy of t in this partition
+            use = kmask[u];
+        }
         const bool active = col0 < H;
-        int myrow = (lane < K) ? row_of_pair[(int64_t)t * K + lane] : -1;
+        int myrow = (lane < K && ((use >> lane) & 1u)) ? row_of_pair[(int64_t)t * K + lane] : -1;
         if (myrow >= n_rows) myrow = -1;     // not a receive row: treated as masked
-        const float myw = (lane < K) ? topk_w[(int64_t)t * K + lane] : 0.0f;
+        float myw = 0.0f;
+        if constexpr (kMode == kReduce) myw = 1.0f;
+        else myw = (lane < K) ? topk_w[(int64_t)t * K + lane] : 0.0f;
 
         uint4 v[kMaxK];
 #pragma unroll
@@ -75,7 +102,7 @@ __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
             o.y = pack2_bf16(acc[2], acc[3]);
             o.z = pack2_bf16(acc[4], acc[5]);
             o.w = pack2_bf16(acc[6], acc[7]);
-            store16<kStream>(out + (int64_t)t * H + col0, o);
+            store16<kStream>(out + (int64_t)orow * H + col0, o);
         }
     }
 }
@@ -88,13 +115,37 @@ constexpr int64_t kMaxGridBlocks = 1 << 20;
 // because its once-read rows no longer evict the dispatch's fresh lines.
 // EP_FORCE_POLICY (build option for A/B runs): 1 = cached accesses everywhere,
 // 2 = streaming combine only, 3 = streaming dispatch and combine.
-bool combine_streams(int T, int H, int K)
+bool combine_streams(int64_t gathered_rows, int H)
 {
 #if defined(EP_FORCE_POLICY)
     if (EP_FORCE_POLICY == 1) return false;
     if (EP_FORCE_POLICY >= 2) return true;
 #endif
-    return (int64_t)T * K * H * 2 >= kStreamMinBytes;
+    return gathered_rows * H * 2 >= kStreamMinBytes;
+}
+
+}  // namespace
+
+namespace {
+
+template <int kMode>
+hipError_t launch_combine_mode(const uint16_t* y, const int32_t* row_of_pair,
+                               const float* topk_w, int n_units, int H, int K, int n_rows,
+                               const int32_t* tp_row, const uint32_t* kmask, int P, int out_rows,
+                               int64_t gathered_rows, uint16_t* out, hipStream_t stream)
+{
+    const int steps = (H + kStepCols - 1) / kStepCols;
+    const int64_t items = (int64_t)n_units * steps;
+    if (items == 0) return hipSuccess;
+    if (items + kMaxGridBlocks * kMoveWaves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
+    if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
+    const bool stream_policy = combine_streams(gathered_rows, H);
+    auto k = K <= 8 ? (stream_policy ? combine_kernel<8, true, kMode> : combine_kernel<8, false, kMode>)
+                    : (stream_policy ? combine_kernel<16, true, kMode> : combine_kernel<16, false, kMode>);
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kMoveThreads), 0, stream, y, row_of_pair,
+                       topk_w, H, K, out, steps, (int)items, n_rows, tp_row, kmask, P, out_rows);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -102,18 +153,24 @@ bool combine_streams(int T, int H, int K)
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of_pair, const float* topk_w,
                           int T, int H, int K, uint16_t* out, hipStream_t stream)
 {
-    const int steps = (H + kStepCols - 1) / kStepCols;
-    const int64_t items = (int64_t)T * steps;
-    if (items == 0) return hipSuccess;
-    if (items + kMaxGridBlocks * kMoveWaves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
-    if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
-    const bool stream_policy = combine_streams(T, H, K);
-    auto k = K <= 8 ? (stream_policy ? combine_kernel<8, true> : combine_kernel<8, false>)
-                    : (stream_policy ? combine_kernel<16, true> : combine_kernel<16, false>);
-    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kMoveThreads), 0, stream, y, row_of_pair,
-                       topk_w, H, K, out, steps, (int)items, T * K);
-    return hipGetLastError();
+    return launch_combine_mode<kPlain>(y, row_of_pair, topk_w, T, H, K, T * K, nullptr, nullptr,
+                                       1, T, (int64_t)T * K, out, stream);
+}
+
+hipError_t launch_combine_partial(const uint16_t* y, const int32_t* row_of_pair,
+                                  const float* topk_w, const int32_t* tp_row,
+                                  const uint32_t* kmask, int T, int H, int K, int P,
+                                  uint16_t* partial, hipStream_t stream)
+{
+    return launch_combine_mode<kPartial>(y, row_of_pair, topk_w, T * P, H, K, T * K, tp_row, kmask,
+                                         P, T * P, (int64_t)T * K, partial, stream);
+}
+
+hipError_t launch_combine_reduce(const uint16_t* partial, const int32_t* tp_row, int T, int H,
+                                 int P, uint16_t* out, hipStream_t stream)
+{
+    return launch_combine_mode<kReduce>(partial, tp_row, nullptr, T, H, P, T * P, nullptr, nullptr,
+                                        1, T, (int64_t)T * P, out, stream);
 }
 
 }  // namespace ep

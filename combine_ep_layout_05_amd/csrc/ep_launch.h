@@ -34,6 +34,21 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* row_of_pair,
                           const float* topk_w, int T, int H, int K,
                           uint16_t* out, hipStream_t stream);
 
+size_t dedup_layout_workspace_bytes(int T, int P);
+
+hipError_t launch_dedup_layout(const int32_t* topk_idx, int T, int K, int E, int P,
+                               int32_t* tp_row, int32_t* part_tokens, int32_t* part_token_offset,
+                               int32_t* tp_src, uint32_t* kmask, uint32_t* status, void* ws,
+                               hipStream_t stream);
+
+hipError_t launch_combine_partial(const uint16_t* y, const int32_t* row_of_pair,
+                                  const float* topk_w, const int32_t* tp_row,
+                                  const uint32_t* kmask, int T, int H, int K, int P,
+                                  uint16_t* partial, hipStream_t stream);
+
+hipError_t launch_combine_reduce(const uint16_t* partial, const int32_t* tp_row, int T, int H,
+                                 int P, uint16_t* out, hipStream_t stream);
+
 hipError_t launch_e4m3fn_encode(const float* in, int64_t n, uint8_t* out,
                                 hipStream_t stream);
 

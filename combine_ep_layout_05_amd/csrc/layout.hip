@@ -31,6 +31,8 @@
 // building the histogram are reused for the ranks.  Scans use DPP wave scans.
 // No atomic's return value ever decides a slot, so the result is the same on
 // every run.  LDS atomics are used only for order-free histogram sums.
+#include <type_traits>
+
 #include "ep_device.h"
 #include "ep_launch.h"
 
@@ -47,6 +49,50 @@ struct LayoutSmem {
     int32_t wsum[kLayoutWaves];
     uint32_t bad;
     int32_t total;
+};
+
+// Where a layout entry's id comes from.
+//   Plain: entry p is the (t, k) pair p = t*K + k; its id is topk_idx[p] and an
+//   id >= E is reported as bad.
+//   Dedup: entry j is the (token, partition) couple j = t*P + p of the
+//   per-destination layout (UCCL PR #749: tokens batched per destination;
+//   MoRI PR #614, DispatchIntraNode paragraph: one copy of a token per
+//   destination).  Its id is p when token t has a valid expert in partition
+//   p, else -1, so the layout over ids 0..P-1 gives every present couple a
+//   row in token order within its partition.  The top-k entries served by
+//   that copy form a bit mask (bit k), written out when `kmask` is set; bad
+//   ids of the token are reported by every couple of that token.
+struct PlainEntries {
+    const int32_t* idx;
+    __device__ __forceinline__ int load(int64_t p, int E, bool& bad) const
+    {
+        const int e = idx[p];
+        bad |= e >= E;
+        return e;
+    }
+};
+
+struct DedupEntries {
+    const int32_t* idx;
+    uint32_t* kmask;   // null: masks not wanted by this pass
+    int K, E, L, P;    // the real routing: top-k, experts, experts per partition, partitions
+    __device__ __forceinline__ int load(int64_t j, int, bool& bad) const
+    {
+        const int t = (int)j / P;              // T*P < 2^31 (checked by the caller)
+        const int p = (int)j - t * P;
+        const int lo = p * L, hi = lo + L;
+        int e[kMaxTopK];
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) e[k] = (k < K) ? idx[(int64_t)t * K + k] : -1;
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+            bad |= e[k] >= E;
+            if (e[k] >= lo && e[k] < hi) m |= 1u << k;
+        }
+        if (kmask) kmask[j] = m;
+        return m ? p : -1;
+    }
 };
 
 __device__ __forceinline__ int id_bits(int E)
@@ -156,8 +202,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, LayoutSmem& s, int* t
 }
 
 // From per-expert counts (one per thread, tid < E): write expert_count,
-// expert_offset, part_count, part_offset and status; leave the exclusive
-// offsets in s.cursor and N in s.total.
+// expert_offset, part_count, part_offset (skipped when part_count is null)
+// and status; leave the exclusive offsets in s.cursor and N in s.total.
 __device__ __forceinline__ void finish_counts(int count, int E, int P, uint32_t bad, LayoutSmem& s, bool write_out,
                               int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
                               int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
@@ -180,19 +226,20 @@ __device__ __forceinline__ void finish_counts(int count, int E, int P, uint32_t 
     }
     __syncthreads();
     const int L = E / P;
-    if (write_out && tid < P) {
+    if (write_out && part_count && tid < P) {
         const int lo = s.cursor[tid * L];
         const int hi = (tid + 1 < P) ? s.cursor[(tid + 1) * L] : N;
         part_offset[tid] = lo;
         part_count[tid] = hi - lo;
     }
-    if (write_out && tid == 0) part_offset[P] = N;
+    if (write_out && part_count && tid == 0) part_offset[P] = N;
 }
 
 // ---------------------------------------------------------------------------
 // Small batches (T*K <= kSmallMaxPairs): one workgroup does everything.
+template <class Entries>
 __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
-    const int32_t* __restrict__ idx, int64_t n, int E, int P,
+    const Entries src, int64_t n, int E, int P,
     int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
     int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair,
@@ -203,24 +250,21 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
     const int nbits = id_bits(E);
     const int rounds = (int)((n + kLayoutThreads - 1) / kLayoutThreads);
     int ids[kSmallRounds];
+    bool bad = false;
 #pragma unroll
     for (int r = 0; r < kSmallRounds; ++r) {
         const int64_t p = (int64_t)r * kLayoutThreads + tid;
-        ids[r] = (p < n) ? idx[p] : -1;
+        ids[r] = (p < n) ? src.load(p, E, bad) : -1;
     }
     zero_smem(s, E);
     __syncthreads();
 
     // pass 1: histogram
     uint64_t peers[kSmallRounds];
-    bool bad = false;
 #pragma unroll
     for (int r = 0; r < kSmallRounds; ++r) {
         peers[r] = 0ull;
-        if (r < rounds) {
-            bad |= ids[r] >= E;
-            peers[r] = hist_round(ids[r], E, nbits, s.hist);
-        }
+        if (r < rounds) peers[r] = hist_round(ids[r], E, nbits, s.hist);
     }
     if (bad) s.bad = 1u;
     __syncthreads();
@@ -246,8 +290,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
 // writes the chunk's histogram into ws_hist[chunk][E] and a bad-id flag into
 // ws_bad[chunk] (ballot-aggregated LDS atomics: a hot expert costs one atomic
 // per wave, not one per entry).
+template <class Entries>
 __global__ __launch_bounds__(kLayoutThreads) void layout_hist_kernel(
-    const int32_t* __restrict__ idx, int64_t n, int E, int32_t* __restrict__ ws_hist,
+    const Entries src, int64_t n, int E, int32_t* __restrict__ ws_hist,
     uint32_t* __restrict__ ws_bad)
 {
     __shared__ int32_t hist[kMaxExperts];
@@ -258,20 +303,17 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_hist_kernel(
     const int64_t c0 = (int64_t)chunk * kChunkPairs;
     const int64_t c1 = (c0 + kChunkPairs < n) ? c0 + kChunkPairs : n;
     int ids[kChunkRounds];
+    bool b = false;
 #pragma unroll
     for (int r = 0; r < kChunkRounds; ++r) {
         const int64_t p = c0 + (int64_t)r * kLayoutThreads + tid;
-        ids[r] = (p < c1) ? idx[p] : -1;
+        ids[r] = (p < c1) ? src.load(p, E, b) : -1;
     }
     if (tid < E) hist[tid] = 0;
     if (tid == 0) bad = 0u;
     __syncthreads();
-    bool b = false;
 #pragma unroll
-    for (int r = 0; r < kChunkRounds; ++r) {
-        b |= ids[r] >= E;
-        (void)hist_round(ids[r], E, nbits, hist);
-    }
+    for (int r = 0; r < kChunkRounds; ++r) (void)hist_round(ids[r], E, nbits, hist);
     if (b) bad = 1u;
     __syncthreads();
     if (tid < E) ws_hist[(int64_t)chunk * E + tid] = hist[tid];
@@ -330,8 +372,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(
 // the count outputs) and the rows of each expert taken by earlier chunks --
 // reading C*E integers from L2 is cheaper than another launch.  With
 // bases_ready == 1 the scan kernel has already put the bases in ws_hist.
+template <class Entries>
 __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
-    const int32_t* __restrict__ idx, int64_t n, int E, int P, int nchunks, int bases_ready,
+    const Entries src, int64_t n, int E, int P, int nchunks, int bases_ready,
     const int32_t* __restrict__ ws_hist, const uint32_t* __restrict__ ws_bad,
     int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
@@ -345,11 +388,13 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     const int64_t c0 = (int64_t)chunk * kChunkPairs;
     const int64_t c1 = (c0 + kChunkPairs < n) ? c0 + kChunkPairs : n;
     int ids[kChunkRounds];
+    bool unused_bad = false;   // bad ids were collected by the histogram pass
 #pragma unroll
     for (int r = 0; r < kChunkRounds; ++r) {
         const int64_t p = c0 + (int64_t)r * kLayoutThreads + tid;
-        ids[r] = (p < c1) ? idx[p] : -1;
+        ids[r] = (p < c1) ? src.load(p, E, unused_bad) : -1;
     }
+    (void)unused_bad;
     zero_smem(s, E);
     __syncthreads();
 
@@ -414,16 +459,20 @@ size_t layout_workspace_bytes(int T, int K, int E)
     return hist_padded + (size_t)c * sizeof(uint32_t);
 }
 
-hipError_t launch_layout(const int32_t* idx, int T, int K, int E, int P,
-                         int32_t* expert_count, int32_t* expert_offset,
-                         int32_t* part_count, int32_t* part_offset,
-                         int32_t* row_of_pair, int32_t* src_pair, uint32_t* status,
-                         void* ws, hipStream_t stream)
+namespace {
+
+// n entries with ids in 0..E-1 (E <= kMaxExperts) and P partitions; the
+// workspace sizing of layout_workspace_bytes for the same n and E.
+template <class Entries>
+hipError_t launch_layout_entries(const Entries& src, int64_t n, int E, int P,
+                                 int32_t* expert_count, int32_t* expert_offset,
+                                 int32_t* part_count, int32_t* part_offset,
+                                 int32_t* row_of_pair, int32_t* src_pair, uint32_t* status,
+                                 void* ws, hipStream_t stream)
 {
-    const int64_t n = (int64_t)T * K;
     if (n <= kSmallMaxPairs) {
-        hipLaunchKernelGGL(layout_single_kernel, dim3(1), dim3(kLayoutThreads), 0, stream,
-                           idx, n, E, P, expert_count, expert_offset, part_count, part_offset,
+        hipLaunchKernelGGL(layout_single_kernel<Entries>, dim3(1), dim3(kLayoutThreads), 0, stream,
+                           src, n, E, P, expert_count, expert_offset, part_count, part_offset,
                            row_of_pair, src_pair, status);
         return hipGetLastError();
     }
@@ -431,17 +480,45 @@ hipError_t launch_layout(const int32_t* idx, int T, int K, int E, int P,
     const size_t hist = (size_t)c * E * sizeof(int32_t);
     int32_t* ws_hist = (int32_t*)ws;
     uint32_t* ws_bad = (uint32_t*)((char*)ws + ((hist + 255) & ~(size_t)255));
-    hipLaunchKernelGGL(layout_hist_kernel, dim3((unsigned)c), dim3(kLayoutThreads), 0, stream,
-                       idx, n, E, ws_hist, ws_bad);
+    Entries hist_src = src;
+    if constexpr (std::is_same_v<Entries, DedupEntries>) hist_src.kmask = nullptr;
+    hipLaunchKernelGGL(layout_hist_kernel<Entries>, dim3((unsigned)c), dim3(kLayoutThreads), 0,
+                       stream, hist_src, n, E, ws_hist, ws_bad);
     const int bases_ready = c > kMaxChunksTwoPass ? 1 : 0;
     if (bases_ready)
         hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kLayoutThreads), 0, stream,
                            (int)c, E, P, ws_hist, ws_bad, expert_count, expert_offset, part_count,
                            part_offset, status);
-    hipLaunchKernelGGL(layout_rank_kernel, dim3((unsigned)c), dim3(kLayoutThreads), 0, stream,
-                       idx, n, E, P, (int)c, bases_ready, ws_hist, ws_bad, expert_count,
+    hipLaunchKernelGGL(layout_rank_kernel<Entries>, dim3((unsigned)c), dim3(kLayoutThreads), 0,
+                       stream, src, n, E, P, (int)c, bases_ready, ws_hist, ws_bad, expert_count,
                        expert_offset, part_count, part_offset, row_of_pair, src_pair, status);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_layout(const int32_t* idx, int T, int K, int E, int P,
+                         int32_t* expert_count, int32_t* expert_offset,
+                         int32_t* part_count, int32_t* part_offset,
+                         int32_t* row_of_pair, int32_t* src_pair, uint32_t* status,
+                         void* ws, hipStream_t stream)
+{
+    return launch_layout_entries(PlainEntries{idx}, (int64_t)T * K, E, P, expert_count,
+                                 expert_offset, part_count, part_offset, row_of_pair, src_pair,
+                                 status, ws, stream);
+}
+
+size_t dedup_layout_workspace_bytes(int T, int P) { return layout_workspace_bytes(T, P, P); }
+
+hipError_t launch_dedup_layout(const int32_t* idx, int T, int K, int E, int P, int32_t* tp_row,
+                               int32_t* part_tokens, int32_t* part_token_offset, int32_t* tp_src,
+                               uint32_t* kmask, uint32_t* status, void* ws, hipStream_t stream)
+{
+    // ids 0..P-1 with one partition per id: the per-"expert" counts and scan
+    // are the per-partition token counts and offsets.
+    const DedupEntries src{idx, kmask, K, E, E / P, P};
+    return launch_layout_entries(src, (int64_t)T * P, P, P, part_tokens, part_token_offset,
+                                 nullptr, nullptr, tp_row, tp_src, status, ws, stream);
 }
 
 }  // namespace ep

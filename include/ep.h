@@ -171,6 +171,80 @@ int ep_combine(const uint16_t* expert_out, const int32_t* row_of_pair,
                uint16_t* out, void* stream);
 
 /*
+ * Per-destination (dedup) variant.  A token whose top-k experts share a
+ * destination is sent there once, with a bit mask of the top-k entries that
+ * copy serves, and the destination sums its share of the combine before
+ * sending one partial row back (UCCL PR #749 "[EP] Low-latency mode batch
+ * tokens per destination"; MoRI PR #614, DispatchIntraNode paragraph: the
+ * flat work split leaves the dedup unchanged).  A "couple" is (t, p), flat
+ * index t*P + p; it is present when token t has at least one valid expert
+ * in partition p.  M = number of present couples.  P <= 16.
+ *
+ * The dedup dispatch is ep_dispatch with K = P and row_of_pair = tp_row:
+ * each present couple's row gets one copy of the token (fp8 + scales, or
+ * bf16), M rows in all instead of N.
+ */
+#define EP_MAX_DEDUP_PARTITIONS 16
+
+/* Workspace bytes ep_dedup_layout needs (0: none).  Host-only; 0 as well for
+ * arguments ep_dedup_layout would reject. */
+size_t ep_dedup_layout_workspace_bytes(int T, int K, int E, int P);
+
+/*
+ * Dedup layout.
+ *   topk_idx          int32 [T, K], as for ep_layout (negative = masked, id >= E
+ *                     sets EP_STATUS_BAD_EXPERT_ID and is masked).
+ *   tp_row            int32 [T*P] out: dedup row of couple t*P+p, -1 when absent.
+ *                     Partition p owns rows part_token_offset[p] ..
+ *                     part_token_offset[p+1]-1, in ascending token order.
+ *   part_tokens       int32 [P]   out: present couples (distinct tokens) per partition.
+ *   part_token_offset int32 [P+1] out: exclusive scan; part_token_offset[P] = M.
+ *   tp_src            int32 [T*P] out: tp_src[row] = t*P+p for row < M, -1 for
+ *                     rows M .. T*P-1.
+ *   kmask             uint32 [T*P] out: bit k set when topk_idx[t, k] is a valid
+ *                     expert of partition p (0 for absent couples).
+ *   status            uint32 [1] out: cleared, then EP_STATUS_* bits.
+ *   ws, ws_bytes      workspace of ep_dedup_layout_workspace_bytes(T, K, E, P)
+ *                     bytes, 16-byte aligned; scratch, not shared by concurrent calls.
+ * Errors: EP_EINVAL for the routing errors of ep_layout, P outside 1..16,
+ * E % P != 0, T*P >= 2^31, NULL or misaligned (4 B; ws 16 B) pointers, or
+ * ws_bytes too small.
+ */
+int ep_dedup_layout(const int32_t* topk_idx, int T, int K, int E, int P,
+                    int32_t* tp_row, int32_t* part_tokens, int32_t* part_token_offset,
+                    int32_t* tp_src, uint32_t* kmask, uint32_t* status,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Combine level 1, at the destination: for every present couple (t, p),
+ * partial[tp_row[t*P+p], c] = bf16_rne(acc), acc = 0.0f, then for k = 0..K-1
+ * in order with bit k of kmask[t*P+p] set and r = row_of_pair[t*K+k] >= 0:
+ * acc = fmaf(topk_w[t*K+k], expert_out[r, c], acc).  Rows of absent couples
+ * are not written.
+ *   expert_out  bf16 [T*K, H] in the receive-row layout of ep_layout (the
+ *               per-expert rows the experts computed), 16-B aligned.
+ *   row_of_pair int32 [T*K] from ep_layout; topk_w fp32 [T, K];
+ *   tp_row, kmask from ep_dedup_layout;  partial bf16 [T*P, H], 16-B aligned.
+ * Errors: EP_EINVAL for T < 0, K outside 1..16, P outside 1..16, T*K or
+ * T*P >= 2^31, H <= 0 or H % 8 != 0, NULL or misaligned pointers when T > 0.
+ */
+int ep_combine_partial(const uint16_t* expert_out, const int32_t* row_of_pair,
+                       const float* topk_w, const int32_t* tp_row, const uint32_t* kmask,
+                       int T, int H, int K, int P, uint16_t* partial, void* stream);
+
+/*
+ * Combine level 2, at the token's home: out[t, c] = bf16_rne(acc), acc = 0.0f,
+ * then for p = 0..P-1 in order with r = tp_row[t*P+p] >= 0:
+ * acc = acc + partial[r, c] (fp32).  A token with no present couple gives +0.
+ *   partial bf16 [T*P, H] from ep_combine_partial; tp_row int32 [T*P];
+ *   out bf16 [T, H]; 16-B aligned rows.
+ * Errors: EP_EINVAL for T < 0, P outside 1..16, T*P >= 2^31, H <= 0 or
+ * H % 8 != 0, NULL or misaligned pointers when T > 0.
+ */
+int ep_combine_reduce(const uint16_t* partial, const int32_t* tp_row, int T, int H, int P,
+                      uint16_t* out, void* stream);
+
+/*
  * HIP graph capture for the small-token regime, where host enqueue paces the
  * GPU (MoRI PR #614, view-cache paragraph: at 4 tokens most of a round's
  * wall time was host work, and stable buffers are what make the op

@@ -98,3 +98,83 @@ def compare(wl, got, ref, check_poison=True):
     dist = bf16_ulp_distance(got["out"], ref["out"])
     assert dist.max(initial=0) <= 1, "%s: combine off by %d ulp" % (wl.name, dist.max())
     return int(np.count_nonzero(dist))
+
+
+DEDUP_KEYS = ("tp_row", "part_tokens", "part_token_offset", "tp_src", "kmask")
+
+
+def run_gpu_dedup(wl, d, stream=None):
+    """Per-destination path on the GPU: ep_layout (expert rows for the expert
+    outputs), ep_dedup_layout, ep_dispatch with K = P over tp_row,
+    ep_combine_partial and ep_combine_reduce.  Buffers start poisoned."""
+    ep = gpu_lib()
+    buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    db = ep.EpDedupBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    db.recv_x.view(torch.uint8).fill_(POISON_BYTE)
+    if db.recv_scales is not None:
+        db.recv_scales.view(torch.int32).fill_(POISON_F32_BITS)
+    for t in (db.tp_row, db.tp_src, db.kmask):
+        t.fill_(-7)
+    db.partial.view(torch.int16).fill_(0x5A5A)
+    db.out.view(torch.int16).fill_(0x5A5A)
+    idx = to_dev(d["idx"])
+    x = to_dev(d["x"].view(np.int16), torch.bfloat16)
+    y = to_dev(d["y"].view(np.int16), torch.bfloat16)
+    w = to_dev(d["w"])
+    buf.layout(idx, stream)
+    db.layout(idx, stream)
+    db.dispatch(x, stream)
+    db.combine_partial(y, buf.row_of_pair, w, stream)
+    db.combine_reduce(stream)
+    torch.cuda.synchronize()
+    res = {k: getattr(db, k).cpu().numpy() for k in DEDUP_KEYS}
+    res["kmask"] = res["kmask"].view(np.uint32)
+    res["status"] = db.status.cpu().numpy().view(np.uint32)
+    res["row_of_pair"] = buf.row_of_pair.cpu().numpy()
+    res["recv_x"] = db.recv_x.view(torch.uint8).cpu().numpy() if wl.payload == "fp8" else \
+        db.recv_x.view(torch.int16).cpu().numpy().view(np.uint16)
+    if db.recv_scales is not None:
+        res["recv_scales"] = db.recv_scales.cpu().numpy()
+    res["partial"] = db.partial.view(torch.int16).cpu().numpy().view(np.uint16)
+    res["out"] = db.out.view(torch.int16).cpu().numpy().view(np.uint16)
+    return res
+
+
+def run_oracle_dedup(wl, d):
+    lo = oracle.layout(d["idx"], wl.E, wl.P)
+    dl = oracle.dedup_layout(d["idx"], wl.E, wl.P)
+    res = dict(dl)
+    res["row_of_pair"] = lo["row_of_pair"]
+    if wl.payload == "fp8":
+        res["recv_x"], res["recv_scales"] = oracle.dispatch_fp8(d["x"], dl["tp_row"], wl.P)
+    else:
+        res["recv_x"] = oracle.dispatch_bf16(d["x"], dl["tp_row"], wl.P)
+    res["partial"] = oracle.combine_partial(d["y"], lo["row_of_pair"], d["w"], dl["tp_row"],
+                                            dl["kmask"], wl.T, wl.H, wl.K, wl.P)
+    res["out"] = oracle.combine_reduce(res["partial"], dl["tp_row"], wl.T, wl.H, wl.P)
+    return res
+
+
+def compare_dedup(wl, got, ref):
+    """Bit-exact layout, dispatch rows and scales; partial and output within
+    1 bf16 ulp; rows past M untouched.  Returns the number of differing
+    partial + output values (expected 0: same fmaf / add order)."""
+    from tests.helpers import bf16_ulp_distance
+    for k in DEDUP_KEYS + ("row_of_pair",):
+        np.testing.assert_array_equal(got[k], ref[k], err_msg="%s: %s" % (wl.name, k))
+    assert int(got["status"][0]) == int(ref["status"][0]), (wl.name, "status")
+    M = int(ref["part_token_offset"][wl.P])
+    gx, rx = got["recv_x"], ref["recv_x"]
+    bad = np.nonzero((gx[:M] != rx[:M]).any(axis=1))[0]
+    assert bad.size == 0, "%s: dedup recv_x rows differ, first row %d" % (wl.name, bad[0])
+    assert np.all(gx[M:].view(np.uint8) == POISON_BYTE), "%s: rows >= M were written" % wl.name
+    if wl.payload == "fp8":
+        np.testing.assert_array_equal(got["recv_scales"][:M].view(np.uint32),
+                                      ref["recv_scales"][:M].view(np.uint32))
+        assert np.all(got["recv_scales"][M:].view(np.uint32) == POISON_F32_BITS)
+    dp = bf16_ulp_distance(got["partial"][:M], ref["partial"][:M])
+    assert dp.max(initial=0) <= 1, "%s: partial off by %d ulp" % (wl.name, dp.max())
+    assert np.all(got["partial"][M:] == 0x5A5A), "%s: partial rows >= M were written" % wl.name
+    do = bf16_ulp_distance(got["out"], ref["out"])
+    assert do.max(initial=0) <= 1, "%s: output off by %d ulp" % (wl.name, do.max())
+    return int(np.count_nonzero(dp)) + int(np.count_nonzero(do))

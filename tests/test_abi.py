@@ -28,7 +28,9 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("ep_layout", "ep_dispatch", "ep_combine", "ep_layout_workspace_bytes",
               "ep_strerror", "ep_last_hip_error", "ep_graph_begin", "ep_graph_end",
-              "ep_graph_launch", "ep_graph_destroy", "ep_e4m3fn_encode"):
+              "ep_graph_launch", "ep_graph_destroy", "ep_e4m3fn_encode", "ep_layout_dispatch",
+              "ep_dedup_layout", "ep_dedup_layout_workspace_bytes", "ep_combine_partial",
+              "ep_combine_reduce"):
         assert n in names, n
 
 
@@ -69,3 +71,34 @@ def test_host_side_validation(lib):
     assert L.ep_dispatch(None, 0, 1024, 8, None, 0, None, None, None) == 0
     assert L.ep_combine(None, None, None, 0, 1024, 8, None, None) == 0
     assert b"invalid" in L.ep_strerror(-1)
+
+
+def test_dedup_host_side_validation(lib):
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L = lib
+    L.ep_dedup_layout.argtypes = [P, I, I, I, I] + [P] * 6 + [P, ctypes.c_size_t, P]
+    L.ep_dedup_layout_workspace_bytes.argtypes = [I, I, I, I]
+    L.ep_dedup_layout_workspace_bytes.restype = ctypes.c_size_t
+    L.ep_combine_partial.argtypes = [P] * 5 + [I, I, I, I, P, P]
+    L.ep_combine_reduce.argtypes = [P, P, I, I, I, P, P]
+    fake = P(0x10000)          # never dereferenced: every case below fails a host check first
+    odd = P(0x10004)
+    outs = [fake] * 6
+    # P above 16, E % P != 0, P = 0
+    assert L.ep_dedup_layout(fake, 4, 8, 64, 32, *outs, None, 0, None) == -1
+    assert L.ep_dedup_layout(fake, 4, 8, 30, 8, *outs, None, 0, None) == -1
+    assert L.ep_dedup_layout(fake, 4, 8, 32, 0, *outs, None, 0, None) == -1
+    # null kmask; a chunked batch without its workspace
+    assert L.ep_dedup_layout(fake, 4, 8, 32, 8, *outs[:4], None, fake, None, 0, None) == -1
+    assert L.ep_dedup_layout_workspace_bytes(4096, 8, 256, 8) > 0
+    assert L.ep_dedup_layout_workspace_bytes(4, 8, 256, 32) == 0
+    assert L.ep_dedup_layout(fake, 4096, 8, 256, 8, *outs, None, 0, None) == -1
+    # combine levels: P out of range, H % 8, misaligned partial
+    assert L.ep_combine_partial(fake, fake, fake, fake, fake, 4, 1024, 8, 17, fake, None) == -1
+    assert L.ep_combine_partial(fake, fake, fake, fake, fake, 4, 1001, 8, 8, fake, None) == -1
+    assert L.ep_combine_partial(fake, fake, fake, fake, fake, 4, 1024, 8, 8, odd, None) == -1
+    assert L.ep_combine_reduce(fake, fake, 4, 1024, 0, fake, None) == -1
+    assert L.ep_combine_reduce(odd, fake, 4, 1024, 8, fake, None) == -1
+    # empty batches launch nothing
+    assert L.ep_combine_partial(None, None, None, None, None, 0, 1024, 8, 8, None, None) == 0
+    assert L.ep_combine_reduce(None, None, 0, 1024, 8, None, None) == 0
