@@ -139,6 +139,78 @@ class Path:
         return us
 
 
+class DedupPath(Path):
+    """The per-destination (dedup) step on the same inputs: ep_layout (expert
+    rows for the expert outputs) + ep_dedup_layout + the dedup dispatch
+    (ep_dispatch with K = P over tp_row) + ep_combine_partial +
+    ep_combine_reduce."""
+
+    def __init__(self, wl, seed=None):
+        super().__init__(wl, seed)
+        self.db = self.ep.EpDedupBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+        self.enqueue("dedup_layout")
+        self.torch.cuda.synchronize()
+        self.M = int(self.db.part_token_offset[wl.P].item())
+
+    def enqueue(self, phase="dedup"):
+        """dedup_step: ep_dedup_layout_dispatch (one launch for small batches)
+        + ep_combine_partial + ep_combine_reduce; dedup: the same step with
+        ep_layout, ep_dedup_layout and ep_dispatch as separate calls."""
+        s, b, db = self.stream, self.buf, self.db
+        if phase in ("dedup_step", "dedup_layout_dispatch"):
+            db.layout_dispatch(self.idx, self.x, b, s)
+        if phase in ("dedup_step", "combine_partial", "combine_reduce"):
+            if phase != "combine_reduce":
+                db.combine_partial(self.y, b.row_of_pair, self.w, s)
+            if phase != "combine_partial":
+                db.combine_reduce(s)
+            return
+        if phase in ("dedup", "layout"):
+            b.layout(self.idx, s)
+        if phase in ("dedup", "dedup_layout"):
+            db.layout(self.idx, s)
+        if phase in ("dedup", "dedup_dispatch"):
+            db.dispatch(self.x, s)
+        if phase == "dedup":
+            db.combine_partial(self.y, b.row_of_pair, self.w, s)
+            db.combine_reduce(s)
+
+
+def dedup_bytes(wl, N, M):
+    """Algorithmic HBM bytes of the dedup step's kernels, and the bytes that
+    would cross between GPUs (rows sent to a destination and back)."""
+    T, H = wl.T, wl.H
+    row = H + (H // 128) * 4 if wl.payload == "fp8" else 2 * H
+    b = {"dedup_dispatch": T * 2 * H + M * row,
+         "dedup_layout_dispatch": T * 2 * H + M * row,
+         "combine_partial": N * 2 * H + M * 2 * H,
+         "combine_reduce": M * 2 * H + T * 2 * H}
+    b["link_dedup"] = M * row + M * 2 * H
+    b["link_plain"] = N * row + N * 2 * H
+    return b
+
+
+def dedup_report(wl, steps=1000):
+    p = DedupPath(wl)
+    b = dedup_bytes(wl, p.N, p.M)
+    us = time_steps(p, steps, 20, "graph", "dedup_step")
+    us_sep = time_steps(p, steps, 20, "graph", "dedup")
+    ph = {k: p.phase_us(k) for k in ("dedup_layout_dispatch", "layout", "dedup_layout",
+                                     "dedup_dispatch", "combine_partial", "combine_reduce")}
+    out = {"workload": wl.name, "E": wl.E, "P": wl.P, "pairs_N": p.N, "copies_M": p.M,
+           "us_per_step_graph": round(us, 3),
+           "step": "ep_dedup_layout_dispatch + ep_combine_partial + ep_combine_reduce",
+           "us_per_step_graph_separate_calls": round(us_sep, 3),
+           "phases_us": {k: round(v, 3) for k, v in ph.items()},
+           "phase_GBps": {k: round(b[k] / (ph[k] * 1e-6) / 1e9, 1)
+                          for k in ("dedup_layout_dispatch", "dedup_dispatch", "combine_partial",
+                                    "combine_reduce")},
+           "link_bytes_dedup": b["link_dedup"], "link_bytes_plain": b["link_plain"],
+           "link_bytes_ratio": round(b["link_dedup"] / max(b["link_plain"], 1), 4)}
+    del p
+    return out
+
+
 def recorded_traffic(phase, workload):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     readings (profiles/traffic.txt), or None when there is no reading for this
@@ -253,8 +325,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-targets", action="store_true")
+    ap.add_argument("--no-dedup", action="store_true")
     ap.add_argument("--only", choices=["layout", "dispatch", "combine", "layout_dispatch", "step",
-                                       "step3"],
+                                       "step3", "dedup_layout", "dedup_dispatch", "combine_partial",
+                                       "combine_reduce", "dedup", "dedup_layout_dispatch",
+                                       "dedup_step"],
                     help="profiling mode: launch only this phase (eagerly) steps times, print nothing else")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="profiling mode: first run one device copy of this many MiB (counter calibration)")
@@ -279,8 +354,8 @@ def main():
             torch.cuda.synchronize()
             print("calib copy %d bytes" % n, flush=True)
         if args.only:
-            p = Path(wl)
-            p.enqueue("step3")
+            p = DedupPath(wl) if args.only.startswith(("dedup", "combine_")) else Path(wl)
+            p.enqueue("dedup" if isinstance(p, DedupPath) else "step3")
             torch.cuda.synchronize()
             for _ in range(args.warmup + args.steps):
                 p.enqueue(args.only)
@@ -366,6 +441,10 @@ def main():
         del pm
         del pb
         res["targets"] = tg
+
+    if not args.no_dedup:
+        res["dedup"] = [dedup_report(wl),
+                        dedup_report(wl.with_(name=wl.name + "_e32p8", E=32, P=8))]
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, p.d, p.N, args.cpu_seconds)

@@ -49,6 +49,9 @@ _SIGS = {
     "ep_dedup_layout_workspace_bytes": ([_I, _I, _I, _I], _SZ),
     "ep_dedup_layout": ([_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "ep_combine_partial": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
+    "ep_dedup_layout_dispatch_workspace_bytes": ([_I, _I, _I, _I], _SZ),
+    "ep_dedup_layout_dispatch": ([_P, _P, _I, _I, _I, _I, _I, _I] + [_P] * 12 + [_P, _SZ, _P, _P, _P],
+                                 _I),
     "ep_combine_reduce": ([_P, _P, _I, _I, _I, _P, _P], _I),
     "ep_strerror": ([_I], ctypes.c_char_p),
     "ep_last_hip_error": ([], _I),
@@ -180,6 +183,28 @@ def ep_dedup_layout(topk_idx, E, P, tp_row, part_tokens, part_token_offset, tp_s
         _ptr(tp_src), _ptr(kmask), _ptr(status), _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def ep_dedup_layout_dispatch_workspace_bytes(T: int, K: int, E: int, P: int) -> int:
+    return int(_lib.ep_dedup_layout_dispatch_workspace_bytes(T, K, E, P))
+
+
+def ep_dedup_layout_dispatch(topk_idx, x, E, P, payload, expert_count, expert_offset, part_count,
+                             part_offset, row_of_pair, src_pair, tp_row, part_tokens,
+                             part_token_offset, tp_src, kmask, status, ws, recv_x,
+                             recv_scales=None, stream=None):
+    """Per-expert layout + dedup layout + dedup dispatch (one launch for small batches)."""
+    _dt(topk_idx, torch.int32)
+    _dt(x, torch.bfloat16, torch.int16, torch.uint16)
+    payload = PAYLOADS.get(payload, payload)
+    T, K = topk_idx.shape
+    H = x.shape[1]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("ep_dedup_layout_dispatch", _lib.ep_dedup_layout_dispatch(
+        _ptr(topk_idx), _ptr(x), T, H, K, E, P, payload, _ptr(expert_count), _ptr(expert_offset),
+        _ptr(part_count), _ptr(part_offset), _ptr(row_of_pair), _ptr(src_pair), _ptr(tp_row),
+        _ptr(part_tokens), _ptr(part_token_offset), _ptr(tp_src), _ptr(kmask), _ptr(status),
+        _ptr(ws), ws_bytes, _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
+
+
 def ep_combine_partial(expert_out, row_of_pair, topk_w, tp_row, kmask, P, partial, stream=None):
     """Level 1: expert_out bf16 [T*K, H] -> partial bf16 [T*P, H] (rows of present couples)."""
     _dt(expert_out, torch.bfloat16, torch.int16, torch.uint16)
@@ -295,7 +320,7 @@ class EpDedupBuffers:
         self.tp_src = torch.empty(T * P, **i32)
         self.kmask = torch.empty(T * P, **i32)
         self.status = torch.empty(1, **i32)
-        wsb = ep_dedup_layout_workspace_bytes(T, K, E, P)
+        wsb = ep_dedup_layout_dispatch_workspace_bytes(T, K, E, P)
         self.ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
         if payload == "fp8":
             self.recv_x = torch.empty((T * P, H), dtype=torch.uint8, device=dev)
@@ -310,6 +335,15 @@ class EpDedupBuffers:
         ep_dedup_layout(topk_idx, self.E, self.P, self.tp_row, self.part_tokens,
                         self.part_token_offset, self.tp_src, self.kmask, self.status, self.ws,
                         stream)
+
+    def layout_dispatch(self, topk_idx, x, plain, stream=None):
+        """ep_dedup_layout_dispatch: the per-expert layout into `plain` (an
+        EpBuffers of the same shape), the dedup layout and dispatch here."""
+        ep_dedup_layout_dispatch(topk_idx, x, self.E, self.P, self.payload, plain.expert_count,
+                                 plain.expert_offset, plain.part_count, plain.part_offset,
+                                 plain.row_of_pair, plain.src_pair, self.tp_row, self.part_tokens,
+                                 self.part_token_offset, self.tp_src, self.kmask, self.status,
+                                 self.ws, self.recv_x, self.recv_scales, stream)
 
     def dispatch(self, x, stream=None):
         """One copy of each token per partition it reaches (ep_dispatch, K = P, tp_row)."""

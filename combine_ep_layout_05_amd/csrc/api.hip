@@ -145,6 +145,58 @@ int ep_dedup_layout(const int32_t* topk_idx, int T, int K, int E, int P, int32_t
                                             (hipStream_t)stream));
 }
 
+size_t ep_dedup_layout_dispatch_workspace_bytes(int T, int K, int E, int P)
+{
+    if (!routing_ok(T, K) || !dedup_ok(T, P) || E < 1 || E > EP_MAX_EXPERTS || E % P != 0) return 0;
+    const size_t a = ep::layout_workspace_bytes(T, K, E);
+    const size_t b = ep::dedup_layout_workspace_bytes(T, P);
+    return a > b ? a : b;
+}
+
+int ep_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
+                             int P, int payload, int32_t* expert_count, int32_t* expert_offset,
+                             int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
+                             int32_t* src_pair, int32_t* tp_row, int32_t* part_tokens,
+                             int32_t* part_token_offset, int32_t* tp_src, uint32_t* kmask,
+                             uint32_t* status, void* ws, size_t ws_bytes, void* recv_x,
+                             float* recv_scales, void* stream)
+{
+    if (payload != EP_PAYLOAD_FP8_E4M3FN && payload != EP_PAYLOAD_BF16) return EP_ENOTSUP;
+    if (!routing_ok(T, K) || !dedup_ok(T, P) || E < 1 || E > EP_MAX_EXPERTS || E % P != 0 || H <= 0)
+        return EP_EINVAL;
+    if (payload == EP_PAYLOAD_FP8_E4M3FN && H % ep::kScaleBlock != 0) return EP_EINVAL;
+    if (payload == EP_PAYLOAD_BF16 && H % ep::kColsPerLane != 0) return EP_EINVAL;
+    if (!ptr_ok(expert_count, 4) || !ptr_ok(expert_offset, 4) || !ptr_ok(part_count, 4) ||
+        !ptr_ok(part_offset, 4) || !ptr_ok(part_tokens, 4) || !ptr_ok(part_token_offset, 4) ||
+        !ptr_ok(status, 4))
+        return EP_EINVAL;
+    if (T > 0) {
+        if (!ptr_ok(topk_idx, 4) || !ptr_ok(row_of_pair, 4) || !ptr_ok(src_pair, 4) ||
+            !ptr_ok(tp_row, 4) || !ptr_ok(tp_src, 4) || !ptr_ok(kmask, 4) || !ptr_ok(x, 16) ||
+            !ptr_ok(recv_x, 16))
+            return EP_EINVAL;
+        if (payload == EP_PAYLOAD_FP8_E4M3FN && !ptr_ok(recv_scales, 4)) return EP_EINVAL;
+    }
+    const size_t need = ep_dedup_layout_dispatch_workspace_bytes(T, K, E, P);
+    if (need > 0 && (ws_bytes < need || !ptr_ok(ws, 16))) return EP_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (T > 0 && ep::fused_layout_dispatch_fits(T, K))
+        return from_hip(ep::launch_dedup_layout_dispatch(
+            topk_idx, x, T, H, K, E, P, payload, expert_count, expert_offset, part_count,
+            part_offset, row_of_pair, src_pair, tp_row, part_tokens, part_token_offset, tp_src,
+            kmask, status, recv_x, recv_scales, s));
+    // larger batches: the two layouts one after the other on the stream (they
+    // share the workspace), then the dispatch to the dedup rows
+    int rc = from_hip(ep::launch_layout(topk_idx, T, K, E, P, expert_count, expert_offset,
+                                        part_count, part_offset, row_of_pair, src_pair, status,
+                                        ws, s));
+    if (rc != EP_OK) return rc;
+    rc = from_hip(ep::launch_dedup_layout(topk_idx, T, K, E, P, tp_row, part_tokens,
+                                          part_token_offset, tp_src, kmask, status, ws, s));
+    if (rc != EP_OK || T == 0) return rc;
+    return from_hip(ep::launch_dispatch(x, T, H, P, tp_row, payload, recv_x, recv_scales, s));
+}
+
 int ep_combine_partial(const uint16_t* expert_out, const int32_t* row_of_pair,
                        const float* topk_w, const int32_t* tp_row, const uint32_t* kmask, int T,
                        int H, int K, int P, uint16_t* partial, void* stream)

@@ -20,12 +20,12 @@
 // The same kernel runs the two levels of the per-destination (dedup) combine
 // (UCCL PR #749: tokens batched per destination; MoRI PR #614,
 // DispatchIntraNode paragraph: one copy of a token per destination):
-//   partial: one item per (token, partition) couple that has a row; it sums,
-//            in k order, only the top-k entries whose bit is set in that
-//            couple's mask and writes the bf16 partial to the couple's row;
-//   reduce:  one item per token; it adds the token's partial rows in
-//            partition order (weight 1: fmaf(1, v, acc) is the correctly
-//            rounded acc + v) and writes the bf16 result.
+//   partial: for each partition holding a copy of the token, sums in k order
+//            only the top-k entries whose bit is set in that copy's mask and
+//            writes the bf16 partial to the copy's row;
+//   reduce:  adds the token's partial rows in partition order (weight 1:
+//            fmaf(1, v, acc) is the correctly rounded acc + v) and writes
+//            the bf16 result.
 #include "ep_device.h"
 #include "ep_launch.h"
 #include "ep_numerics.h"
@@ -35,10 +35,48 @@ namespace {
 
 enum CombineMode { kPlain = 0, kPartial = 1, kReduce = 2 };
 
-// Plain and reduce: an item is (token t, column step); its K source rows are
-// row_of_pair[t*K ..] (tp_row with K = P for reduce) and it writes out row t.
-// Partial: an item is (couple j = t*P + p, column step); it writes row
-// tp_row[j] of `out` (skipped when -1) from the entries in kmask[j].
+// acc[0..7] = fmaf over k = 0..K-1 in order, for the k with bit k of `use`
+// set and a source row (row_k >= 0), of w_k * y[row_k, 8 columns].  rows and
+// weights are lane-k values of `myrow` / `myw`; v[k] holds the loaded columns.
+template <int kMaxK>
+__device__ __forceinline__ uint4 reduce_rows(const uint4 (&v)[kMaxK], int myrow, float myw, int K,
+                                             uint32_t use)
+{
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        if (k < K && ((use >> k) & 1u)) {
+            const int r = read_lane(myrow, k);
+            if (r >= 0) {
+                const float wk = __builtin_bit_cast(float, read_lane(__builtin_bit_cast(int, myw), k));
+                acc[0] = __builtin_fmaf(wk, bf16_lo(v[k].x), acc[0]);
+                acc[1] = __builtin_fmaf(wk, bf16_hi(v[k].x), acc[1]);
+                acc[2] = __builtin_fmaf(wk, bf16_lo(v[k].y), acc[2]);
+                acc[3] = __builtin_fmaf(wk, bf16_hi(v[k].y), acc[3]);
+                acc[4] = __builtin_fmaf(wk, bf16_lo(v[k].z), acc[4]);
+                acc[5] = __builtin_fmaf(wk, bf16_hi(v[k].z), acc[5]);
+                acc[6] = __builtin_fmaf(wk, bf16_lo(v[k].w), acc[6]);
+                acc[7] = __builtin_fmaf(wk, bf16_hi(v[k].w), acc[7]);
+            }
+        }
+    }
+    uint4 o;
+    o.x = pack2_bf16(acc[0], acc[1]);
+    o.y = pack2_bf16(acc[2], acc[3]);
+    o.z = pack2_bf16(acc[4], acc[5]);
+    o.w = pack2_bf16(acc[6], acc[7]);
+    return o;
+}
+
+// An item is (token t, 512-column step).  Its K source rows are
+// row_of_pair[t*K ..] (tp_row with K = P for reduce, weight 1).
+// Plain and reduce write row t of `out`.  Partial loads the token's K expert
+// rows once and, for each partition p with a copy of t (tp_row[t*P+p] >= 0,
+// taken in ascending p), reduces the entries of kmask[t*P+p] into row
+// tp_row[t*P+p] of `out`: every expert row is read once, as in the plain
+// combine, and no wave is spent on (token, partition) couples without a copy.
 template <int kMaxK, bool kStream, int kMode>
 __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
     const uint16_t* __restrict__ y, const int32_t* __restrict__ row_of_pair,
@@ -50,22 +88,23 @@ __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
     const int stride = gridDim.x * kMoveWaves;
     for (int item = blockIdx.x * kMoveWaves + wave_uniform(threadIdx.x / kWave); item < n_items;
          item += stride) {                   // n_items + stride < 2^31 (checked by the launcher)
-        const int u = item / steps_per_token;
-        const int col0 = (item - u * steps_per_token) * kStepCols + lane * kColsPerLane;
-        int t = u, orow = u;
-        uint32_t use = ~0u;
-        if constexpr (kMode == kPartial) {
-            t = u / P;
-            orow = tp_row[u];
-            if (orow < 0 || orow >= out_rows) continue;   // no copy of t in this partition
-            use = kmask[u];
-        }
+        const int t = item / steps_per_token;
+        const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
         const bool active = col0 < H;
-        int myrow = (lane < K && ((use >> lane) & 1u)) ? row_of_pair[(int64_t)t * K + lane] : -1;
+        int myrow = (lane < K) ? row_of_pair[(int64_t)t * K + lane] : -1;
         if (myrow >= n_rows) myrow = -1;     // not a receive row: treated as masked
         float myw = 0.0f;
         if constexpr (kMode == kReduce) myw = 1.0f;
         else myw = (lane < K) ? topk_w[(int64_t)t * K + lane] : 0.0f;
+        int prow = -1;
+        uint32_t pmask = 0u;
+        if constexpr (kMode == kPartial) {
+            if (lane < P) {
+                prow = tp_row[(int64_t)t * P + lane];
+                pmask = kmask[(int64_t)t * P + lane];
+            }
+            if (prow >= out_rows) prow = -1;
+        }
 
         uint4 v[kMaxK];
 #pragma unroll
@@ -76,33 +115,19 @@ __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
                 if (r >= 0 && active) v[k] = load16<kStream>(y + (int64_t)r * H + col0);
             }
         }
-        float acc[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < kMaxK; ++k) {
-            if (k < K) {
-                const int r = read_lane(myrow, k);
-                if (r >= 0) {
-                    const float wk = __builtin_bit_cast(float, read_lane(__builtin_bit_cast(int, myw), k));
-                    acc[0] = __builtin_fmaf(wk, bf16_lo(v[k].x), acc[0]);
-                    acc[1] = __builtin_fmaf(wk, bf16_hi(v[k].x), acc[1]);
-                    acc[2] = __builtin_fmaf(wk, bf16_lo(v[k].y), acc[2]);
-                    acc[3] = __builtin_fmaf(wk, bf16_hi(v[k].y), acc[3]);
-                    acc[4] = __builtin_fmaf(wk, bf16_lo(v[k].z), acc[4]);
-                    acc[5] = __builtin_fmaf(wk, bf16_hi(v[k].z), acc[5]);
-                    acc[6] = __builtin_fmaf(wk, bf16_lo(v[k].w), acc[6]);
-                    acc[7] = __builtin_fmaf(wk, bf16_hi(v[k].w), acc[7]);
-                }
+        if constexpr (kMode == kPartial) {
+            uint64_t present = __ballot(prow >= 0);   // lanes < P only: prow is -1 elsewhere
+            while (present) {
+                const int p = __builtin_ctzll(present);
+                present &= present - 1;
+                const uint32_t use = (uint32_t)read_lane((int)pmask, p);
+                const int orow = read_lane(prow, p);
+                const uint4 o = reduce_rows<kMaxK>(v, myrow, myw, K, use);
+                if (active) store16<kStream>(out + (int64_t)orow * H + col0, o);
             }
-        }
-        if (active) {
-            uint4 o;
-            o.x = pack2_bf16(acc[0], acc[1]);
-            o.y = pack2_bf16(acc[2], acc[3]);
-            o.z = pack2_bf16(acc[4], acc[5]);
-            o.w = pack2_bf16(acc[6], acc[7]);
-            store16<kStream>(out + (int64_t)orow * H + col0, o);
+        } else {
+            const uint4 o = reduce_rows<kMaxK>(v, myrow, myw, K, ~0u);
+            if (active) store16<kStream>(out + (int64_t)t * H + col0, o);
         }
     }
 }
@@ -162,8 +187,8 @@ hipError_t launch_combine_partial(const uint16_t* y, const int32_t* row_of_pair,
                                   const uint32_t* kmask, int T, int H, int K, int P,
                                   uint16_t* partial, hipStream_t stream)
 {
-    return launch_combine_mode<kPartial>(y, row_of_pair, topk_w, T * P, H, K, T * K, tp_row, kmask,
-                                         P, T * P, (int64_t)T * K, partial, stream);
+    return launch_combine_mode<kPartial>(y, row_of_pair, topk_w, T, H, K, T * K, tp_row, kmask, P,
+                                         T * P, (int64_t)T * K, partial, stream);
 }
 
 hipError_t launch_combine_reduce(const uint16_t* partial, const int32_t* tp_row, int T, int H,

@@ -46,23 +46,19 @@ __device__ __forceinline__ void store_item(uint4 v, uint2 q, float scale, int my
                                            float* __restrict__ recv_scales)
 {
     const bool active = col0 < H;
-    if constexpr (kPayload == 0) {
-        const int nb = H / kScaleBlock;
-        for (int k = 0; k < K; ++k) {
-            const int r = read_lane(myrow, k);
-            if (r < 0 || r >= n_rows) continue;     // masked (or not a receive row)
-            if (active) {
-                store8<kStream>(recv_x + (int64_t)r * H + col0, q);
-                if ((lane % kLanesPerScaleBlock) == 0)
-                    recv_scales[(int64_t)r * nb + col0 / kScaleBlock] = scale;
-            }
-        }
-    } else {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(recv_x);
-        for (int k = 0; k < K; ++k) {
-            const int r = read_lane(myrow, k);
-            if (r < 0 || r >= n_rows) continue;
-            if (active) store16<kStream>(dst + (int64_t)r * H + col0, v);
+    // only the entries that have a receive row (masked ones cost nothing)
+    uint64_t live = __ballot(lane < K && myrow >= 0 && myrow < n_rows);
+    while (live) {
+        const int k = __builtin_ctzll(live);
+        live &= live - 1;
+        const int r = read_lane(myrow, k);
+        if (!active) continue;
+        if constexpr (kPayload == 0) {
+            store8<kStream>(recv_x + (int64_t)r * H + col0, q);
+            if ((lane % kLanesPerScaleBlock) == 0)
+                recv_scales[(int64_t)r * (H / kScaleBlock) + col0 / kScaleBlock] = scale;
+        } else {
+            store16<kStream>(reinterpret_cast<uint16_t*>(recv_x) + (int64_t)r * H + col0, v);
         }
     }
 }
@@ -140,6 +136,25 @@ __global__ __launch_bounds__(kMoveThreads) void dispatch_kernel(
 // holding a token's first 512-column step writes that token's row_of_pair
 // and src_pair entries.  Every output equals ep_layout's followed by
 // ep_dispatch's.
+//
+// The per-destination (dedup) variant derives in the same launch, from the
+// same ids, the dedup layout as well: each token's partition set (every
+// valid entry ors its partition bit into its token's LDS word; e / L and
+// entry / K by multiply-shifts that are exact in these ranges), the
+// per-partition token totals and the tokens before this workgroup's first
+// token (counted by the entry that finds its bit still clear), their scan,
+// and the rows and top-k masks of its own tokens' (token, partition) couples.
+// The payload then goes once to each of a token's partitions (the dedup
+// rows) instead of once per top-k entry; both layouts are written out, the
+// per-expert one for the expert side and the combine.
+struct DedupOutputs {
+    int32_t* tp_row;
+    int32_t* part_tokens;
+    int32_t* part_token_offset;
+    int32_t* tp_src;
+    uint32_t* kmask;
+};
+
 struct FusedSmem {
     int32_t ids[kFusedMaxPairs];
     int32_t cnt[kMaxExperts];
@@ -148,19 +163,26 @@ struct FusedSmem {
     int32_t rows[kMoveWaves * kMaxTopK];
     int32_t wsum[kMoveWaves];
     uint32_t bad;
+    // dedup variant
+    int32_t ptot[kMaxTopK];                    // tokens per partition
+    int32_t pbef[kMaxTopK];                    // of those, before this workgroup's first token
+    int32_t ptoff[kMaxTopK + 1];               // exclusive scan of ptot
+    uint32_t tpres[kFusedMaxPairs];            // partition set (bit p) of every token
+    int32_t drows[kMoveWaves * kMaxTopK];      // own couples' dedup rows (-1: absent)
+    uint32_t dmask[kMoveWaves * kMaxTopK];     // own couples' top-k masks
 };
 
 constexpr int kFusedIdsPerThread = kFusedMaxPairs / kMoveThreads;   // 8
 static_assert(kFusedIdsPerThread * kMoveThreads == kFusedMaxPairs, "ids split evenly");
 
-template <int kPayload>
+template <int kPayload, bool kDedup>
 __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, int n, int H, int K, int E,
     int P, int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
     int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair,
     uint32_t* __restrict__ status, uint8_t* __restrict__ recv_x, float* __restrict__ recv_scales,
-    int steps_per_token, int n_items)
+    int steps_per_token, int n_items, DedupOutputs dd)
 {
     __shared__ FusedSmem s;
     const int tid = threadIdx.x;
@@ -172,7 +194,8 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
     const int t_lo = item0 / steps_per_token;
     const int t_hi = last / steps_per_token;
     const int p_lo = t_lo * K;
-    const int nq = (t_hi - t_lo + 1) * K;         // <= kMoveWaves * kMaxTopK = 64
+    const int nown = t_hi - t_lo + 1;             // own tokens, <= kMoveWaves
+    const int nq = nown * K;                      // <= kMoveWaves * kMaxTopK = 64
 
     // every load is independent: x vector and all ids together
     int t = 0, col0 = H;
@@ -190,6 +213,10 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
     }
     for (int e = tid; e < E; e += kMoveThreads) { s.cnt[e] = 0; s.before[e] = 0; }
     if (tid == 0) s.bad = 0u;
+    if constexpr (kDedup) {
+        if (tid < P) { s.ptot[tid] = 0; s.pbef[tid] = 0; }
+        for (int tt = tid; tt < n / K; tt += kMoveThreads) s.tpres[tt] = 0u;
+    }
 #pragma unroll
     for (int j = 0; j < kFusedIdsPerThread; ++j) {
         const int p = j * kMoveThreads + tid;
@@ -197,6 +224,8 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
     }
     __syncthreads();
 
+    const int T = n / K;
+    const int L = E / P;
     bool bad = false;
 #pragma unroll
     for (int j = 0; j < kFusedIdsPerThread; ++j) {
@@ -209,6 +238,37 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
         }
     }
     if (bad) s.bad = 1u;
+    if constexpr (kDedup) {
+        // partition set of every token: each valid entry ors its partition
+        // bit into its token's LDS word; the entry that finds the bit still
+        // clear counts the token once for that partition, and once more in
+        // the total before t_lo when the token precedes the workgroup's own
+        // (order-free sums)
+        const uint32_t magic_l = (1u << 20) / (uint32_t)L + 1u;   // e / L = (e * magic_l) >> 20, e < 1024
+        const uint32_t magic_k = (1u << 16) / (uint32_t)K + 1u;   // p / K = (p * magic_k) >> 16, p < 2048
+        uint32_t old[kFusedIdsPerThread], pk[kFusedIdsPerThread];
+        int tk[kFusedIdsPerThread];
+#pragma unroll
+        for (int j = 0; j < kFusedIdsPerThread; ++j) {
+            const int p = j * kMoveThreads + tid;
+            const int e = ids[j];
+            tk[j] = -1;
+            old[j] = 0u;
+            pk[j] = 0u;
+            if (e >= 0 && e < E) {
+                tk[j] = (int)(((uint32_t)p * magic_k) >> 16);
+                pk[j] = ((uint32_t)e * magic_l) >> 20;
+                old[j] = atomicOr(&s.tpres[tk[j]], 1u << pk[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kFusedIdsPerThread; ++j) {
+            if (tk[j] >= 0 && !((old[j] >> pk[j]) & 1u)) {
+                atomicAdd(&s.ptot[pk[j]], 1);
+                if (tk[j] < t_lo) atomicAdd(&s.pbef[pk[j]], 1);
+            }
+        }
+    }
     // while the atomics drain: quantise this wave's item, and (wave 0) find the
     // peers of the workgroup's own entries
     float scale = 0.0f;
@@ -254,14 +314,49 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
         if (e < E) s.off[e] = run;
         run += c[j];
     }
+    if constexpr (kDedup) {
+        if (w == 1) {                              // partition offsets (totals complete: barrier above)
+            const int pc = (lane < P) ? s.ptot[lane] : 0;
+            const int pincl = wave_inclusive_scan(pc);
+            if (lane < P) s.ptoff[lane] = pincl - pc;
+            if (lane == P - 1) s.ptoff[P] = pincl;
+        }
+    }
     __syncthreads();
 
     if (w == 0 && lane < nq) s.rows[lane] = mvalid ? s.off[me] + s.before[me] + rank : -1;
+    if constexpr (kDedup) {
+        if (w == 1 && lane < nown * P) {           // own couples: (token t_lo + i, partition p)
+            const int i = lane / P, p = lane - i * P;
+            const int lo = p * L;
+            const int base = (t_lo + i) * K;
+            int before = 0;
+#pragma unroll
+            for (int j = 0; j < kMoveWaves - 1; ++j)
+                before += (j < i) ? (int)((s.tpres[t_lo + j] >> p) & 1u) : 0;
+            const bool present = (s.tpres[t_lo + i] >> p) & 1u;
+            uint32_t m = 0u;
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k) {   // reads issued together (index clamped below K)
+                const int e = s.ids[base + (k < K ? k : K - 1)];
+                if (k < K && (uint32_t)e - (uint32_t)lo < (uint32_t)L) m |= 1u << k;
+            }
+            s.drows[lane] = present ? s.ptoff[p] + s.pbef[p] + before : -1;
+            s.dmask[lane] = m;
+        }
+    }
     __syncthreads();
 
     if (item < n_items) {
-        const int myrow = (lane < K) ? s.rows[(t - t_lo) * K + lane] : -1;
-        store_item<kPayload, false>(v, q, scale, myrow, col0, lane, H, K, n, recv_x, recv_scales);
+        if constexpr (kDedup) {
+            const int myrow = (lane < P) ? s.drows[(t - t_lo) * P + lane] : -1;
+            store_item<kPayload, false>(v, q, scale, myrow, col0, lane, H, P, T * P, recv_x,
+                                        recv_scales);
+        } else {
+            const int myrow = (lane < K) ? s.rows[(t - t_lo) * K + lane] : -1;
+            store_item<kPayload, false>(v, q, scale, myrow, col0, lane, H, K, n, recv_x,
+                                        recv_scales);
+        }
     }
 
     // layout outputs, after the payload stores
@@ -283,7 +378,6 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
                 expert_offset[e] = s.off[e];
             }
         }
-        const int L = E / P;
         for (int p = tid; p < P; p += kMoveThreads) {
             const int lo = s.off[p * L];
             const int hi = (p + 1 < P) ? s.off[(p + 1) * L] : N;
@@ -298,6 +392,28 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
     }
     for (int r = N + blockIdx.x * kMoveThreads + tid; r < n; r += gridDim.x * kMoveThreads)
         src_pair[r] = -1;
+
+    if constexpr (kDedup) {
+        if (tid < nown * P) {
+            const int i = tid / P, p = tid - i * P;
+            const int tt = t_lo + i;
+            if (tt * steps_per_token >= item0) {  // this workgroup holds the token's first step
+                const int j = tt * P + p;
+                const int r = s.drows[tid];
+                dd.tp_row[j] = r;
+                dd.kmask[j] = s.dmask[tid];
+                if (r >= 0) dd.tp_src[r] = j;
+            }
+        }
+        const int M = s.ptoff[P];
+        if (blockIdx.x == 0 && tid < P) {
+            dd.part_tokens[tid] = s.ptot[tid];
+            dd.part_token_offset[tid] = s.ptoff[tid];
+            if (tid == 0) dd.part_token_offset[P] = M;
+        }
+        for (int r = M + blockIdx.x * kMoveThreads + tid; r < T * P; r += gridDim.x * kMoveThreads)
+            dd.tp_src[r] = -1;
+    }
 }
 
 __global__ __launch_bounds__(256) void e4m3fn_encode_kernel(const float* __restrict__ in, int64_t n,
@@ -356,16 +472,46 @@ hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, in
     const int n = T * K;
     const int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
     if (T == 0 || n > kFusedMaxPairs || blocks > kMaxGridBlocks) return hipErrorInvalidValue;
+    const DedupOutputs none{};
     if (payload == 0)
-        hipLaunchKernelGGL(layout_dispatch_kernel<0>, dim3((unsigned)blocks), dim3(kMoveThreads), 0,
-                           stream, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
-                           part_count, part_offset, row_of_pair, src_pair, status,
-                           (uint8_t*)recv_x, recv_scales, steps, (int)items);
+        hipLaunchKernelGGL((layout_dispatch_kernel<0, false>), dim3((unsigned)blocks),
+                           dim3(kMoveThreads), 0, stream, topk_idx, x, n, H, K, E, P, expert_count,
+                           expert_offset, part_count, part_offset, row_of_pair, src_pair, status,
+                           (uint8_t*)recv_x, recv_scales, steps, (int)items, none);
     else
-        hipLaunchKernelGGL(layout_dispatch_kernel<1>, dim3((unsigned)blocks), dim3(kMoveThreads), 0,
-                           stream, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
-                           part_count, part_offset, row_of_pair, src_pair, status,
-                           (uint8_t*)recv_x, nullptr, steps, (int)items);
+        hipLaunchKernelGGL((layout_dispatch_kernel<1, false>), dim3((unsigned)blocks),
+                           dim3(kMoveThreads), 0, stream, topk_idx, x, n, H, K, E, P, expert_count,
+                           expert_offset, part_count, part_offset, row_of_pair, src_pair, status,
+                           (uint8_t*)recv_x, nullptr, steps, (int)items, none);
+    return hipGetLastError();
+}
+
+hipError_t launch_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H,
+                                        int K, int E, int P, int payload, int32_t* expert_count,
+                                        int32_t* expert_offset, int32_t* part_count,
+                                        int32_t* part_offset, int32_t* row_of_pair,
+                                        int32_t* src_pair, int32_t* tp_row, int32_t* part_tokens,
+                                        int32_t* part_token_offset, int32_t* tp_src,
+                                        uint32_t* kmask, uint32_t* status, void* recv_x,
+                                        float* recv_scales, hipStream_t stream)
+{
+    const int steps = (H + kStepCols - 1) / kStepCols;
+    const int64_t items = (int64_t)T * steps;
+    const int n = T * K;
+    const int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
+    if (T == 0 || n > kFusedMaxPairs || P > kMaxTopK || blocks > kMaxGridBlocks)
+        return hipErrorInvalidValue;
+    const DedupOutputs dd{tp_row, part_tokens, part_token_offset, tp_src, kmask};
+    if (payload == 0)
+        hipLaunchKernelGGL((layout_dispatch_kernel<0, true>), dim3((unsigned)blocks),
+                           dim3(kMoveThreads), 0, stream, topk_idx, x, n, H, K, E, P, expert_count,
+                           expert_offset, part_count, part_offset, row_of_pair, src_pair, status,
+                           (uint8_t*)recv_x, recv_scales, steps, (int)items, dd);
+    else
+        hipLaunchKernelGGL((layout_dispatch_kernel<1, true>), dim3((unsigned)blocks),
+                           dim3(kMoveThreads), 0, stream, topk_idx, x, n, H, K, E, P, expert_count,
+                           expert_offset, part_count, part_offset, row_of_pair, src_pair, status,
+                           (uint8_t*)recv_x, nullptr, steps, (int)items, dd);
     return hipGetLastError();
 }
 

@@ -215,6 +215,28 @@ int ep_dedup_layout(const int32_t* topk_idx, int T, int K, int E, int P,
                     int32_t* tp_src, uint32_t* kmask, uint32_t* status,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes ep_dedup_layout_dispatch needs (0: none); host-only. */
+size_t ep_dedup_layout_dispatch_workspace_bytes(int T, int K, int E, int P);
+
+/*
+ * The sender's whole dedup step in one call: the per-expert layout (every
+ * output of ep_layout), the dedup layout (every output of ep_dedup_layout)
+ * and the dedup dispatch (ep_dispatch with K = P over tp_row), bit for bit
+ * the same as those three calls.  For T*K <= 2048 it is ONE kernel launch
+ * (each workgroup derives both layouts' values for its own tokens from the
+ * T*K ids); larger batches run the three calls' kernels back to back.
+ *   recv_x / recv_scales are sized for T*P rows (only rows < M are written).
+ *   ws: ep_dedup_layout_dispatch_workspace_bytes(T, K, E, P) bytes.
+ * Errors: those of the three calls.
+ */
+int ep_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
+                             int P, int payload, int32_t* expert_count, int32_t* expert_offset,
+                             int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
+                             int32_t* src_pair, int32_t* tp_row, int32_t* part_tokens,
+                             int32_t* part_token_offset, int32_t* tp_src, uint32_t* kmask,
+                             uint32_t* status, void* ws, size_t ws_bytes, void* recv_x,
+                             float* recv_scales, void* stream);
+
 /*
  * Combine level 1, at the destination: for every present couple (t, p),
  * partial[tp_row[t*P+p], c] = bf16_rne(acc), acc = 0.0f, then for k = 0..K-1

@@ -103,17 +103,23 @@ def compare(wl, got, ref, check_poison=True):
 DEDUP_KEYS = ("tp_row", "part_tokens", "part_token_offset", "tp_src", "kmask")
 
 
-def run_gpu_dedup(wl, d, stream=None):
+PLAIN_LAYOUT_KEYS = ("expert_count", "expert_offset", "part_count", "part_offset", "row_of_pair",
+                     "src_pair")
+
+
+def run_gpu_dedup(wl, d, stream=None, fused=False):
     """Per-destination path on the GPU: ep_layout (expert rows for the expert
     outputs), ep_dedup_layout, ep_dispatch with K = P over tp_row,
-    ep_combine_partial and ep_combine_reduce.  Buffers start poisoned."""
+    ep_combine_partial and ep_combine_reduce; fused=True runs
+    ep_dedup_layout_dispatch in place of the first three.  Buffers start
+    poisoned."""
     ep = gpu_lib()
     buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
     db = ep.EpDedupBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
     db.recv_x.view(torch.uint8).fill_(POISON_BYTE)
     if db.recv_scales is not None:
         db.recv_scales.view(torch.int32).fill_(POISON_F32_BITS)
-    for t in (db.tp_row, db.tp_src, db.kmask):
+    for t in (db.tp_row, db.tp_src, db.kmask, buf.row_of_pair, buf.src_pair):
         t.fill_(-7)
     db.partial.view(torch.int16).fill_(0x5A5A)
     db.out.view(torch.int16).fill_(0x5A5A)
@@ -121,16 +127,20 @@ def run_gpu_dedup(wl, d, stream=None):
     x = to_dev(d["x"].view(np.int16), torch.bfloat16)
     y = to_dev(d["y"].view(np.int16), torch.bfloat16)
     w = to_dev(d["w"])
-    buf.layout(idx, stream)
-    db.layout(idx, stream)
-    db.dispatch(x, stream)
+    if fused:
+        db.layout_dispatch(idx, x, buf, stream)
+    else:
+        buf.layout(idx, stream)
+        db.layout(idx, stream)
+        db.dispatch(x, stream)
     db.combine_partial(y, buf.row_of_pair, w, stream)
     db.combine_reduce(stream)
     torch.cuda.synchronize()
     res = {k: getattr(db, k).cpu().numpy() for k in DEDUP_KEYS}
     res["kmask"] = res["kmask"].view(np.uint32)
     res["status"] = db.status.cpu().numpy().view(np.uint32)
-    res["row_of_pair"] = buf.row_of_pair.cpu().numpy()
+    for k in PLAIN_LAYOUT_KEYS:
+        res[k] = getattr(buf, k).cpu().numpy()
     res["recv_x"] = db.recv_x.view(torch.uint8).cpu().numpy() if wl.payload == "fp8" else \
         db.recv_x.view(torch.int16).cpu().numpy().view(np.uint16)
     if db.recv_scales is not None:
@@ -144,7 +154,8 @@ def run_oracle_dedup(wl, d):
     lo = oracle.layout(d["idx"], wl.E, wl.P)
     dl = oracle.dedup_layout(d["idx"], wl.E, wl.P)
     res = dict(dl)
-    res["row_of_pair"] = lo["row_of_pair"]
+    for k in PLAIN_LAYOUT_KEYS:
+        res[k] = lo[k]
     if wl.payload == "fp8":
         res["recv_x"], res["recv_scales"] = oracle.dispatch_fp8(d["x"], dl["tp_row"], wl.P)
     else:
@@ -160,7 +171,7 @@ def compare_dedup(wl, got, ref):
     1 bf16 ulp; rows past M untouched.  Returns the number of differing
     partial + output values (expected 0: same fmaf / add order)."""
     from tests.helpers import bf16_ulp_distance
-    for k in DEDUP_KEYS + ("row_of_pair",):
+    for k in DEDUP_KEYS + PLAIN_LAYOUT_KEYS:
         np.testing.assert_array_equal(got[k], ref[k], err_msg="%s: %s" % (wl.name, k))
     assert int(got["status"][0]) == int(ref["status"][0]), (wl.name, "status")
     M = int(ref["part_token_offset"][wl.P])

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
               "ep_strerror", "ep_last_hip_error", "ep_graph_begin", "ep_graph_end",
               "ep_graph_launch", "ep_graph_destroy", "ep_e4m3fn_encode", "ep_layout_dispatch",
               "ep_dedup_layout", "ep_dedup_layout_workspace_bytes", "ep_combine_partial",
-              "ep_combine_reduce"):
+              "ep_combine_reduce", "ep_dedup_layout_dispatch",
+              "ep_dedup_layout_dispatch_workspace_bytes"):
         assert n in names, n
 
 
@@ -102,3 +103,28 @@ def test_dedup_host_side_validation(lib):
     # empty batches launch nothing
     assert L.ep_combine_partial(None, None, None, None, None, 0, 1024, 8, 8, None, None) == 0
     assert L.ep_combine_reduce(None, None, 0, 1024, 8, None, None) == 0
+
+
+def test_dedup_layout_dispatch_host_side_validation(lib):
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L = lib
+    L.ep_dedup_layout_dispatch.argtypes = [P, P, I, I, I, I, I, I] + [P] * 12 + [P, ctypes.c_size_t,
+                                                                               P, P, P]
+    L.ep_dedup_layout_dispatch_workspace_bytes.argtypes = [I, I, I, I]
+    L.ep_dedup_layout_dispatch_workspace_bytes.restype = ctypes.c_size_t
+    fake = P(0x10000)
+    outs = [fake] * 12
+    # bad payload; P above 16; fp8 with H % 128 != 0; misaligned x
+    assert L.ep_dedup_layout_dispatch(fake, fake, 4, 1024, 8, 32, 8, 5, *outs, None, 0, fake, fake,
+                                      None) == -2
+    assert L.ep_dedup_layout_dispatch(fake, fake, 4, 1024, 8, 64, 32, 0, *outs, None, 0, fake, fake,
+                                      None) == -1
+    assert L.ep_dedup_layout_dispatch(fake, fake, 4, 1000, 8, 32, 8, 0, *outs, None, 0, fake, fake,
+                                      None) == -1
+    assert L.ep_dedup_layout_dispatch(fake, P(0x10004), 4, 1024, 8, 32, 8, 0, *outs, None, 0, fake,
+                                      fake, None) == -1
+    # a large batch needs the larger of the two layouts' workspaces
+    need = L.ep_dedup_layout_dispatch_workspace_bytes(4096, 8, 256, 8)
+    assert need >= L.ep_layout_workspace_bytes(4096, 8, 256) > 0
+    assert L.ep_dedup_layout_dispatch(fake, fake, 4096, 1024, 8, 256, 8, 0, *outs, fake, need - 16,
+                                      fake, fake, None) == -1

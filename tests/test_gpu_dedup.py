@@ -15,11 +15,11 @@ from workloads import WORKLOADS, generate
 pytestmark = pytest.mark.gpu
 
 
-def _case(wl, seed=None, d=None):
-    print("dedup case %s T=%d H=%d E=%d P=%d K=%d %s seed=%s" % (
-        wl.name, wl.T, wl.H, wl.E, wl.P, wl.K, wl.payload, seed), flush=True)
+def _case(wl, seed=None, d=None, fused=False):
+    print("dedup case %s T=%d H=%d E=%d P=%d K=%d %s seed=%s fused=%s" % (
+        wl.name, wl.T, wl.H, wl.E, wl.P, wl.K, wl.payload, seed, fused), flush=True)
     d = generate(wl, seed=seed) if d is None else d
-    got = run_gpu_dedup(wl, d)
+    got = run_gpu_dedup(wl, d, fused=fused)
     ref = run_oracle_dedup(wl, d)
     ndiff = compare_dedup(wl, got, ref)
     assert ndiff == 0, "%s: %d partial/output values differ by 1 ulp" % (wl.name, ndiff)
@@ -59,6 +59,53 @@ DEDUP_EDGE = {
 def test_dedup_edge_shapes(edge):
     wl = WORKLOADS["tiny_4x1024"].with_(name="dedup_" + edge, **DEDUP_EDGE[edge])
     _case(wl, 79)
+
+
+FUSED_NAMES = ["tiny_4x1024", "ll_128x7168", "sweep_4x6144", "sweep_8x6144", "sweep_16x6144",
+               "bw_4096x7168_zipf"]
+
+
+@pytest.mark.parametrize("name", FUSED_NAMES)
+def test_dedup_layout_dispatch(name):
+    """ep_dedup_layout_dispatch (one launch up to T*K = 2048, three kernels
+    above): both layouts, dedup rows and scales equal to the oracle."""
+    wl = WORKLOADS[name]
+    _case(wl, wl.seed + 12, fused=True)
+
+
+FUSED_EDGE = {
+    "T1": dict(T=1),
+    "P1": dict(P=1, E=32),
+    "K1_many_tokens": dict(K=1, T=2048, H=128),          # 2048 tokens, one per lane of 8 waves
+    "K16_P16": dict(K=16, E=64, P=16),
+    "E1024_P16": dict(E=1024, P=16, T=64),               # L = 64
+    "E1024_P1": dict(E=1024, P=1, T=40),                 # L = 1024: the shift divide at its limit
+    "E96_P3": dict(E=96, P=3, T=50),                     # P not a power of two
+    "H128_tokens_share_wg": dict(H=128, T=200),          # 4 tokens per workgroup
+    "H640": dict(H=640, T=33),
+    "at_limit_2048": dict(T=256, H=256),
+    "over_limit_2056": dict(T=257, H=256),
+    "bf16": dict(payload="bf16", T=50, H=512),
+}
+
+
+@pytest.mark.parametrize("edge", list(FUSED_EDGE))
+def test_dedup_layout_dispatch_edges(edge):
+    wl = WORKLOADS["tiny_4x1024"].with_(name="dedup_fused_" + edge, **FUSED_EDGE[edge])
+    _case(wl, 80, fused=True)
+
+
+def test_dedup_fused_masked_duplicate_and_bad_ids():
+    wl = WORKLOADS["tiny_4x1024"].with_(name="dedup_fused_ids", T=40, H=256, E=16, P=4, K=6)
+    d = generate(wl, seed=9)
+    rng = np.random.default_rng(9)
+    idx = rng.integers(-3, 20, size=(wl.T, wl.K)).astype(np.int32)
+    idx[3] = 7
+    idx[4] = -1
+    idx[5] = 99
+    d["idx"] = idx
+    got, ref, _ = _case(wl, d=d, fused=True)
+    assert int(got["status"][0]) == 1
 
 
 def test_dedup_masked_duplicate_and_bad_ids():
