@@ -37,21 +37,22 @@ namespace ep {
 namespace {
 
 // Write one item to the token's valid rows: the fp8 bytes q and the block
-// scale (kPayload 0) or the bf16 vector v unchanged (kPayload 1).  `myrow`
-// holds, in lane k < K, the receive row of the token's pair k.
+// scale (kPayload 0) or the bf16 vector v unchanged (kPayload 1).  Lanes
+// lane0 .. lane0+K-1 of `myrow` hold the receive rows of the token's pairs
+// 0..K-1; only rows in [0, n_rows) are written, so masked entries cost
+// nothing.
 template <int kPayload, bool kStream>
-__device__ __forceinline__ void store_item(uint4 v, uint2 q, float scale, int myrow, int col0,
-                                           int lane, int H, int K, int n_rows,
+__device__ __forceinline__ void store_item(uint4 v, uint2 q, float scale, int myrow, int lane0,
+                                           int col0, int lane, int H, int K, int n_rows,
                                            uint8_t* __restrict__ recv_x,
                                            float* __restrict__ recv_scales)
 {
     const bool active = col0 < H;
-    // only the entries that have a receive row (masked ones cost nothing)
-    uint64_t live = __ballot(lane < K && myrow >= 0 && myrow < n_rows);
+    uint64_t live = __ballot(lane >= lane0 && lane < lane0 + K && myrow >= 0 && myrow < n_rows);
     while (live) {
-        const int k = __builtin_ctzll(live);
+        const int l = __builtin_ctzll(live);
         live &= live - 1;
-        const int r = read_lane(myrow, k);
+        const int r = read_lane(myrow, l);
         if (!active) continue;
         if constexpr (kPayload == 0) {
             store8<kStream>(recv_x + (int64_t)r * H + col0, q);
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(kMoveThreads) void dispatch_kernel(
 
         float scale;
         const uint2 q = prepare_item<kPayload>(v, scale);
-        store_item<kPayload, kStream>(v, q, scale, myrow, col0, lane, H, K, n_rows, recv_x,
+        store_item<kPayload, kStream>(v, q, scale, myrow, 0, col0, lane, H, K, n_rows, recv_x,
                                       recv_scales);
 
         if (next >= n_items) break;
@@ -124,29 +125,32 @@ __global__ __launch_bounds__(kMoveThreads) void dispatch_kernel(
 // 4/8/16 tokens).  Here every dispatch workgroup derives, from all T*K ids (at
 // most 8 KB, read from L2), exactly the layout values it needs, so no
 // separate layout launch precedes the dispatch:
-//   - the per-expert totals (LDS atomics: integer sums, order-free) and their
-//     exclusive scan -> expert offsets (4 experts per thread, DPP wave scan);
-//   - per expert, the number of entries before this workgroup's first token;
+//   - the per-expert totals (LDS atomics: integer sums, order-free), and per
+//     expert the number of entries before this workgroup's first token;
+//   - the exclusive scan of the totals (4 experts per thread, DPP wave scan;
+//     each thread leaves its experts' in-wave prefixes in LDS and the wave
+//     totals complete them after one barrier);
 //   - the slots of its own tokens' entries: offset + entries before + rank
-//     among the workgroup's own entries (ballot match-any in one wave).
-// The x vectors are loaded first and quantised while the histogram atomics
-// drain, and the layout outputs are written after the payload stores, so
-// neither sits on the path from the ids to the receive rows.  Workgroup 0
-// writes the counts, offsets, partition sums and status; the workgroup
-// holding a token's first 512-column step writes that token's row_of_pair
-// and src_pair entries.  Every output equals ep_layout's followed by
-// ep_dispatch's.
+//     among the workgroup's own entries (ballot match-any, done by every wave
+//     on the same <= 64 ids, so each wave then stores its own item with no
+//     further barrier).
+// Three barriers in all.  The x vectors are loaded first and quantised while
+// the histogram atomics drain, and the layout outputs are written after the
+// payload stores.  Workgroup 0 writes the counts, offsets, partition sums and
+// status; the workgroup holding a token's first 512-column step writes that
+// token's row_of_pair and src_pair entries.  Every output equals ep_layout's
+// followed by ep_dispatch's.
 //
-// The per-destination (dedup) variant derives in the same launch, from the
-// same ids, the dedup layout as well: each token's partition set (every
-// valid entry ors its partition bit into its token's LDS word; e / L and
-// entry / K by multiply-shifts that are exact in these ranges), the
-// per-partition token totals and the tokens before this workgroup's first
-// token (counted by the entry that finds its bit still clear), their scan,
-// and the rows and top-k masks of its own tokens' (token, partition) couples.
-// The payload then goes once to each of a token's partitions (the dedup
-// rows) instead of once per top-k entry; both layouts are written out, the
-// per-expert one for the expert side and the combine.
+// The per-destination (dedup) variant derives in the same launch the dedup
+// layout as well: each token's partition set (every valid entry ors its
+// partition bit into its token's LDS word; e / L and entry / K by
+// multiply-shifts that are exact in these ranges), the per-partition token
+// totals and the tokens before this workgroup's first token (counted by the
+// entry that finds its bit still clear), and from these, after the second
+// barrier, the rows and top-k masks of each wave's token's (token,
+// partition) couples.  The payload goes once to each of a token's partitions
+// (the dedup rows) right then, before the expert scan; the per-expert layout
+// is still written out for the expert side and the combine.
 struct DedupOutputs {
     int32_t* tp_row;
     int32_t* part_tokens;
@@ -155,21 +159,22 @@ struct DedupOutputs {
     uint32_t* kmask;
 };
 
+constexpr int kFusedExpertsPerThread = kMaxExperts / kMoveThreads;      // 4
+constexpr int kFusedExpertsPerWave = kFusedExpertsPerThread * kWave;    // 256
+static_assert(kFusedExpertsPerThread * kMoveThreads == kMaxExperts, "experts split evenly");
+static_assert(kMoveWaves == 4, "the wave prefixes below are written out for 4 waves");
+
 struct FusedSmem {
-    int32_t ids[kFusedMaxPairs];
     int32_t cnt[kMaxExperts];
-    int32_t off[kMaxExperts];
     int32_t before[kMaxExperts];
-    int32_t rows[kMoveWaves * kMaxTopK];
+    int32_t offp[kMaxExperts];                 // in-wave exclusive prefix of cnt
+    int32_t off[kMaxExperts];                  // workgroup 0: full offsets, for the partition sums
     int32_t wsum[kMoveWaves];
     uint32_t bad;
     // dedup variant
     int32_t ptot[kMaxTopK];                    // tokens per partition
     int32_t pbef[kMaxTopK];                    // of those, before this workgroup's first token
-    int32_t ptoff[kMaxTopK + 1];               // exclusive scan of ptot
     uint32_t tpres[kFusedMaxPairs];            // partition set (bit p) of every token
-    int32_t drows[kMoveWaves * kMaxTopK];      // own couples' dedup rows (-1: absent)
-    uint32_t dmask[kMoveWaves * kMaxTopK];     // own couples' top-k masks
 };
 
 constexpr int kFusedIdsPerThread = kFusedMaxPairs / kMoveThreads;   // 8
@@ -193,11 +198,13 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
     const int last = (item0 + kMoveWaves - 1 < n_items) ? item0 + kMoveWaves - 1 : n_items - 1;
     const int t_lo = item0 / steps_per_token;
     const int t_hi = last / steps_per_token;
-    const int p_lo = t_lo * K;
     const int nown = t_hi - t_lo + 1;             // own tokens, <= kMoveWaves
-    const int nq = nown * K;                      // <= kMoveWaves * kMaxTopK = 64
+    const int p_lo = t_lo * K;
+    const int nq = nown * K;                      // own entries, <= kMoveWaves * kMaxTopK = 64
+    const int T = n / K;
+    const int L = E / P;
 
-    // every load is independent: x vector and all ids together
+    // every load is independent: x vector, all ids, the own entries' ids
     int t = 0, col0 = H;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (item < n_items) {
@@ -211,21 +218,15 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
         const int p = j * kMoveThreads + tid;
         ids[j] = (p < n) ? idx[p] : -1;
     }
+    const int me = (lane < nq) ? idx[p_lo + lane] : -1;     // own entry q = lane
     for (int e = tid; e < E; e += kMoveThreads) { s.cnt[e] = 0; s.before[e] = 0; }
     if (tid == 0) s.bad = 0u;
     if constexpr (kDedup) {
         if (tid < P) { s.ptot[tid] = 0; s.pbef[tid] = 0; }
-        for (int tt = tid; tt < n / K; tt += kMoveThreads) s.tpres[tt] = 0u;
+        for (int tt = tid; tt < T; tt += kMoveThreads) s.tpres[tt] = 0u;
     }
-#pragma unroll
-    for (int j = 0; j < kFusedIdsPerThread; ++j) {
-        const int p = j * kMoveThreads + tid;
-        if (p < n) s.ids[p] = ids[j];
-    }
-    __syncthreads();
+    lds_barrier();                                         // (1) counters cleared
 
-    const int T = n / K;
-    const int L = E / P;
     bool bad = false;
 #pragma unroll
     for (int j = 0; j < kFusedIdsPerThread; ++j) {
@@ -269,151 +270,130 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
             }
         }
     }
-    // while the atomics drain: quantise this wave's item, and (wave 0) find the
-    // peers of the workgroup's own entries
+    // while the atomics drain: quantise this wave's item and rank the
+    // workgroup's own entries among themselves (every wave, same ids)
     float scale = 0.0f;
     uint2 q = make_uint2(0u, 0u);
     if (item < n_items) q = prepare_item<kPayload>(v, scale);
-    const int me = (w == 0 && lane < nq) ? s.ids[p_lo + lane] : -1;
     const bool mvalid = (me >= 0) && (me < E);
-    int rank = 0;
-    if (w == 0) {
-        uint64_t peers = __ballot(mvalid);
-        for (int b = 0; b < 10; ++b) {            // ids < kMaxExperts = 2^10
-            const bool bit = (me >> b) & 1;
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
-        }
-        rank = lanes_below(peers);
+    uint64_t peers = __ballot(mvalid);
+    for (int b = 0; b < 10; ++b) {                // ids < kMaxExperts = 2^10
+        const bool bit = (me >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
     }
-    __syncthreads();
+    const int rank = lanes_below(peers);
+    lds_barrier();                                         // (2) totals complete
 
-    // exclusive scan of the counts: 4 consecutive experts per thread
-    constexpr int kPer = kMaxExperts / kMoveThreads;
-    static_assert(kPer * kMoveThreads == kMaxExperts, "experts split evenly over threads");
-    int c[kPer], sum = 0;
+    if constexpr (kDedup) {
+        // this wave's token: couple (t, p) in lane p < P
+        const int pc = (lane < P) ? s.ptot[lane] : 0;
+        const int pincl = wave_inclusive_scan(pc);          // partition offsets
+        const int M = read_lane(pincl, P - 1);
+        int drow = -1;
+        uint32_t m = 0u;
+        if (item < n_items && lane < P) {
+            const uint32_t bit = 1u << lane;
+            int before = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int e = tid * kPer + j;
+            for (int j = 0; j < kMoveWaves - 1; ++j)
+                before += (t_lo + j < t && (s.tpres[t_lo + j] & bit)) ? 1 : 0;
+            if (s.tpres[t] & bit) drow = pincl - pc + s.pbef[lane] + before;
+            const uint32_t lo = (uint32_t)(lane * L);
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k)           // token t's ids: own entries (t - t_lo)*K + k
+                if (k < K && (uint32_t)read_lane(me, (t - t_lo) * K + k) - lo < (uint32_t)L)
+                    m |= 1u << k;
+        }
+        if (item < n_items) {
+            store_item<kPayload, false>(v, q, scale, drow, 0, col0, lane, H, P, T * P, recv_x,
+                                        recv_scales);
+            if (t * steps_per_token == item && lane < P) {   // the token's first step writes its couples
+                const int j = t * P + lane;
+                dd.tp_row[j] = drow;
+                dd.kmask[j] = m;
+                if (drow >= 0) dd.tp_src[drow] = j;
+            }
+        }
+        if (blockIdx.x == 0 && w == 0 && lane < P) {
+            dd.part_tokens[lane] = pc;
+            dd.part_token_offset[lane] = pincl - pc;
+            if (lane == P - 1) dd.part_token_offset[P] = M;
+        }
+        for (int r = M + blockIdx.x * kMoveThreads + tid; r < T * P; r += gridDim.x * kMoveThreads)
+            dd.tp_src[r] = -1;
+    }
+
+    // exclusive scan of the expert totals: 4 consecutive experts per thread;
+    // in-wave prefixes go to LDS, the wave totals complete them
+    int c[kFusedExpertsPerThread], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kFusedExpertsPerThread; ++j) {
+        const int e = tid * kFusedExpertsPerThread + j;
         c[j] = (e < E) ? s.cnt[e] : 0;
         sum += c[j];
     }
     const int incl = wave_inclusive_scan(sum);
     if (lane == kWave - 1) s.wsum[w] = incl;
-    __syncthreads();
-    int before_wave = 0, N = 0;
+    int run = incl - sum;
 #pragma unroll
-    for (int u = 0; u < kMoveWaves; ++u) {
-        if (u < w) before_wave += s.wsum[u];
-        N += s.wsum[u];
-    }
-    int run = before_wave + incl - sum;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int e = tid * kPer + j;
-        if (e < E) s.off[e] = run;
+    for (int j = 0; j < kFusedExpertsPerThread; ++j) {
+        const int e = tid * kFusedExpertsPerThread + j;
+        if (e < E) s.offp[e] = run;
         run += c[j];
     }
-    if constexpr (kDedup) {
-        if (w == 1) {                              // partition offsets (totals complete: barrier above)
-            const int pc = (lane < P) ? s.ptot[lane] : 0;
-            const int pincl = wave_inclusive_scan(pc);
-            if (lane < P) s.ptoff[lane] = pincl - pc;
-            if (lane == P - 1) s.ptoff[P] = pincl;
-        }
-    }
-    __syncthreads();
+    lds_barrier();                                         // (3) prefixes complete
 
-    if (w == 0 && lane < nq) s.rows[lane] = mvalid ? s.off[me] + s.before[me] + rank : -1;
-    if constexpr (kDedup) {
-        if (w == 1 && lane < nown * P) {           // own couples: (token t_lo + i, partition p)
-            const int i = lane / P, p = lane - i * P;
-            const int lo = p * L;
-            const int base = (t_lo + i) * K;
-            int before = 0;
-#pragma unroll
-            for (int j = 0; j < kMoveWaves - 1; ++j)
-                before += (j < i) ? (int)((s.tpres[t_lo + j] >> p) & 1u) : 0;
-            const bool present = (s.tpres[t_lo + i] >> p) & 1u;
-            uint32_t m = 0u;
-#pragma unroll
-            for (int k = 0; k < kMaxTopK; ++k) {   // reads issued together (index clamped below K)
-                const int e = s.ids[base + (k < K ? k : K - 1)];
-                if (k < K && (uint32_t)e - (uint32_t)lo < (uint32_t)L) m |= 1u << k;
-            }
-            s.drows[lane] = present ? s.ptoff[p] + s.pbef[p] + before : -1;
-            s.dmask[lane] = m;
-        }
-    }
-    __syncthreads();
+    const int ws0 = s.wsum[0], ws1 = s.wsum[1], ws2 = s.wsum[2], ws3 = s.wsum[3];
+    const int N = ws0 + ws1 + ws2 + ws3;
+    auto wave_base = [&](int ww) { return (ww > 0 ? ws0 : 0) + (ww > 1 ? ws1 : 0) + (ww > 2 ? ws2 : 0); };
+    int myrow = -1;                               // row of own entry q = lane
+    if (mvalid)
+        myrow = s.offp[me] + wave_base(me / kFusedExpertsPerWave) + s.before[me] + rank;
 
-    if (item < n_items) {
-        if constexpr (kDedup) {
-            const int myrow = (lane < P) ? s.drows[(t - t_lo) * P + lane] : -1;
-            store_item<kPayload, false>(v, q, scale, myrow, col0, lane, H, P, T * P, recv_x,
-                                        recv_scales);
-        } else {
-            const int myrow = (lane < K) ? s.rows[(t - t_lo) * K + lane] : -1;
-            store_item<kPayload, false>(v, q, scale, myrow, col0, lane, H, K, n, recv_x,
-                                        recv_scales);
-        }
+    if constexpr (!kDedup) {
+        if (item < n_items)
+            store_item<kPayload, false>(v, q, scale, myrow, (t - t_lo) * K, col0, lane, H, K, n,
+                                        recv_x, recv_scales);
     }
 
     // layout outputs, after the payload stores
-    if (tid < nq) {
-        const int tt = t_lo + tid / K;
-        if (tt * steps_per_token >= item0) {     // this workgroup holds the token's first step
-            const int p = p_lo + tid;
-            const int r = s.rows[tid];
-            row_of_pair[p] = r;
-            if (r >= 0 && r < n) src_pair[r] = p;
+    if (w == 0 && lane < nq) {
+        const int tt = t_lo + lane / K;
+        if (tt * steps_per_token >= item0) {      // this workgroup holds the token's first step
+            const int p = p_lo + lane;
+            row_of_pair[p] = myrow;
+            if (myrow >= 0 && myrow < n) src_pair[myrow] = p;
         }
     }
     if (blockIdx.x == 0) {
+        const int base = wave_base(w);
+        int o = base + incl - sum;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int e = tid * kPer + j;
+        for (int j = 0; j < kFusedExpertsPerThread; ++j) {
+            const int e = tid * kFusedExpertsPerThread + j;
             if (e < E) {
                 expert_count[e] = c[j];
-                expert_offset[e] = s.off[e];
+                expert_offset[e] = o;
+                s.off[e] = o;
             }
-        }
-        for (int p = tid; p < P; p += kMoveThreads) {
-            const int lo = s.off[p * L];
-            const int hi = (p + 1 < P) ? s.off[(p + 1) * L] : N;
-            part_offset[p] = lo;
-            part_count[p] = hi - lo;
+            o += c[j];
         }
         if (tid == 0) {
             expert_offset[E] = N;
             part_offset[P] = N;
             *status = s.bad ? 1u : 0u;
         }
+        lds_barrier();                                     // workgroup 0 only: full offsets
+        for (int p = tid; p < P; p += kMoveThreads) {
+            const int lo = s.off[p * L];
+            const int hi = (p + 1 < P) ? s.off[(p + 1) * L] : N;
+            part_offset[p] = lo;
+            part_count[p] = hi - lo;
+        }
     }
     for (int r = N + blockIdx.x * kMoveThreads + tid; r < n; r += gridDim.x * kMoveThreads)
         src_pair[r] = -1;
-
-    if constexpr (kDedup) {
-        if (tid < nown * P) {
-            const int i = tid / P, p = tid - i * P;
-            const int tt = t_lo + i;
-            if (tt * steps_per_token >= item0) {  // this workgroup holds the token's first step
-                const int j = tt * P + p;
-                const int r = s.drows[tid];
-                dd.tp_row[j] = r;
-                dd.kmask[j] = s.dmask[tid];
-                if (r >= 0) dd.tp_src[r] = j;
-            }
-        }
-        const int M = s.ptoff[P];
-        if (blockIdx.x == 0 && tid < P) {
-            dd.part_tokens[tid] = s.ptot[tid];
-            dd.part_token_offset[tid] = s.ptoff[tid];
-            if (tid == 0) dd.part_token_offset[P] = M;
-        }
-        for (int r = M + blockIdx.x * kMoveThreads + tid; r < T * P; r += gridDim.x * kMoveThreads)
-            dd.tp_src[r] = -1;
-    }
 }
 
 __global__ __launch_bounds__(256) void e4m3fn_encode_kernel(const float* __restrict__ in, int64_t n,

@@ -97,6 +97,17 @@ __device__ __forceinline__ int wave_inclusive_scan(int v)
     return v;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also makes every
+// wave wait for its own outstanding global loads and stores (vmcnt 0) before
+// the barrier; the layout kernels synchronise through LDS alone, so their
+// global stores (rows, payload) keep draining across the barrier instead.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ int wave_uniform(int v)
 {
     return __builtin_amdgcn_readfirstlane(v);

@@ -151,7 +151,7 @@ __device__ __forceinline__ void rank_round(int e, int64_t p, bool real, uint64_t
     const bool valid = real && (e >= 0) && (e < E);
     const int rank = lanes_below(peers);
     if (valid && rank == 0) s.wtab[w][e] = (uint16_t)__popcll(peers);
-    __syncthreads();
+    lds_barrier();
 
     int run = 0;
     if (tid < E) {
@@ -161,7 +161,7 @@ __device__ __forceinline__ void rank_round(int e, int64_t p, bool real, uint64_t
             run += c;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     if (real) {
         int row = -1;
@@ -172,13 +172,13 @@ __device__ __forceinline__ void rank_round(int e, int64_t p, bool real, uint64_t
         row_of_pair[p] = row;
     }
     if (last) return;
-    __syncthreads();
+    lds_barrier();
 
     if (tid < E) {
         s.cursor[tid] += run;
         for (int v = 0; v < kLayoutWaves; ++v) s.wtab[v][tid] = 0;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Exclusive scan of one value per thread over the whole workgroup; *total
@@ -189,15 +189,15 @@ __device__ __forceinline__ int block_exclusive_scan(int v, LayoutSmem& s, int* t
     const int lane = tid % kWave, w = tid / kWave;
     const int x = wave_inclusive_scan(v);
     if (lane == kWave - 1) s.wsum[w] = x;
-    __syncthreads();
+    lds_barrier();
     if (w == 0) {
         const int t = wave_inclusive_scan(lane < kLayoutWaves ? s.wsum[lane] : 0);
         if (lane < kLayoutWaves) s.wsum[lane] = t;   // inclusive prefix of wave sums
     }
-    __syncthreads();
+    lds_barrier();
     const int before = (w > 0) ? s.wsum[w - 1] : 0;
     *total = s.wsum[kLayoutWaves - 1];
-    __syncthreads();
+    lds_barrier();
     return before + x - v;
 }
 
@@ -224,7 +224,7 @@ __device__ __forceinline__ void finish_counts(int count, int E, int P, uint32_t 
             *status = bad ? 1u : 0u;
         }
     }
-    __syncthreads();
+    lds_barrier();
     const int L = E / P;
     if (write_out && part_count && tid < P) {
         const int lo = s.cursor[tid * L];
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
         ids[r] = (p < n) ? src.load(p, E, bad) : -1;
     }
     zero_smem(s, E);
-    __syncthreads();
+    lds_barrier();
 
     // pass 1: histogram
     uint64_t peers[kSmallRounds];
@@ -267,11 +267,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
         if (r < rounds) peers[r] = hist_round(ids[r], E, nbits, s.hist);
     }
     if (bad) s.bad = 1u;
-    __syncthreads();
+    lds_barrier();
 
     finish_counts(tid < E ? s.hist[tid] : 0, E, P, s.bad, s, true, expert_count, expert_offset,
                   part_count, part_offset, status);
-    __syncthreads();
+    lds_barrier();
 
     // pass 2: deterministic slots
 #pragma unroll
@@ -311,11 +311,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_hist_kernel(
     }
     if (tid < E) hist[tid] = 0;
     if (tid == 0) bad = 0u;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int r = 0; r < kChunkRounds; ++r) (void)hist_round(ids[r], E, nbits, hist);
     if (b) bad = 1u;
-    __syncthreads();
+    lds_barrier();
     if (tid < E) ws_hist[(int64_t)chunk * E + tid] = hist[tid];
     if (tid == 0) ws_bad[chunk] = bad;
 }
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(
     __shared__ LayoutSmem s;
     const int tid = threadIdx.x;
     if (tid == 0) s.bad = 0u;
-    __syncthreads();
+    lds_barrier();
     uint32_t b = 0;
     for (int c = tid; c < nchunks; c += kLayoutThreads) b |= ws_bad[c];
     if (b) s.bad = 1u;
@@ -356,10 +356,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     finish_counts(run, E, P, s.bad, s, true, expert_count, expert_offset, part_count, part_offset,
                   status);
-    __syncthreads();
+    lds_barrier();
     if (tid < E) {
         const int off = s.cursor[tid];
         for (int c = 0; c < nchunks; ++c) ws_hist[(int64_t)c * E + tid] += off;
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     }
     (void)unused_bad;
     zero_smem(s, E);
-    __syncthreads();
+    lds_barrier();
 
     if (!bases_ready) {
         // groups of E threads split the chunks; partial sums meet in LDS
@@ -415,18 +415,18 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
         uint32_t b = 0;
         for (int c = tid; c < nchunks; c += kLayoutThreads) b |= ws_bad[c];
         if (b) s.bad = 1u;
-        __syncthreads();
+        lds_barrier();
         const int before = (tid < E) ? s.cursor[tid] : 0;
-        __syncthreads();
+        lds_barrier();
         finish_counts(tid < E ? s.hist[tid] : 0, E, P, s.bad, s, chunk == 0, expert_count,
                       expert_offset, part_count, part_offset, status);
-        __syncthreads();                     // partition sums above read s.cursor
+        lds_barrier();                     // partition sums above read s.cursor
         if (tid < E) s.cursor[tid] += before;
     } else {
         if (tid < E) s.cursor[tid] = ws_hist[(int64_t)chunk * E + tid];
         if (tid == 0) s.total = expert_offset[E];
     }
-    __syncthreads();
+    lds_barrier();
 
     const int rounds = (int)((c1 - c0 + kLayoutThreads - 1) / kLayoutThreads);
 #pragma unroll
