@@ -61,7 +61,8 @@ class Path:
         self.w = up(self.d["w"])
         self.x = up(self.d["x"].view(np.int16), torch.bfloat16)
         self.y = up(self.d["y"].view(np.int16), torch.bfloat16)
-        self.buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+        self.buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload,
+                                geometry=GEOMETRY)
         self.stream = torch.cuda.Stream()
         self.N = self.d["N"]
 
@@ -254,6 +255,7 @@ def cpu_baseline(wl, d, N, min_seconds):
 
 
 STEPS_PER_GRAPH = 50
+GEOMETRY = "tuned"      # launch geometry of dispatch/combine: the saved tuner rules for the shape
 
 
 def time_steps(p, steps, warmup, mode, phase="step"):
@@ -323,6 +325,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="step = ep_layout + ep_dispatch + ep_combine (default: ep_layout_dispatch + ep_combine)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--default-geometry", action="store_true",
+                    help="launch dispatch/combine with the library's default geometry, not the tuned rules")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-targets", action="store_true")
     ap.add_argument("--no-dedup", action="store_true")
@@ -343,6 +347,9 @@ def main():
     import torch
     from workloads import WORKLOADS
     wl = WORKLOADS[args.workload]
+    global GEOMETRY
+    if args.default_geometry:
+        GEOMETRY = None
 
     if args.only or args.calib_copy_mib:
         if args.calib_copy_mib:
@@ -405,7 +412,8 @@ def main():
                    "HIP graphs of %d whole steps, replayed" % STEPS_PER_GRAPH,
                    "step": "ep_layout + ep_dispatch + ep_combine" if args.unfused
                    else "ep_layout_dispatch + ep_combine",
-                   "parallelism": "single GPU (partitions stand in for EP ranks)"},
+                   "parallelism": "single GPU (partitions stand in for EP ranks)",
+                   "geometry": {k: list(v) for k, v in p.buf.geometry.items()} or "library default"},
         "bytes_per_step": b["step"],
         "phases_us": {k: round(v, 3) for k, v in phases.items()},
         "eager_us_per_step": round(eager_us, 3),

@@ -46,6 +46,8 @@ _SIGS = {
     "ep_graph_launch": ([_P, _P], _I),
     "ep_graph_destroy": ([_P], _I),
     "ep_e4m3fn_encode": ([_P, _I64, _P, _P], _I),
+    "ep_dispatch_geom": ([_P, _I, _I, _I, _P, _I, _P, _P, _I, _I, _P], _I),
+    "ep_combine_geom": ([_P, _P, _P, _I, _I, _I, _P, _I, _I, _P], _I),
     "ep_dedup_layout_workspace_bytes": ([_I, _I, _I, _I], _SZ),
     "ep_dedup_layout": ([_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "ep_combine_partial": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
@@ -119,14 +121,21 @@ def ep_layout(topk_idx, E, P, expert_count, expert_offset, part_count, part_offs
         _stream(stream)))
 
 
-def ep_dispatch(x, K, row_of_pair, payload, recv_x, recv_scales=None, stream=None):
-    """x bf16 [T, H] -> recv_x (uint8 fp8 bytes or bf16) [T*K, H], recv_scales fp32 [T*K, H/128]."""
+def ep_dispatch(x, K, row_of_pair, payload, recv_x, recv_scales=None, stream=None, geometry=None):
+    """x bf16 [T, H] -> recv_x (uint8 fp8 bytes or bf16) [T*K, H], recv_scales fp32 [T*K, H/128].
+    geometry: None (library default) or (waves_per_block, max_blocks)."""
     _dt(x, torch.bfloat16, torch.int16, torch.uint16)
     _dt(row_of_pair, torch.int32)
     payload = PAYLOADS.get(payload, payload)
     T, H = x.shape
-    _check("ep_dispatch", _lib.ep_dispatch(_ptr(x), T, H, K, _ptr(row_of_pair), payload,
-                                           _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
+    if geometry is None:
+        _check("ep_dispatch", _lib.ep_dispatch(_ptr(x), T, H, K, _ptr(row_of_pair), payload,
+                                               _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
+    else:
+        wv, mb = geometry
+        _check("ep_dispatch_geom", _lib.ep_dispatch_geom(
+            _ptr(x), T, H, K, _ptr(row_of_pair), payload, _ptr(recv_x), _ptr(recv_scales), wv, mb,
+            _stream(stream)))
 
 
 def ep_layout_dispatch(topk_idx, x, E, P, payload, expert_count, expert_offset, part_count,
@@ -145,16 +154,23 @@ def ep_layout_dispatch(topk_idx, x, E, P, payload, expert_count, expert_offset, 
         _ptr(ws), ws_bytes, _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
 
 
-def ep_combine(expert_out, row_of_pair, topk_w, out, stream=None):
-    """expert_out bf16 [T*K, H] (receive-row layout), topk_w fp32 [T, K] -> out bf16 [T, H]."""
+def ep_combine(expert_out, row_of_pair, topk_w, out, stream=None, geometry=None):
+    """expert_out bf16 [T*K, H] (receive-row layout), topk_w fp32 [T, K] -> out bf16 [T, H].
+    geometry: None (library default) or (waves_per_block, max_blocks)."""
     _dt(expert_out, torch.bfloat16, torch.int16, torch.uint16)
     _dt(out, torch.bfloat16, torch.int16, torch.uint16)
     _dt(topk_w, torch.float32)
     _dt(row_of_pair, torch.int32)
     T, K = topk_w.shape
     H = out.shape[1]
-    _check("ep_combine", _lib.ep_combine(_ptr(expert_out), _ptr(row_of_pair), _ptr(topk_w), T, H,
-                                         K, _ptr(out), _stream(stream)))
+    if geometry is None:
+        _check("ep_combine", _lib.ep_combine(_ptr(expert_out), _ptr(row_of_pair), _ptr(topk_w), T,
+                                             H, K, _ptr(out), _stream(stream)))
+    else:
+        wv, mb = geometry
+        _check("ep_combine_geom", _lib.ep_combine_geom(
+            _ptr(expert_out), _ptr(row_of_pair), _ptr(topk_w), T, H, K, _ptr(out), wv, mb,
+            _stream(stream)))
 
 
 def ep_e4m3fn_encode(values_f32, out_u8, stream=None):
@@ -265,9 +281,16 @@ class EpBuffers:
     """Persistent device buffers for one shape (allocated once, reused by every
     call, so the calls can be captured into a graph)."""
 
-    def __init__(self, T, H, K, E, P, payload="fp8", device="cuda"):
+    def __init__(self, T, H, K, E, P, payload="fp8", device="cuda", geometry=None):
+        """geometry: None (library defaults), "tuned" (the saved rules for this
+        shape, where there are any) or {"dispatch": (waves, max_blocks),
+        "combine": (waves, max_blocks)}."""
         self.T, self.H, self.K, self.E, self.P = T, H, K, E, P
         self.payload = payload
+        if geometry == "tuned":
+            from . import tuning
+            geometry = {ph: tuning.lookup(ph, T, H, K, payload) for ph in ("dispatch", "combine")}
+        self.geometry = {k: v for k, v in (geometry or {}).items() if v is not None}
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         self.expert_count = torch.empty(E, **i32)
@@ -297,10 +320,12 @@ class EpBuffers:
                            self.src_pair, self.status, self.ws, self.recv_x, self.recv_scales, stream)
 
     def dispatch(self, x, stream=None):
-        ep_dispatch(x, self.K, self.row_of_pair, self.payload, self.recv_x, self.recv_scales, stream)
+        ep_dispatch(x, self.K, self.row_of_pair, self.payload, self.recv_x, self.recv_scales, stream,
+                    self.geometry.get("dispatch"))
 
     def combine(self, expert_out, topk_w, stream=None):
-        ep_combine(expert_out, self.row_of_pair, topk_w, self.out, stream)
+        ep_combine(expert_out, self.row_of_pair, topk_w, self.out, stream,
+                   self.geometry.get("combine"))
         return self.out
 
 
@@ -386,9 +411,16 @@ class BoundStep:
                     _ptr(buf.part_offset), _ptr(buf.row_of_pair), _ptr(buf.src_pair),
                     _ptr(buf.status), _ptr(buf.ws), ws_bytes, _ptr(buf.recv_x),
                     _ptr(buf.recv_scales), s)
-        self._cb = (_ptr(expert_out), _ptr(buf.row_of_pair), _ptr(topk_w), T, buf.H, K,
-                    _ptr(buf.out), s)
-        self._f_ld, self._f_cb = _lib.ep_layout_dispatch, _lib.ep_combine
+        g = buf.geometry.get("combine")
+        if g is None:
+            self._cb = (_ptr(expert_out), _ptr(buf.row_of_pair), _ptr(topk_w), T, buf.H, K,
+                        _ptr(buf.out), s)
+            self._f_cb = _lib.ep_combine
+        else:
+            self._cb = (_ptr(expert_out), _ptr(buf.row_of_pair), _ptr(topk_w), T, buf.H, K,
+                        _ptr(buf.out), int(g[0]), int(g[1]), s)
+            self._f_cb = _lib.ep_combine_geom
+        self._f_ld = _lib.ep_layout_dispatch
 
     def layout_dispatch(self):
         rc = self._f_ld(*self._ld)

@@ -110,6 +110,47 @@ int ep_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H,
     return from_hip(ep::launch_dispatch(x, T, H, K, row_of_pair, payload, recv_x, recv_scales, s));
 }
 
+namespace {
+
+bool geometry_ok(int waves_per_block, int max_blocks)
+{
+    return (waves_per_block == 1 || waves_per_block == 2 || waves_per_block == 4 ||
+            waves_per_block == 8) && max_blocks >= 0;
+}
+
+}  // namespace
+
+int ep_dispatch_geom(const uint16_t* x, int T, int H, int K, const int32_t* row_of_pair,
+                     int payload, void* recv_x, float* recv_scales, int waves_per_block,
+                     int max_blocks, void* stream)
+{
+    if (!geometry_ok(waves_per_block, max_blocks)) return EP_EINVAL;
+    if (payload != EP_PAYLOAD_FP8_E4M3FN && payload != EP_PAYLOAD_BF16) return EP_ENOTSUP;
+    if (!routing_ok(T, K) || H <= 0) return EP_EINVAL;
+    if (payload == EP_PAYLOAD_FP8_E4M3FN && H % ep::kScaleBlock != 0) return EP_EINVAL;
+    if (payload == EP_PAYLOAD_BF16 && H % ep::kColsPerLane != 0) return EP_EINVAL;
+    if (T == 0) return EP_OK;
+    if (!ptr_ok(x, 16) || !ptr_ok(row_of_pair, 4) || !ptr_ok(recv_x, 16)) return EP_EINVAL;
+    if (payload == EP_PAYLOAD_FP8_E4M3FN && !ptr_ok(recv_scales, 4)) return EP_EINVAL;
+    return from_hip(ep::launch_dispatch(x, T, H, K, row_of_pair, payload, recv_x, recv_scales,
+                                        (hipStream_t)stream,
+                                        ep::MoveGeometry{waves_per_block, max_blocks}));
+}
+
+int ep_combine_geom(const uint16_t* expert_out, const int32_t* row_of_pair, const float* topk_w,
+                    int T, int H, int K, uint16_t* out, int waves_per_block, int max_blocks,
+                    void* stream)
+{
+    if (!geometry_ok(waves_per_block, max_blocks)) return EP_EINVAL;
+    if (!routing_ok(T, K) || H <= 0 || H % ep::kColsPerLane != 0) return EP_EINVAL;
+    if (T == 0) return EP_OK;
+    if (!ptr_ok(expert_out, 16) || !ptr_ok(row_of_pair, 4) || !ptr_ok(topk_w, 4) || !ptr_ok(out, 16))
+        return EP_EINVAL;
+    return from_hip(ep::launch_combine(expert_out, row_of_pair, topk_w, T, H, K, out,
+                                       (hipStream_t)stream,
+                                       ep::MoveGeometry{waves_per_block, max_blocks}));
+}
+
 int ep_combine(const uint16_t* expert_out, const int32_t* row_of_pair, const float* topk_w, int T,
                int H, int K, uint16_t* out, void* stream)
 {

@@ -78,15 +78,16 @@ __device__ __forceinline__ uint4 reduce_rows(const uint4 (&v)[kMaxK], int myrow,
 // tp_row[t*P+p] of `out`: every expert row is read once, as in the plain
 // combine, and no wave is spent on (token, partition) couples without a copy.
 template <int kMaxK, bool kStream, int kMode>
-__global__ __launch_bounds__(kMoveThreads) void combine_kernel(
+__global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
     const uint16_t* __restrict__ y, const int32_t* __restrict__ row_of_pair,
     const float* __restrict__ topk_w, int H, int K, uint16_t* __restrict__ out,
     int steps_per_token, int n_items, int n_rows,
     const int32_t* __restrict__ tp_row, const uint32_t* __restrict__ kmask, int P, int out_rows)
 {
     const int lane = threadIdx.x % kWave;
-    const int stride = gridDim.x * kMoveWaves;
-    for (int item = blockIdx.x * kMoveWaves + wave_uniform(threadIdx.x / kWave); item < n_items;
+    const int waves = blockDim.x / kWave;
+    const int stride = gridDim.x * waves;
+    for (int item = blockIdx.x * waves + wave_uniform(threadIdx.x / kWave); item < n_items;
          item += stride) {                   // n_items + stride < 2^31 (checked by the launcher)
         const int t = item / steps_per_token;
         const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
@@ -157,18 +158,21 @@ template <int kMode>
 hipError_t launch_combine_mode(const uint16_t* y, const int32_t* row_of_pair,
                                const float* topk_w, int n_units, int H, int K, int n_rows,
                                const int32_t* tp_row, const uint32_t* kmask, int P, int out_rows,
-                               int64_t gathered_rows, uint16_t* out, hipStream_t stream)
+                               int64_t gathered_rows, uint16_t* out, hipStream_t stream,
+                               MoveGeometry g)
 {
     const int steps = (H + kStepCols - 1) / kStepCols;
     const int64_t items = (int64_t)n_units * steps;
     if (items == 0) return hipSuccess;
-    if (items + kMaxGridBlocks * kMoveWaves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
+    if (g.waves < 1 || g.waves > kMaxMoveWaves || g.max_blocks < 0) return hipErrorInvalidValue;
+    if (items + kMaxGridBlocks * kMaxMoveWaves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    int64_t blocks = (items + g.waves - 1) / g.waves;
+    if (g.max_blocks > 0 && blocks > g.max_blocks) blocks = g.max_blocks;
     if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
     const bool stream_policy = combine_streams(gathered_rows, H);
     auto k = K <= 8 ? (stream_policy ? combine_kernel<8, true, kMode> : combine_kernel<8, false, kMode>)
                     : (stream_policy ? combine_kernel<16, true, kMode> : combine_kernel<16, false, kMode>);
-    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kMoveThreads), 0, stream, y, row_of_pair,
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(g.waves * kWave), 0, stream, y, row_of_pair,
                        topk_w, H, K, out, steps, (int)items, n_rows, tp_row, kmask, P, out_rows);
     return hipGetLastError();
 }
@@ -176,10 +180,10 @@ hipError_t launch_combine_mode(const uint16_t* y, const int32_t* row_of_pair,
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of_pair, const float* topk_w,
-                          int T, int H, int K, uint16_t* out, hipStream_t stream)
+                          int T, int H, int K, uint16_t* out, hipStream_t stream, MoveGeometry g)
 {
     return launch_combine_mode<kPlain>(y, row_of_pair, topk_w, T, H, K, T * K, nullptr, nullptr,
-                                       1, T, (int64_t)T * K, out, stream);
+                                       1, T, (int64_t)T * K, out, stream, g);
 }
 
 hipError_t launch_combine_partial(const uint16_t* y, const int32_t* row_of_pair,
@@ -188,14 +192,14 @@ hipError_t launch_combine_partial(const uint16_t* y, const int32_t* row_of_pair,
                                   uint16_t* partial, hipStream_t stream)
 {
     return launch_combine_mode<kPartial>(y, row_of_pair, topk_w, T, H, K, T * K, tp_row, kmask, P,
-                                         T * P, (int64_t)T * K, partial, stream);
+                                         T * P, (int64_t)T * K, partial, stream, kDefaultGeometry);
 }
 
 hipError_t launch_combine_reduce(const uint16_t* partial, const int32_t* tp_row, int T, int H,
                                  int P, uint16_t* out, hipStream_t stream)
 {
     return launch_combine_mode<kReduce>(partial, tp_row, nullptr, T, H, P, T * P, nullptr, nullptr,
-                                        1, T, (int64_t)T * P, out, stream);
+                                        1, T, (int64_t)T * P, out, stream, kDefaultGeometry);
 }
 
 }  // namespace ep

@@ -75,14 +75,15 @@ __device__ __forceinline__ uint2 prepare_item(uint4 v, float& scale)
 }
 
 template <int kPayload, bool kStream>
-__global__ __launch_bounds__(kMoveThreads) void dispatch_kernel(
+__global__ __launch_bounds__(kMaxMoveWaves * kWave) void dispatch_kernel(
     const uint16_t* __restrict__ x, int H, int K, const int32_t* __restrict__ row_of_pair,
     uint8_t* __restrict__ recv_x, float* __restrict__ recv_scales,
     int steps_per_token, int n_items, int n_rows)
 {
     const int lane = threadIdx.x % kWave;
-    const int stride = gridDim.x * kMoveWaves;
-    int item = blockIdx.x * kMoveWaves + wave_uniform(threadIdx.x / kWave);
+    const int waves = blockDim.x / kWave;
+    const int stride = gridDim.x * waves;
+    int item = blockIdx.x * waves + wave_uniform(threadIdx.x / kWave);
     if (item >= n_items) return;
 
     // load stage of one item: row ids (lanes < K) and this lane's 16 bytes of x
@@ -421,18 +422,21 @@ bool dispatch_streams(int T, int H, int K, int payload)
 }  // namespace
 
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, const int32_t* row_of_pair,
-                           int payload, void* recv_x, float* recv_scales, hipStream_t stream)
+                           int payload, void* recv_x, float* recv_scales, hipStream_t stream,
+                           MoveGeometry g)
 {
     const int steps = (H + kStepCols - 1) / kStepCols;
     const int64_t items = (int64_t)T * steps;
     if (items == 0) return hipSuccess;
-    if (items + kMaxGridBlocks * kMoveWaves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
+    if (g.waves < 1 || g.waves > kMaxMoveWaves || g.max_blocks < 0) return hipErrorInvalidValue;
+    if (items + kMaxGridBlocks * kMaxMoveWaves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    int64_t blocks = (items + g.waves - 1) / g.waves;
+    if (g.max_blocks > 0 && blocks > g.max_blocks) blocks = g.max_blocks;
     if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
     const bool st = dispatch_streams(T, H, K, payload);
     auto k = payload == 0 ? (st ? dispatch_kernel<0, true> : dispatch_kernel<0, false>)
                           : (st ? dispatch_kernel<1, true> : dispatch_kernel<1, false>);
-    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kMoveThreads), 0, stream, x, H, K,
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(g.waves * kWave), 0, stream, x, H, K,
                        row_of_pair, (uint8_t*)recv_x, payload == 0 ? recv_scales : nullptr, steps,
                        (int)items, T * K);
     return hipGetLastError();

@@ -40,6 +40,17 @@ constexpr int kStepCols = kWave * kColsPerLane;   // 512 columns per wave step
 constexpr int kScaleBlock = 128;           // columns per fp8 scale
 constexpr int kLanesPerScaleBlock = kScaleBlock / kColsPerLane;   // 16 = one DPP row
 static_assert(kLanesPerScaleBlock == 16, "a scale block must be one 16-lane DPP row");
+
+// Launch geometry of the dispatch and combine kernels: waves per workgroup
+// (1, 2, 4 or 8; the kernels read it from blockDim) and a cap on the number
+// of workgroups (0: one wave per work item; otherwise the waves stride over
+// the items).  The default is 4 waves, uncapped.
+constexpr int kMaxMoveWaves = 8;
+struct MoveGeometry {
+    int waves;
+    int max_blocks;
+};
+constexpr MoveGeometry kDefaultGeometry{kMoveWaves, 0};
 static_assert(kMoveWaves * kMaxTopK <= kWave, "a workgroup's own entries fit in one wave");
 static_assert(kMaxExperts <= 1024, "fused slot ranks compare 10 id bits");
 

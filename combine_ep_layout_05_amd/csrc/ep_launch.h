@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ep_device.h"
+
 namespace ep {
 
 size_t layout_workspace_bytes(int T, int K, int E);
@@ -19,7 +21,8 @@ hipError_t launch_layout(const int32_t* topk_idx, int T, int K, int E, int P,
 
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K,
                            const int32_t* row_of_pair, int payload,
-                           void* recv_x, float* recv_scales, hipStream_t stream);
+                           void* recv_x, float* recv_scales, hipStream_t stream,
+                           MoveGeometry g = kDefaultGeometry);
 
 bool fused_layout_dispatch_fits(int T, int K);
 
@@ -32,7 +35,8 @@ hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, in
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of_pair,
                           const float* topk_w, int T, int H, int K,
-                          uint16_t* out, hipStream_t stream);
+                          uint16_t* out, hipStream_t stream,
+                          MoveGeometry g = kDefaultGeometry);
 
 size_t dedup_layout_workspace_bytes(int T, int P);
 

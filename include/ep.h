@@ -267,6 +267,29 @@ int ep_combine_reduce(const uint16_t* partial, const int32_t* tp_row, int T, int
                       uint16_t* out, void* stream);
 
 /*
+ * Launch geometry (for tuning).  ep_dispatch and ep_combine launch 4 waves
+ * (256 threads) per workgroup and one wave per work item, a work item being
+ * one token's 512-column slice.  These variants take the geometry
+ * explicitly: waves_per_block in {1, 2, 4, 8}, and max_blocks = 0 (one wave
+ * per item) or a cap on the number of workgroups, whose waves then stride
+ * over the items.  The outputs do not depend on the geometry (bit for bit);
+ * only the time does.  The sources found that the best geometry moves with
+ * token count and phase, and pick it by measurement (MoRI PR #614, tuner
+ * paragraphs).
+ * Errors: those of ep_dispatch / ep_combine, and EP_EINVAL for another
+ * waves_per_block or a negative max_blocks.
+ */
+#define EP_MAX_WAVES_PER_BLOCK 8
+
+int ep_dispatch_geom(const uint16_t* x, int T, int H, int K, const int32_t* row_of_pair,
+                     int payload, void* recv_x, float* recv_scales, int waves_per_block,
+                     int max_blocks, void* stream);
+
+int ep_combine_geom(const uint16_t* expert_out, const int32_t* row_of_pair, const float* topk_w,
+                    int T, int H, int K, uint16_t* out, int waves_per_block, int max_blocks,
+                    void* stream);
+
+/*
  * HIP graph capture for the small-token regime, where host enqueue paces the
  * GPU (MoRI PR #614, view-cache paragraph: at 4 tokens most of a round's
  * wall time was host work, and stable buffers are what make the op

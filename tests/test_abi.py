@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
               "ep_graph_launch", "ep_graph_destroy", "ep_e4m3fn_encode", "ep_layout_dispatch",
               "ep_dedup_layout", "ep_dedup_layout_workspace_bytes", "ep_combine_partial",
               "ep_combine_reduce", "ep_dedup_layout_dispatch",
-              "ep_dedup_layout_dispatch_workspace_bytes"):
+              "ep_dedup_layout_dispatch_workspace_bytes", "ep_dispatch_geom", "ep_combine_geom"):
         assert n in names, n
 
 
@@ -128,3 +128,17 @@ def test_dedup_layout_dispatch_host_side_validation(lib):
     assert need >= L.ep_layout_workspace_bytes(4096, 8, 256) > 0
     assert L.ep_dedup_layout_dispatch(fake, fake, 4096, 1024, 8, 256, 8, 0, *outs, fake, need - 16,
                                       fake, fake, None) == -1
+
+
+def test_geometry_host_side_validation(lib):
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L = lib
+    L.ep_dispatch_geom.argtypes = [P, I, I, I, P, I, P, P, I, I, P]
+    L.ep_combine_geom.argtypes = [P, P, P, I, I, I, P, I, I, P]
+    fake = P(0x10000)
+    for wv, mb in [(3, 0), (0, 0), (16, 0), (4, -1)]:
+        assert L.ep_dispatch_geom(fake, 4, 1024, 8, fake, 0, fake, fake, wv, mb, None) == -1
+        assert L.ep_combine_geom(fake, fake, fake, 4, 1024, 8, fake, wv, mb, None) == -1
+    # valid geometry, empty batch: accepted, nothing launched
+    assert L.ep_dispatch_geom(None, 0, 1024, 8, None, 0, None, None, 8, 0, None) == 0
+    assert L.ep_combine_geom(None, None, None, 0, 1024, 8, None, 1, 256, None) == 0
