@@ -59,9 +59,10 @@ KERNEL_SOURCES = {
 
 def source_digest(kernel=None) -> str:
     """sha256 of the HIP sources a kernel is built from (all sources when
-    kernel is None) and the code-generation flags, with comments and
-    whitespace removed: it changes when the compiled code can change, not when
-    a comment does.  Recorded next to rocprofv3 counter readings so that a
+    kernel is None), the code-generation flags and, for dispatch and combine,
+    the tuned launch-geometry rules, with comments and whitespace removed: it
+    changes when the compiled code or its launch can change, not when a
+    comment does.  Recorded next to rocprofv3 counter readings so that a
     reading is only reused for the kernel code it was taken from."""
     import hashlib
     import re
@@ -71,7 +72,12 @@ def source_digest(kernel=None) -> str:
         files = sorted(sources() + glob.glob(os.path.join(CSRC, "*.h")))
     else:
         files = [os.path.join(CSRC, n) for n in KERNEL_SOURCES[kernel]]
+    if kernel in ("dispatch", "combine"):
+        # the launch geometry the bench takes from the tuned rules
+        files = files + [os.path.join(HERE, "tuned_geometry.json")]
     for p in files:
+        if not os.path.exists(p):
+            continue
         text = open(p).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
