@@ -64,6 +64,67 @@ def test_graph_replay_matches_eager(name, fused):
     g.destroy()
 
 
+@pytest.mark.parametrize("name", ["ll_128x7168", "bw_4096x7168_zipf"])
+def test_dedup_graph_replay_matches_eager(name):
+    """The per-destination step (ep_dedup_layout_dispatch, ep_combine_partial,
+    ep_combine_reduce), captured once, replays bit-exactly to the eager result
+    with unrelated eager work in between; the small batch runs the one-launch
+    path, the 1024-token batch the three-kernel path."""
+    import combine_ep_layout_05_amd as ep
+    wl = WORKLOADS[name]
+    if wl.T > 1024:
+        wl = wl.with_(T=1024)
+    print("dedup graph case", wl.name, wl.T, flush=True)
+    d = generate(wl)
+    idx, w = to_dev(d["idx"]), to_dev(d["w"])
+    x = to_dev(d["x"].view(np.int16), torch.bfloat16)
+    y = to_dev(d["y"].view(np.int16), torch.bfloat16)
+
+    def run(buf, db, s=None):
+        db.layout_dispatch(idx, x, buf, s)
+        db.combine_partial(y, buf.row_of_pair, w, s)
+        db.combine_reduce(s)
+
+    def grab(buf, db):
+        torch.cuda.synchronize()
+        r = {k: getattr(db, k).cpu().numpy().copy() for k in
+             ("tp_row", "part_tokens", "part_token_offset", "tp_src", "kmask", "status")}
+        M = int(r["part_token_offset"][wl.P])
+        r["recv_x"] = db.recv_x.view(torch.uint8).cpu().numpy()[:M].copy()
+        r["partial"] = db.partial.view(torch.int16).cpu().numpy()[:M].copy()
+        r["out"] = db.out.view(torch.int16).cpu().numpy().copy()
+        r["row_of_pair"] = buf.row_of_pair.cpu().numpy().copy()
+        return r
+
+    b0 = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    d0 = ep.EpDedupBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    run(b0, d0)
+    ref = grab(b0, d0)
+
+    b1 = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    d1 = ep.EpDedupBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ep.ep_graph_begin(s)
+        run(b1, d1, s)
+        g = ep.ep_graph_end(s)
+    for rep in range(4):
+        d1.recv_x.view(torch.uint8).fill_(0)
+        d1.partial.zero_()
+        d1.out.zero_()
+        d1.tp_row.fill_(-5)
+        b1.row_of_pair.fill_(-5)
+        junk = torch.randn(1 << 20, device="cuda").sum()     # unrelated eager work
+        torch.cuda.synchronize()
+        g.launch(s)
+        s.synchronize()
+        got = grab(b1, d1)
+        for k in ref:
+            assert np.array_equal(got[k], ref[k]), "replay %d: %s" % (rep, k)
+        del junk
+    g.destroy()
+
+
 def test_device_encoder_against_oracle_ranges():
     """All fp32 bit patterns with magnitude in [2^-12, 512) (both signs), plus
     the special values: the device encoder equals the oracle's."""
