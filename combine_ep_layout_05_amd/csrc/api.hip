@@ -98,7 +98,7 @@ int ep_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H,
     const size_t need = ep::layout_workspace_bytes(T, K, E);
     if (need > 0 && (ws_bytes < need || !ptr_ok(ws, 16))) return EP_EINVAL;
     hipStream_t s = (hipStream_t)stream;
-    if (T > 0 && ep::fused_layout_dispatch_fits(T, K))
+    if (T > 0 && ep::fused_layout_dispatch_fits(T, H, K))
         return from_hip(ep::launch_layout_dispatch(topk_idx, x, T, H, K, E, P, payload, expert_count,
                                                    expert_offset, part_count, part_offset,
                                                    row_of_pair, src_pair, status, recv_x,
@@ -221,7 +221,7 @@ int ep_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, 
     const size_t need = ep_dedup_layout_dispatch_workspace_bytes(T, K, E, P);
     if (need > 0 && (ws_bytes < need || !ptr_ok(ws, 16))) return EP_EINVAL;
     hipStream_t s = (hipStream_t)stream;
-    if (T > 0 && ep::fused_layout_dispatch_fits(T, K))
+    if (T > 0 && ep::fused_layout_dispatch_fits(T, H, K))
         return from_hip(ep::launch_dedup_layout_dispatch(
             topk_idx, x, T, H, K, E, P, payload, expert_count, expert_offset, part_count,
             part_offset, row_of_pair, src_pair, tp_row, part_tokens, part_token_offset, tp_src,

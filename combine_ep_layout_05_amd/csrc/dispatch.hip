@@ -160,17 +160,14 @@ struct DedupOutputs {
     uint32_t* kmask;
 };
 
-constexpr int kFusedExpertsPerThread = kMaxExperts / kMoveThreads;      // 4
-constexpr int kFusedExpertsPerWave = kFusedExpertsPerThread * kWave;    // 256
-static_assert(kFusedExpertsPerThread * kMoveThreads == kMaxExperts, "experts split evenly");
-static_assert(kMoveWaves == 4, "the wave prefixes below are written out for 4 waves");
+constexpr int kMaxFusedWaves = 8;          // workgroups of 4 or 8 waves
 
 struct FusedSmem {
     int32_t cnt[kMaxExperts];
     int32_t before[kMaxExperts];
     int32_t offp[kMaxExperts];                 // in-wave exclusive prefix of cnt
     int32_t off[kMaxExperts];                  // workgroup 0: full offsets, for the partition sums
-    int32_t wsum[kMoveWaves];
+    int32_t wsum[kMaxFusedWaves];
     uint32_t bad;
     // dedup variant
     int32_t ptot[kMaxTopK];                    // tokens per partition
@@ -178,11 +175,10 @@ struct FusedSmem {
     uint32_t tpres[kFusedMaxPairs];            // partition set (bit p) of every token
 };
 
-constexpr int kFusedIdsPerThread = kFusedMaxPairs / kMoveThreads;   // 8
-static_assert(kFusedIdsPerThread * kMoveThreads == kFusedMaxPairs, "ids split evenly");
-
-template <int kPayload, bool kDedup>
-__global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
+// kW waves per workgroup, each wave one work item; the workgroup's own
+// tokens' entries (at most 64, checked by the launcher) are ranked in one wave.
+template <int kPayload, bool kDedup, int kW>
+__global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, int n, int H, int K, int E,
     int P, int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
@@ -190,22 +186,38 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
     uint32_t* __restrict__ status, uint8_t* __restrict__ recv_x, float* __restrict__ recv_scales,
     int steps_per_token, int n_items, DedupOutputs dd)
 {
+    constexpr int kThreads = kW * kWave;
+    constexpr int kIds = kFusedMaxPairs / kThreads;        // ids per thread
+    constexpr int kPer = kMaxExperts / kThreads;           // experts per thread
+    constexpr int kPerWave = kPer * kWave;
+    static_assert(kIds * kThreads == kFusedMaxPairs && kPer * kThreads == kMaxExperts,
+                  "ids and experts split evenly over the threads");
+    static_assert(kW <= kMaxFusedWaves, "wave totals fit");
     __shared__ FusedSmem s;
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int w = wave_uniform(tid / kWave);
-    const int item0 = blockIdx.x * kMoveWaves;
+    const int item0 = blockIdx.x * kW;
     const int item = item0 + w;
-    const int last = (item0 + kMoveWaves - 1 < n_items) ? item0 + kMoveWaves - 1 : n_items - 1;
+    const int last = (item0 + kW - 1 < n_items) ? item0 + kW - 1 : n_items - 1;
     const int t_lo = item0 / steps_per_token;
     const int t_hi = last / steps_per_token;
-    const int nown = t_hi - t_lo + 1;             // own tokens, <= kMoveWaves
+    const int nown = t_hi - t_lo + 1;             // own tokens, <= kW
     const int p_lo = t_lo * K;
-    const int nq = nown * K;                      // own entries, <= kMoveWaves * kMaxTopK = 64
+    const int nq = nown * K;                      // own entries, <= kW * kMaxTopK = 64
     const int T = n / K;
     const int L = E / P;
 
-    // every load is independent: x vector, all ids, the own entries' ids
+    // every load is independent: all ids (issued back to back, addresses
+    // clamped into the array instead of branching), the own entries' ids, and
+    // the x vector
+    int ids[kIds];
+#pragma unroll
+    for (int j = 0; j < kIds; ++j) {
+        const int p = j * kThreads + tid;
+        ids[j] = idx[p < n ? p : n - 1];
+    }
+    int me = idx[p_lo + (lane < nq ? lane : 0)];           // own entry q = lane
     int t = 0, col0 = H;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (item < n_items) {
@@ -213,25 +225,22 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
         col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
         if (col0 < H) v = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + col0);
     }
-    int ids[kFusedIdsPerThread];
 #pragma unroll
-    for (int j = 0; j < kFusedIdsPerThread; ++j) {
-        const int p = j * kMoveThreads + tid;
-        ids[j] = (p < n) ? idx[p] : -1;
-    }
-    const int me = (lane < nq) ? idx[p_lo + lane] : -1;     // own entry q = lane
-    for (int e = tid; e < E; e += kMoveThreads) { s.cnt[e] = 0; s.before[e] = 0; }
+    for (int j = 0; j < kIds; ++j)
+        if (j * kThreads + tid >= n) ids[j] = -1;
+    if (lane >= nq) me = -1;
+    for (int e = tid; e < E; e += kThreads) { s.cnt[e] = 0; s.before[e] = 0; }
     if (tid == 0) s.bad = 0u;
     if constexpr (kDedup) {
         if (tid < P) { s.ptot[tid] = 0; s.pbef[tid] = 0; }
-        for (int tt = tid; tt < T; tt += kMoveThreads) s.tpres[tt] = 0u;
+        for (int tt = tid; tt < T; tt += kThreads) s.tpres[tt] = 0u;
     }
     lds_barrier();                                         // (1) counters cleared
 
     bool bad = false;
 #pragma unroll
-    for (int j = 0; j < kFusedIdsPerThread; ++j) {
-        const int p = j * kMoveThreads + tid;
+    for (int j = 0; j < kIds; ++j) {
+        const int p = j * kThreads + tid;
         const int e = ids[j];
         bad |= (e >= E);
         if (e >= 0 && e < E) {
@@ -248,11 +257,11 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
         // (order-free sums)
         const uint32_t magic_l = (1u << 20) / (uint32_t)L + 1u;   // e / L = (e * magic_l) >> 20, e < 1024
         const uint32_t magic_k = (1u << 16) / (uint32_t)K + 1u;   // p / K = (p * magic_k) >> 16, p < 2048
-        uint32_t old[kFusedIdsPerThread], pk[kFusedIdsPerThread];
-        int tk[kFusedIdsPerThread];
+        uint32_t old[kIds], pk[kIds];
+        int tk[kIds];
 #pragma unroll
-        for (int j = 0; j < kFusedIdsPerThread; ++j) {
-            const int p = j * kMoveThreads + tid;
+        for (int j = 0; j < kIds; ++j) {
+            const int p = j * kThreads + tid;
             const int e = ids[j];
             tk[j] = -1;
             old[j] = 0u;
@@ -264,7 +273,7 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
             }
         }
 #pragma unroll
-        for (int j = 0; j < kFusedIdsPerThread; ++j) {
+        for (int j = 0; j < kIds; ++j) {
             if (tk[j] >= 0 && !((old[j] >> pk[j]) & 1u)) {
                 atomicAdd(&s.ptot[pk[j]], 1);
                 if (tk[j] < t_lo) atomicAdd(&s.pbef[pk[j]], 1);
@@ -284,6 +293,7 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
         peers &= bit ? m : ~m;
     }
     const int rank = lanes_below(peers);
+    asm volatile("" : : "v"(rank));                          // rank now, not after the barriers
     lds_barrier();                                         // (2) totals complete
 
     if constexpr (kDedup) {
@@ -297,7 +307,7 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
             const uint32_t bit = 1u << lane;
             int before = 0;
 #pragma unroll
-            for (int j = 0; j < kMoveWaves - 1; ++j)
+            for (int j = 0; j < kW - 1; ++j)
                 before += (t_lo + j < t && (s.tpres[t_lo + j] & bit)) ? 1 : 0;
             if (s.tpres[t] & bit) drow = pincl - pc + s.pbef[lane] + before;
             const uint32_t lo = (uint32_t)(lane * L);
@@ -321,16 +331,16 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
             dd.part_token_offset[lane] = pincl - pc;
             if (lane == P - 1) dd.part_token_offset[P] = M;
         }
-        for (int r = M + blockIdx.x * kMoveThreads + tid; r < T * P; r += gridDim.x * kMoveThreads)
+        for (int r = M + blockIdx.x * kThreads + tid; r < T * P; r += gridDim.x * kThreads)
             dd.tp_src[r] = -1;
     }
 
     // exclusive scan of the expert totals: 4 consecutive experts per thread;
     // in-wave prefixes go to LDS, the wave totals complete them
-    int c[kFusedExpertsPerThread], sum = 0;
+    int c[kPer], sum = 0;
 #pragma unroll
-    for (int j = 0; j < kFusedExpertsPerThread; ++j) {
-        const int e = tid * kFusedExpertsPerThread + j;
+    for (int j = 0; j < kPer; ++j) {
+        const int e = tid * kPer + j;
         c[j] = (e < E) ? s.cnt[e] : 0;
         sum += c[j];
     }
@@ -338,19 +348,28 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
     if (lane == kWave - 1) s.wsum[w] = incl;
     int run = incl - sum;
 #pragma unroll
-    for (int j = 0; j < kFusedExpertsPerThread; ++j) {
-        const int e = tid * kFusedExpertsPerThread + j;
+    for (int j = 0; j < kPer; ++j) {
+        const int e = tid * kPer + j;
         if (e < E) s.offp[e] = run;
         run += c[j];
     }
     lds_barrier();                                         // (3) prefixes complete
 
-    const int ws0 = s.wsum[0], ws1 = s.wsum[1], ws2 = s.wsum[2], ws3 = s.wsum[3];
-    const int N = ws0 + ws1 + ws2 + ws3;
-    auto wave_base = [&](int ww) { return (ww > 0 ? ws0 : 0) + (ww > 1 ? ws1 : 0) + (ww > 2 ? ws2 : 0); };
+    int wsv[kW], N = 0;
+#pragma unroll
+    for (int u = 0; u < kW; ++u) {
+        wsv[u] = s.wsum[u];
+        N += wsv[u];
+    }
+    auto wave_base = [&](int ww) {
+        int b = 0;
+#pragma unroll
+        for (int u = 0; u < kW; ++u) b += (u < ww) ? wsv[u] : 0;
+        return b;
+    };
     int myrow = -1;                               // row of own entry q = lane
     if (mvalid)
-        myrow = s.offp[me] + wave_base(me / kFusedExpertsPerWave) + s.before[me] + rank;
+        myrow = s.offp[me] + wave_base(me / kPerWave) + s.before[me] + rank;
 
     if constexpr (!kDedup) {
         if (item < n_items)
@@ -371,8 +390,8 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
         const int base = wave_base(w);
         int o = base + incl - sum;
 #pragma unroll
-        for (int j = 0; j < kFusedExpertsPerThread; ++j) {
-            const int e = tid * kFusedExpertsPerThread + j;
+        for (int j = 0; j < kPer; ++j) {
+            const int e = tid * kPer + j;
             if (e < E) {
                 expert_count[e] = c[j];
                 expert_offset[e] = o;
@@ -386,14 +405,14 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_kernel(
             *status = s.bad ? 1u : 0u;
         }
         lds_barrier();                                     // workgroup 0 only: full offsets
-        for (int p = tid; p < P; p += kMoveThreads) {
+        for (int p = tid; p < P; p += kThreads) {
             const int lo = s.off[p * L];
             const int hi = (p + 1 < P) ? s.off[(p + 1) * L] : N;
             part_offset[p] = lo;
             part_count[p] = hi - lo;
         }
     }
-    for (int r = N + blockIdx.x * kMoveThreads + tid; r < n; r += gridDim.x * kMoveThreads)
+    for (int r = N + blockIdx.x * kThreads + tid; r < n; r += gridDim.x * kThreads)
         src_pair[r] = -1;
 }
 
@@ -442,7 +461,53 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, const int32_t
     return hipGetLastError();
 }
 
-bool fused_layout_dispatch_fits(int T, int K) { return (int64_t)T * K <= kFusedMaxPairs; }
+bool fused_layout_dispatch_fits(int T, int H, int K)
+{
+    const int64_t steps = (H + kStepCols - 1) / kStepCols;
+    return (int64_t)T * K <= kFusedMaxPairs && (int64_t)T * steps <= kMaxGridBlocks;
+}
+
+namespace {
+
+// Most tokens the items of one W-wave workgroup can touch.
+int max_own_tokens(int W, int steps)
+{
+    const int m = (W - 1 + steps - 1) / steps + 1;
+    return m < W ? m : W;
+}
+
+// Waves per fused workgroup.  Every workgroup redoes the whole histogram, so
+// once 4-wave workgroups would outnumber the 256 CUs, 8-wave ones (half as
+// many) finish sooner: measured at 128 x 7168, 5.8 against 6.1 us per
+// launch; 16-wave ones were slower (7.0 us: every wave repeats the own-entry
+// ranking).  Below that, 4 waves (at 4 and 16 tokens, 4.6 against 4.8 us).
+// The workgroup's own entries must fit one wave.
+constexpr int kCUs = 256;
+
+int fused_waves(int64_t items, int steps, int K)
+{
+    if (items > 4 * kCUs && max_own_tokens(8, steps) * K <= kWave) return 8;
+    return 4;
+}
+
+template <int kPayload, bool kDedup>
+hipError_t launch_fused(int W, const int32_t* topk_idx, const uint16_t* x, int n, int H, int K,
+                        int E, int P, int32_t* expert_count, int32_t* expert_offset,
+                        int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
+                        int32_t* src_pair, uint32_t* status, void* recv_x, float* recv_scales,
+                        int steps, int items, const DedupOutputs& dd, hipStream_t stream)
+{
+    const unsigned blocks = (unsigned)((items + W - 1) / W);
+    auto k = W == 8 ? layout_dispatch_kernel<kPayload, kDedup, 8>
+                    : layout_dispatch_kernel<kPayload, kDedup, 4>;
+    hipLaunchKernelGGL(k, dim3(blocks), dim3(W * kWave), 0, stream, topk_idx, x, n, H, K, E, P,
+                       expert_count, expert_offset, part_count, part_offset, row_of_pair, src_pair,
+                       status, (uint8_t*)recv_x, kPayload == 0 ? recv_scales : nullptr, steps,
+                       items, dd);
+    return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
                                   int E, int P, int payload, int32_t* expert_count,
@@ -454,20 +519,16 @@ hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, in
     const int steps = (H + kStepCols - 1) / kStepCols;
     const int64_t items = (int64_t)T * steps;
     const int n = T * K;
-    const int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
-    if (T == 0 || n > kFusedMaxPairs || blocks > kMaxGridBlocks) return hipErrorInvalidValue;
+    if (T == 0 || n > kFusedMaxPairs || items > kMaxGridBlocks) return hipErrorInvalidValue;
+    const int W = fused_waves(items, steps, K);
     const DedupOutputs none{};
-    if (payload == 0)
-        hipLaunchKernelGGL((layout_dispatch_kernel<0, false>), dim3((unsigned)blocks),
-                           dim3(kMoveThreads), 0, stream, topk_idx, x, n, H, K, E, P, expert_count,
-                           expert_offset, part_count, part_offset, row_of_pair, src_pair, status,
-                           (uint8_t*)recv_x, recv_scales, steps, (int)items, none);
-    else
-        hipLaunchKernelGGL((layout_dispatch_kernel<1, false>), dim3((unsigned)blocks),
-                           dim3(kMoveThreads), 0, stream, topk_idx, x, n, H, K, E, P, expert_count,
-                           expert_offset, part_count, part_offset, row_of_pair, src_pair, status,
-                           (uint8_t*)recv_x, nullptr, steps, (int)items, none);
-    return hipGetLastError();
+    return payload == 0
+        ? launch_fused<0, false>(W, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
+                                 part_count, part_offset, row_of_pair, src_pair, status, recv_x,
+                                 recv_scales, steps, (int)items, none, stream)
+        : launch_fused<1, false>(W, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
+                                 part_count, part_offset, row_of_pair, src_pair, status, recv_x,
+                                 recv_scales, steps, (int)items, none, stream);
 }
 
 hipError_t launch_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H,
@@ -482,21 +543,17 @@ hipError_t launch_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t*
     const int steps = (H + kStepCols - 1) / kStepCols;
     const int64_t items = (int64_t)T * steps;
     const int n = T * K;
-    const int64_t blocks = (items + kMoveWaves - 1) / kMoveWaves;
-    if (T == 0 || n > kFusedMaxPairs || P > kMaxTopK || blocks > kMaxGridBlocks)
+    if (T == 0 || n > kFusedMaxPairs || P > kMaxTopK || items > kMaxGridBlocks)
         return hipErrorInvalidValue;
+    const int W = fused_waves(items, steps, K);
     const DedupOutputs dd{tp_row, part_tokens, part_token_offset, tp_src, kmask};
-    if (payload == 0)
-        hipLaunchKernelGGL((layout_dispatch_kernel<0, true>), dim3((unsigned)blocks),
-                           dim3(kMoveThreads), 0, stream, topk_idx, x, n, H, K, E, P, expert_count,
-                           expert_offset, part_count, part_offset, row_of_pair, src_pair, status,
-                           (uint8_t*)recv_x, recv_scales, steps, (int)items, dd);
-    else
-        hipLaunchKernelGGL((layout_dispatch_kernel<1, true>), dim3((unsigned)blocks),
-                           dim3(kMoveThreads), 0, stream, topk_idx, x, n, H, K, E, P, expert_count,
-                           expert_offset, part_count, part_offset, row_of_pair, src_pair, status,
-                           (uint8_t*)recv_x, nullptr, steps, (int)items, dd);
-    return hipGetLastError();
+    return payload == 0
+        ? launch_fused<0, true>(W, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
+                                part_count, part_offset, row_of_pair, src_pair, status, recv_x,
+                                recv_scales, steps, (int)items, dd, stream)
+        : launch_fused<1, true>(W, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
+                                part_count, part_offset, row_of_pair, src_pair, status, recv_x,
+                                recv_scales, steps, (int)items, dd, stream);
 }
 
 hipError_t launch_e4m3fn_encode(const float* in, int64_t n, uint8_t* out, hipStream_t stream)

@@ -24,7 +24,7 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K,
                            void* recv_x, float* recv_scales, hipStream_t stream,
                            MoveGeometry g = kDefaultGeometry);
 
-bool fused_layout_dispatch_fits(int T, int K);
+bool fused_layout_dispatch_fits(int T, int H, int K);
 
 hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
                                   int E, int P, int payload, int32_t* expert_count,

@@ -86,6 +86,8 @@ FUSED_EDGE = {
     "at_limit_2048": dict(T=256, H=256),
     "over_limit_2056": dict(T=257, H=256),
     "bf16": dict(payload="bf16", T=50, H=512),
+    "w8_K16_T128": dict(T=128, K=16, E=64, P=16, H=7168),
+    "w8_two_steps": dict(T=1024, K=2, H=1024),
 }
 
 

@@ -62,6 +62,11 @@ FUSED_EDGE = {
     "at_limit_2048": dict(T=256, H=256),                  # T*K = 2048: fused
     "over_limit_2056": dict(T=257, H=256),                # T*K = 2056: layout + dispatch
     "bf16_payload": dict(payload="bf16", T=50, H=512),
+    # more than 1024 items: 8-wave workgroups
+    "w8_K16_T128": dict(T=128, K=16, E=64, P=8, H=7168),
+    "w8_one_step_8_tokens_per_wg": dict(T=2048, K=1, H=128),
+    "w8_two_steps": dict(T=1024, K=2, H=1024),
+    "w8_bf16_ragged": dict(payload="bf16", T=200, H=5000 // 8 * 8 + 8),
 }
 
 
