@@ -132,9 +132,9 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void dispatch_kernel(
 //     each thread leaves its experts' in-wave prefixes in LDS and the wave
 //     totals complete them after one barrier);
 //   - the slots of its own tokens' entries: offset + entries before + rank
-//     among the workgroup's own entries (ballot match-any, done by every wave
-//     on the same <= 64 ids, so each wave then stores its own item with no
-//     further barrier).
+//     among the workgroup's own entries (ballot match-any over the <= 64 own
+//     ids in one wave, while the others quantise; each wave then computes
+//     the rows of its own item and stores it with no further barrier).
 // Three barriers in all.  The x vectors are loaded first and quantised while
 // the histogram atomics drain, and the layout outputs are written after the
 // payload stores.  Workgroup 0 writes the counts, offsets, partition sums and
@@ -168,6 +168,7 @@ struct FusedSmem {
     int32_t offp[kMaxExperts];                 // in-wave exclusive prefix of cnt
     int32_t off[kMaxExperts];                  // workgroup 0: full offsets, for the partition sums
     int32_t wsum[kMaxFusedWaves];
+    int32_t rank[kWave];                       // own entry q: earlier own entries, same expert
     uint32_t bad;
     // dedup variant
     int32_t ptot[kMaxTopK];                    // tokens per partition
@@ -280,20 +281,21 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
             }
         }
     }
-    // while the atomics drain: quantise this wave's item and rank the
-    // workgroup's own entries among themselves (every wave, same ids)
+    // while the atomics drain: quantise this wave's item; the last wave also
+    // ranks the workgroup's own entries among themselves (match-any ballots)
     float scale = 0.0f;
     uint2 q = make_uint2(0u, 0u);
     if (item < n_items) q = prepare_item<kPayload>(v, scale);
     const bool mvalid = (me >= 0) && (me < E);
-    uint64_t peers = __ballot(mvalid);
-    for (int b = 0; b < 10; ++b) {                // ids < kMaxExperts = 2^10
-        const bool bit = (me >> b) & 1;
-        const uint64_t m = __ballot(bit);
-        peers &= bit ? m : ~m;
+    if (w == kW - 1) {
+        uint64_t peers = __ballot(mvalid);
+        for (int b = 0; b < 10; ++b) {            // ids < kMaxExperts = 2^10
+            const bool bit = (me >> b) & 1;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        s.rank[lane] = lanes_below(peers);
     }
-    const int rank = lanes_below(peers);
-    asm volatile("" : : "v"(rank));                          // rank now, not after the barriers
     lds_barrier();                                         // (2) totals complete
 
     if constexpr (kDedup) {
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
     };
     int myrow = -1;                               // row of own entry q = lane
     if (mvalid)
-        myrow = s.offp[me] + wave_base(me / kPerWave) + s.before[me] + rank;
+        myrow = s.offp[me] + wave_base(me / kPerWave) + s.before[me] + s.rank[lane];
 
     if constexpr (!kDedup) {
         if (item < n_items)
