@@ -128,9 +128,9 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void dispatch_kernel(
 // separate layout launch precedes the dispatch:
 //   - the per-expert totals (LDS atomics: integer sums, order-free), and per
 //     expert the number of entries before this workgroup's first token;
-//   - the exclusive scan of the totals (4 experts per thread, DPP wave scan;
-//     each thread leaves its experts' in-wave prefixes in LDS and the wave
-//     totals complete them after one barrier);
+//   - the exclusive scan of the totals (1024 / threads consecutive experts per
+//     thread, DPP wave scan; each thread leaves its experts' in-wave prefixes
+//     in LDS and the wave totals complete them after one barrier);
 //   - the slots of its own tokens' entries: offset + entries before + rank
 //     among the workgroup's own entries (ballot match-any over the <= 64 own
 //     ids in one wave, while the others quantise; each wave then computes
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
     const int t_hi = last / steps_per_token;
     const int nown = t_hi - t_lo + 1;             // own tokens, <= kW
     const int p_lo = t_lo * K;
-    const int nq = nown * K;                      // own entries, <= kW * kMaxTopK = 64
+    const int nq = nown * K;                      // own entries, <= 64 (the launcher picks kW so)
     const int T = n / K;
     const int L = E / P;
 
