@@ -256,8 +256,13 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
         // clear counts the token once for that partition, and once more in
         // the total before t_lo when the token precedes the workgroup's own
         // (order-free sums)
-        const uint32_t magic_l = (1u << 20) / (uint32_t)L + 1u;   // e / L = (e * magic_l) >> 20, e < 1024
-        const uint32_t magic_k = (1u << 16) / (uint32_t)K + 1u;   // p / K = (p * magic_k) >> 16, p < 2048
+        // Exact division by multiply-shift: with m = floor(2^s / d) + 1 and
+        // 2^s = q*d + r, a*m / 2^s = a/d + a*(d - r) / (d * 2^s), and the
+        // error term stays below 1/d (so floor is unchanged) whenever
+        // a*(d - r) < 2^s: for e < 1024, L <= 1024, s = 20 (1023 * 1024 <
+        // 2^20), and for entries p < 2048, K <= 16, s = 16 (2047 * 16 < 2^16).
+        const uint32_t magic_l = (1u << 20) / (uint32_t)L + 1u;   // e / L = (e * magic_l) >> 20
+        const uint32_t magic_k = (1u << 16) / (uint32_t)K + 1u;   // p / K = (p * magic_k) >> 16
         uint32_t old[kIds], pk[kIds];
         int tk[kIds];
 #pragma unroll
