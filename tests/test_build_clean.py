@@ -11,8 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_build_from_a_clean_tree(tmp_path):
     dst = tmp_path / "repo"
-    ignore = shutil.ignore_patterns("*.so", "_build", "__pycache__", ".git", "_work", "gpurun_out",
-                                    "profiles", ".pytest_cache")
+    ignore = shutil.ignore_patterns("*.so", "_build", "__pycache__", ".pytest_cache")
     for name in ("combine_ep_layout_05_amd", "oracle", "include", "workloads", "tests"):
         shutil.copytree(os.path.join(ROOT, name), dst / name, ignore=ignore)
     shutil.copy(os.path.join(ROOT, "__graft_entry__.py"), dst / "__graft_entry__.py")
