@@ -9,7 +9,8 @@
 // staging copy of the combine input).
 //
 // Work split: one wave per (token, 512-column step), items strided flatly
-// over the whole grid -- partitioning by (token, hidden slice) rather than by
+// over the whole grid (waves per workgroup and workgroup count from the
+// launch geometry) -- partitioning by (token, hidden slice) rather than by
 // token keeps every wave busy at small token counts (same PR, CombineSync
 // paragraph), and 512 columns per wave is the floor the same PR measured
 // best (MultiWarpIter paragraph).  Each lane owns 8 columns: it issues all of

@@ -12,7 +12,8 @@
 //
 // Work split.  A work item is (token, 512-column step): one wave, 64 lanes,
 // 16 bytes (8 bf16) per lane.  Items are strided flatly over every wave of
-// the grid, so a handful of tokens still spreads over many CUs (MoRI PR #614,
+// the grid (waves per workgroup and the workgroup count are the launch
+// geometry: 4 waves and one wave per item unless the caller tunes them), so a handful of tokens still spreads over many CUs (MoRI PR #614,
 // DispatchIntraNode paragraph: splitting per block over tokens starved most
 // blocks at 4 tokens; MultiWarpIter paragraph: keep at least 512 elements per
 // warp).  Per lane:
@@ -20,9 +21,12 @@
 //   - the 128-column block of a scale is one 16-lane DPP row, so amax is a
 //     per-lane max over 8 values and 4 DPP max steps (quad_perm xor 1,
 //     quad_perm xor 2, row_half_mirror, row_mirror), with no LDS traffic;
-//   - x / scale is the IEEE-correct fp32 division; v_cvt_pk_fp8_f32 packs
-//     two values per instruction (round to nearest even; a NaN-preserving
-//     clamp to +-448 in front gives the saturating behaviour);
+//   - x / scale gives the byte of the IEEE fp32 quotient: a reciprocal plus
+//     one remainder correction where the scale is >= 2^-90 (shown
+//     byte-identical to the division over every pair of bf16 values), the
+//     division itself otherwise (ep_numerics.h); v_cvt_pk_fp8_f32 packs two
+//     values per instruction (round to nearest even; a NaN-preserving clamp
+//     to +-448 in front gives the saturating behaviour);
 //   - K stores of 8 bytes (512 contiguous bytes per wave per row, whole
 //     128-byte lines) and one 4-byte scale per 16-lane row.
 // The next item's x vector and row indices are loaded before the current
