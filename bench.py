@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -309,6 +310,22 @@ def single_step_us(p, reps, flush_bytes=0):
     return float(np.median(times))
 
 
+def native_loop(wl, steps=5000):
+    """ep_layout_dispatch + ep_combine enqueued back to back from C++ (the
+    package's ep_loop program, a child process started before this process
+    touches the GPU): host and wall microseconds per step, i.e. what a native
+    serving loop pays without an interpreter or graph launches in between.
+    Uses the library's default launch geometry."""
+    exe = os.path.join(ROOT, "combine_ep_layout_05_amd", "ep_loop")
+    if not os.path.exists(exe):
+        return None
+    r = subprocess.run([exe, str(wl.T), str(wl.H), str(wl.K), str(wl.E), str(wl.P), wl.payload,
+                        str(steps)], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        return {"error": (r.stderr or r.stdout)[-300:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def measure(wl, steps, warmup, mode="graph", phase="step"):
     p = Path(wl)
     b = algo_bytes(wl, p.N)
@@ -370,6 +387,10 @@ def main():
             print("profiled %s x%d on %s" % (args.only, args.warmup + args.steps, wl.name), flush=True)
         return
 
+    native = None
+    if not args.no_targets:      # before this process initialises the GPU
+        native = {w.name: native_loop(w) for w in (wl, WORKLOADS["sweep_4x6144"])}
+
     step = "step3" if args.unfused else "step"
     mode = "eager" if args.eager else "graph"
     p, b, us = measure(wl, args.steps, args.warmup, mode=mode, phase=step)
@@ -424,7 +445,7 @@ def main():
     }
 
     if not args.no_targets:
-        tg = {}
+        tg = {"native_loop_us_per_step": native}
         pw, bw_, us4 = measure(WORKLOADS["sweep_4x6144"], 2000, 50)
         tg["sweep_4x6144_us_per_step_graph"] = round(us4, 3)
         tg["sweep_4x6144_us_per_step_graph1"] = round(time_steps(pw, 1000, 20, "graph1"), 3)

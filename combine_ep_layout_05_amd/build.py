@@ -23,6 +23,9 @@ FLAGS = [
 ]
 
 
+LOOP = os.path.join(HERE, "ep_loop")     # native serving-loop timer over the C ABI
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -41,6 +44,17 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     if verbose and msg.strip():
         print(msg)
     os.replace(tmp, LIB)
+    # the native loop timer links the library just built (host code only)
+    tmp = LOOP + ".tmp%d" % os.getpid()
+    cmd = ["hipcc", "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+           os.path.join(CSRC, "ep_loop.cpp"), "-L", HERE, "-lep_mi355x",
+           "-Wl,-rpath,$ORIGIN", "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on ep_loop.cpp:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LOOP)
     return LIB
 
 
