@@ -21,5 +21,6 @@ def test_build_from_a_clean_tree(tmp_path):
                        cwd=dst, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
     assert (dst / "combine_ep_layout_05_amd" / "libep_mi355x.so").exists()
+    assert (dst / "combine_ep_layout_05_amd" / "ep_loop").exists()         # native loop timer
     assert r.stdout.strip().endswith(os.path.join("repo", "combine_ep_layout_05_amd",
                                                   "libep_mi355x.so"))
