@@ -88,7 +88,11 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
     const int lane = threadIdx.x % kWave;
     const int waves = blockDim.x / kWave;
     const int stride = gridDim.x * waves;
-    for (int item = blockIdx.x * waves + wave_uniform(threadIdx.x / kWave); item < n_items;
+    // cached regime: the XCD-contiguous block order, so a token's items run on
+    // the XCD that wrote its metadata; streaming regime: launch order (there
+    // the contiguous order measured slower, 88 -> 97 us at 4096 x 7168)
+    const int block = kStream ? (int)blockIdx.x : xcd_block(blockIdx.x, gridDim.x);
+    for (int item = block * waves + wave_uniform(threadIdx.x / kWave); item < n_items;
          item += stride) {                   // n_items + stride < 2^31 (checked by the launcher)
         const int t = item / steps_per_token;
         const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
@@ -178,6 +182,16 @@ hipError_t launch_combine_mode(const uint16_t* y, const int32_t* row_of_pair,
     return hipGetLastError();
 }
 
+// The two dedup combine levels run on the same item -> workgroup -> XCD map
+// as the fused dedup dispatch before them (8 waves per workgroup once 4-wave
+// workgroups would outnumber the CUs, else 4; uncapped), so each reads the
+// masks, row maps and partial rows of a token on the XCD that wrote them.
+MoveGeometry dedup_geometry(int T, int H)
+{
+    const int64_t items = (int64_t)T * ((H + kStepCols - 1) / kStepCols);
+    return MoveGeometry{items > 4 * kCUs ? 8 : 4, 0};
+}
+
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of_pair, const float* topk_w,
@@ -193,14 +207,15 @@ hipError_t launch_combine_partial(const uint16_t* y, const int32_t* row_of_pair,
                                   uint16_t* partial, hipStream_t stream)
 {
     return launch_combine_mode<kPartial>(y, row_of_pair, topk_w, T, H, K, T * K, tp_row, kmask, P,
-                                         T * P, (int64_t)T * K, partial, stream, kDefaultGeometry);
+                                         T * P, (int64_t)T * K, partial, stream,
+                                         dedup_geometry(T, H));
 }
 
 hipError_t launch_combine_reduce(const uint16_t* partial, const int32_t* tp_row, int T, int H,
                                  int P, uint16_t* out, hipStream_t stream)
 {
     return launch_combine_mode<kReduce>(partial, tp_row, nullptr, T, H, P, T * P, nullptr, nullptr,
-                                        1, T, (int64_t)T * P, out, stream, kDefaultGeometry);
+                                        1, T, (int64_t)T * P, out, stream, dedup_geometry(T, H));
 }
 
 }  // namespace ep

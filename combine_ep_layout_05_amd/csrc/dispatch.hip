@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int w = wave_uniform(tid / kWave);
-    const int item0 = blockIdx.x * kW;
+    const int item0 = xcd_block(blockIdx.x, gridDim.x) * kW;
     const int item = item0 + w;
     const int last = (item0 + kW - 1 < n_items) ? item0 + kW - 1 : n_items - 1;
     const int t_lo = item0 / steps_per_token;
@@ -493,8 +493,6 @@ int max_own_tokens(int W, int steps)
 // launch; 16-wave ones were slower (7.0 us: every wave repeats the own-entry
 // ranking).  Below that, 4 waves (at 4 and 16 tokens, 4.6 against 4.8 us).
 // The workgroup's own entries must fit one wave.
-constexpr int kCUs = 256;
-
 int fused_waves(int64_t items, int steps, int K)
 {
     if (items > 4 * kCUs && max_own_tokens(8, steps) * K <= kWave) return 8;

@@ -119,6 +119,23 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// MI355X runs a launch's workgroups on its 8 XCDs round robin (workgroup b
+// on XCD b % 8), each XCD with its own L2.  xcd_block renumbers the grid so
+// that every XCD holds one contiguous range of logical blocks: kernels that
+// map logical block -> items the same way then run a token's items on the
+// same XCD, and a kernel reading what the previous one wrote for that token
+// (row maps, dedup masks, partial rows) finds it in that XCD's L2 instead of
+// going out to the memory-side cache.
+constexpr int kXcds = 8;
+constexpr int kCUs = 256;                  // compute units of an MI355X
+
+__device__ __forceinline__ int xcd_block(int b, int nblocks)
+{
+    const int per = nblocks / kXcds, rem = nblocks % kXcds;
+    const int x = b % kXcds, slot = b / kXcds;
+    return x * per + (x < rem ? x : rem) + slot;
+}
+
 __device__ __forceinline__ int wave_uniform(int v)
 {
     return __builtin_amdgcn_readfirstlane(v);
