@@ -33,6 +33,8 @@
 // item's quantise-and-store work, so each wave keeps one load in flight
 // while its stores drain (the prefetch idea of DeepEP PR #693, with a
 // register double buffer instead of shared-memory TMA staging).
+#include <type_traits>
+
 #include "ep_device.h"
 #include "ep_launch.h"
 #include "ep_numerics.h"
@@ -177,12 +179,18 @@ struct FusedSmem {
     // dedup variant
     int32_t ptot[kMaxTopK];                    // tokens per partition
     int32_t pbef[kMaxTopK];                    // of those, before this workgroup's first token
-    uint32_t tpres[kFusedMaxPairs];            // partition set (bit p) of every token
+};
+
+template <int kMaxN>
+struct FusedDedupSmem : FusedSmem {
+    uint32_t tpres[kMaxN];                     // partition set (bit p) of every token
 };
 
 // kW waves per workgroup, each wave one work item; the workgroup's own
 // tokens' entries (at most 64, checked by the launcher) are ranked in one wave.
-template <int kPayload, bool kDedup, int kW>
+// kMaxN (2048 or 4096) bounds T*K: the ids each thread holds are kMaxN /
+// threads, so small batches take the smaller instance.
+template <int kPayload, bool kDedup, int kW, int kMaxN>
 __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, int n, int H, int K, int E,
     int P, int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
@@ -192,13 +200,14 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
     int steps_per_token, int n_items, DedupOutputs dd)
 {
     constexpr int kThreads = kW * kWave;
-    constexpr int kIds = kFusedMaxPairs / kThreads;        // ids per thread
+    constexpr int kIds = kMaxN / kThreads;                 // ids per thread
     constexpr int kPer = kMaxExperts / kThreads;           // experts per thread
     constexpr int kPerWave = kPer * kWave;
-    static_assert(kIds * kThreads == kFusedMaxPairs && kPer * kThreads == kMaxExperts,
+    static_assert(kIds * kThreads == kMaxN && kPer * kThreads == kMaxExperts,
                   "ids and experts split evenly over the threads");
+    static_assert(kMaxN <= kFusedMaxPairs, "the launcher's bound");
     static_assert(kW <= kMaxFusedWaves, "wave totals fit");
-    __shared__ FusedSmem s;
+    __shared__ std::conditional_t<kDedup, FusedDedupSmem<kMaxN>, FusedSmem> s;
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int w = wave_uniform(tid / kWave);
@@ -219,8 +228,11 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
     int ids[kIds];
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
-        const int p = j * kThreads + tid;
-        ids[j] = idx[p < n ? p : n - 1];
+        ids[j] = -1;
+        if (j * kThreads < n) {                           // rounds with ids (uniform)
+            const int p = j * kThreads + tid;
+            ids[j] = idx[p < n ? p : n - 1];
+        }
     }
     int me = idx[p_lo + (lane < nq ? lane : 0)];           // own entry q = lane
     int t = 0, col0 = H;
@@ -245,6 +257,7 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
     bool bad = false;
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
+        if (j * kThreads >= n) break;                     // no more ids (uniform)
         const int p = j * kThreads + tid;
         const int e = ids[j];
         bad |= (e >= E);
@@ -264,7 +277,7 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
         // 2^s = q*d + r, a*m / 2^s = a/d + a*(d - r) / (d * 2^s), and the
         // error term stays below 1/d (so floor is unchanged) whenever
         // a*(d - r) < 2^s: for e < 1024, L <= 1024, s = 20 (1023 * 1024 <
-        // 2^20), and for entries p < 2048, K <= 16, s = 16 (2047 * 16 < 2^16).
+        // 2^20), and for entries p < 4096, K <= 16, s = 16 (4095 * 16 < 2^16).
         const uint32_t magic_l = (1u << 20) / (uint32_t)L + 1u;   // e / L = (e * magic_l) >> 20
         const uint32_t magic_k = (1u << 16) / (uint32_t)K + 1u;   // p / K = (p * magic_k) >> 16
         uint32_t old[kIds], pk[kIds];
@@ -272,7 +285,7 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
 #pragma unroll
         for (int j = 0; j < kIds; ++j) {
             const int p = j * kThreads + tid;
-            const int e = ids[j];
+            const int e = j * kThreads < n ? ids[j] : -1;
             tk[j] = -1;
             old[j] = 0u;
             pk[j] = 0u;
@@ -507,8 +520,11 @@ hipError_t launch_fused(int W, const int32_t* topk_idx, const uint16_t* x, int n
                         int steps, int items, const DedupOutputs& dd, hipStream_t stream)
 {
     const unsigned blocks = (unsigned)((items + W - 1) / W);
-    auto k = W == 8 ? layout_dispatch_kernel<kPayload, kDedup, 8>
-                    : layout_dispatch_kernel<kPayload, kDedup, 4>;
+    const bool small = n <= kFusedMaxPairs / 2;
+    auto k = W == 8 ? (small ? layout_dispatch_kernel<kPayload, kDedup, 8, kFusedMaxPairs / 2>
+                             : layout_dispatch_kernel<kPayload, kDedup, 8, kFusedMaxPairs>)
+                    : (small ? layout_dispatch_kernel<kPayload, kDedup, 4, kFusedMaxPairs / 2>
+                             : layout_dispatch_kernel<kPayload, kDedup, 4, kFusedMaxPairs>);
     hipLaunchKernelGGL(k, dim3(blocks), dim3(W * kWave), 0, stream, topk_idx, x, n, H, K, E, P,
                        expert_count, expert_offset, part_count, part_offset, row_of_pair, src_pair,
                        status, (uint8_t*)recv_x, kPayload == 0 ? recv_scales : nullptr, steps,

@@ -29,7 +29,7 @@ static_assert(kLayoutWaves * kWave <= 0xFFFF, "per-wave counts fit in uint16");
 
 // ---- dispatch / combine ---------------------------------------------------
 constexpr int kMaxTopK = 16;
-constexpr int kFusedMaxPairs = 2048;       // layout fused into dispatch up to this T*K
+constexpr int kFusedMaxPairs = 4096;       // layout fused into dispatch up to this T*K
 constexpr int kMoveThreads = 256;          // 4 waves per workgroup
 // payload bytes of one call above which dispatch/combine use streaming
 // (nontemporal) accesses; below it the working set stays cache resident

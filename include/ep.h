@@ -140,7 +140,7 @@ int ep_dispatch(const uint16_t* x, int T, int H, int K,
 /*
  * Layout and dispatch in one call: the same results as ep_layout followed by
  * ep_dispatch (every output of both, bit for bit), with the same arguments
- * and errors as those two calls together.  For small batches (T*K <= 2048
+ * and errors as those two calls together.  For small batches (T*K <= 4096
  * and T * ceil(H/512) <= 2^20) it is ONE kernel launch: each dispatch
  * workgroup derives the layout values it needs from the T*K ids, so no
  * separate layout launch precedes it -- at a few tokens the step is paced by
@@ -222,7 +222,7 @@ size_t ep_dedup_layout_dispatch_workspace_bytes(int T, int K, int E, int P);
  * The sender's whole dedup step in one call: the per-expert layout (every
  * output of ep_layout), the dedup layout (every output of ep_dedup_layout)
  * and the dedup dispatch (ep_dispatch with K = P over tp_row), bit for bit
- * the same as those three calls.  For T*K <= 2048 (and T * ceil(H/512) <=
+ * the same as those three calls.  For T*K <= 4096 (and T * ceil(H/512) <=
  * 2^20) it is ONE kernel launch (each workgroup derives both layouts' values
  * for its own tokens from the T*K ids); larger batches run the three calls'
  * kernels back to back.

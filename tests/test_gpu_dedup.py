@@ -85,6 +85,9 @@ FUSED_EDGE = {
     "H640": dict(H=640, T=33),
     "at_limit_2048": dict(T=256, H=256),
     "over_limit_2056": dict(T=257, H=256),
+    "at_limit_4096": dict(T=512, H=256),
+    "over_limit_4104": dict(T=513, H=256),
+    "w8_4096_ids": dict(T=300, H=7168, E=32, P=8),
     "bf16": dict(payload="bf16", T=50, H=512),
     "w8_K16_T128": dict(T=128, K=16, E=64, P=16, H=7168),
     "w8_two_steps": dict(T=1024, K=2, H=1024),

@@ -59,8 +59,11 @@ FUSED_EDGE = {
     "E1024": dict(E=1024, P=8, T=64),
     "H128_many_tokens_per_wg": dict(H=128, T=200),        # 1 step/token: 4 tokens per workgroup
     "H640": dict(H=640, T=33),
-    "at_limit_2048": dict(T=256, H=256),                  # T*K = 2048: fused
-    "over_limit_2056": dict(T=257, H=256),                # T*K = 2056: layout + dispatch
+    "at_2048": dict(T=256, H=256),                        # T*K = 2048: the 2048-id instance
+    "over_2048": dict(T=257, H=256),                      # T*K = 2056: the 4096-id instance
+    "at_limit_4096": dict(T=512, H=256),                  # T*K = 4096: fused
+    "over_limit_4104": dict(T=513, H=256),                # T*K = 4104: layout + dispatch
+    "w8_4096_ids": dict(T=300, H=7168),                   # 4096-id instance with 8-wave workgroups
     "bf16_payload": dict(payload="bf16", T=50, H=512),
     # more than 1024 items: 8-wave workgroups
     "w8_K16_T128": dict(T=128, K=16, E=64, P=8, H=7168),

@@ -1,6 +1,6 @@
 """The fused dedup kernel divides by multiply-shift: e / L as (e * m) >> 20
 with m = floor(2^20 / L) + 1 for ids e < 1024 and L <= 1024, and p / K as
-(p * m) >> 16 with m = floor(2^16 / K) + 1 for entries p < 2048 and K <= 16.
+(p * m) >> 16 with m = floor(2^16 / K) + 1 for entries p < 4096 and K <= 16.
 Checked exhaustively over those ranges in 32-bit unsigned arithmetic, as the
 kernel computes it."""
 import numpy as np
@@ -20,4 +20,4 @@ def test_expert_over_experts_per_partition():
 
 
 def test_entry_over_topk():
-    _check(2048, 16, 16)
+    _check(4096, 16, 16)
