@@ -20,7 +20,7 @@ constexpr int kWave = 64;                  // gfx950 wavefront width
 constexpr int kLayoutThreads = 1024;       // one pair per thread per round
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kMaxExperts = 1024;          // one expert column per thread
-constexpr int kSmallMaxPairs = 4096;       // single-workgroup layout up to this
+constexpr int kSmallMaxPairs = 2048;       // single-workgroup layout up to this
 constexpr int kChunkPairs = 1024;          // pairs per workgroup above it
 constexpr int kMaxChunksTwoPass = 256;     // above: a separate scan launch
 static_assert(kMaxExperts <= kLayoutThreads, "scan assigns one expert per thread");

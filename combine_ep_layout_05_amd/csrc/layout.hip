@@ -39,7 +39,7 @@
 namespace ep {
 namespace {
 
-constexpr int kSmallRounds = kSmallMaxPairs / kLayoutThreads;   // 4
+constexpr int kSmallRounds = kSmallMaxPairs / kLayoutThreads;   // 2
 constexpr int kChunkRounds = kChunkPairs / kLayoutThreads;      // 2
 
 struct LayoutSmem {

@@ -48,7 +48,8 @@ DEDUP_EDGE = {
     "K1": dict(K=1),
     "K16_P16": dict(K=16, E=64, P=16),
     "H640": dict(H=640, T=33),
-    "single_wg_limit_4096": dict(T=512, H=256, P=8),     # T*P = 4096: one layout workgroup
+    "single_wg_limit_2048": dict(T=256, H=256, P=8),     # T*P = 2048: one layout workgroup
+    "chunked_4096": dict(T=512, H=256, P=8),
     "chunked_4104": dict(T=513, H=256, P=8),             # T*P = 4104: chunked layout
     "many_chunks_scan_pass": dict(T=40000, H=128, E=64, P=8),   # > 256 chunks of couples
     "bf16": dict(payload="bf16", T=50, H=512),

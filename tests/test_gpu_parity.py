@@ -100,7 +100,9 @@ EDGE = {
     "H640_ragged_step": dict(H=640),
     "H1152": dict(H=1152),
     "E1024": dict(E=1024, P=8, T=64),
-    "just_over_single_wg": dict(T=513, H=256),        # 4104 pairs -> chunked path, ragged chunk
+    "single_wg_limit": dict(T=256, H=256),            # 2048 pairs: one layout workgroup
+    "just_over_single_wg": dict(T=257, H=256),        # 2056 pairs -> chunked path, ragged chunk
+    "chunked_4104": dict(T=513, H=256),
     "chunked_ragged": dict(T=700, H=384, E=96, P=4),
     "many_chunks_scan_pass": dict(T=70000, H=128, E=64, P=8),   # > 256 chunks: scan launch
 }
