@@ -38,19 +38,33 @@ __device__ __forceinline__ uint8_t encode_e4m3fn_one(float a)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// Max over the 16 lanes of this lane's DPP row (rows are lanes 16r .. 16r+15).
+// Max over the 16 lanes of this lane's DPP row of non-negative fp32 values,
+// taken on their bit patterns (which order like the values); NaN enters as
+// -1, below every pattern, so it survives only where all 16 lanes hold it --
+// the IEEE maxNum of the row.  Integer max lets each step be one DPP-fused
+// v_max_i32 (a float max would first have to quiet the moved operand).
 __device__ __forceinline__ float row16_max(float a)
 {
+    int k = (a == a) ? __builtin_bit_cast(int, a) : -1;
     // the DPP control must be a constant expression, hence the spelled-out steps
-    a = __builtin_fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                               0, __builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false)));   // quad_perm [1,0,3,2]
-    a = __builtin_fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                               0, __builtin_bit_cast(int, a), 0x4E, 0xF, 0xF, false)));   // quad_perm [2,3,0,1]
-    a = __builtin_fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                               0, __builtin_bit_cast(int, a), 0x141, 0xF, 0xF, false)));  // row_half_mirror
-    a = __builtin_fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                               0, __builtin_bit_cast(int, a), 0x140, 0xF, 0xF, false)));  // row_mirror
-    return a;
+    k = __builtin_elementwise_max(k, __builtin_amdgcn_update_dpp(0, k, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    k = __builtin_elementwise_max(k, __builtin_amdgcn_update_dpp(0, k, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    k = __builtin_elementwise_max(k, __builtin_amdgcn_update_dpp(0, k, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    k = __builtin_elementwise_max(k, __builtin_amdgcn_update_dpp(0, k, 0x140, 0xF, 0xF, false));  // row_mirror
+    return k < 0 ? __builtin_nanf("") : __builtin_bit_cast(float, k);
+}
+
+// amax / 448 correctly rounded without a division: with c = RN(1/448),
+// q0 = amax*c, r = fma(-q0, 448, amax) (exact remainder), scale = fma(r, c, q0).
+// Equal to the IEEE quotient for every finite bf16 amax (all 32640 checked on
+// the CPU and on gfx950); an infinite or NaN amax makes r NaN and keeps q0,
+// which is then amax*c = amax/448 (inf or NaN).
+constexpr float kInv448 = 0x1.24924ap-9f;
+__device__ __forceinline__ float block_scale(float amax)
+{
+    const float q0 = amax * kInv448;
+    const float r = __builtin_fmaf(-q0, kE4m3Max, amax);
+    return (r == r) ? __builtin_fmaf(r, kInv448, q0) : q0;
 }
 
 // Smallest scale for which the quotient shortcut below reproduces the IEEE
@@ -59,18 +73,22 @@ constexpr float kFastQuotientMinScale = 0x1p-90f;
 
 // Quantise this lane's 8 bf16 values (16 bytes) with the scale of its
 // 128-column block (= its 16-lane DPP row).  Must be called by all 64 lanes.
-// scale = amax / 448 (IEEE fp32 division; 0 when amax is 0); each byte is
+// scale = amax / 448 (the IEEE fp32 quotient; 0 when amax is 0); each byte is
 // e4m3fn(x / scale) with x / scale the IEEE-rounded fp32 quotient; a zero block
 // gives zero bytes.
 //
-// The quotient: one IEEE reciprocal y = 1/scale per lane, then per element
-// q0 = |x|*y, r = fma(-q0, scale, |x|) (the exact remainder), q = fma(r, y, q0)
-// with x's sign -- the reciprocal-and-remainder correction step of
-// IA-64-style division (Markstein).  Checked exhaustively on the CPU: over
-// every pair of bf16 values x, amax with |x| <= amax and scale >= 2^-90 it
-// yields the same e4m3fn byte as IEEE division (its fp32 result can differ
-// only below 2^-10, where both encode to a signed zero).  Smaller (or
-// non-finite) scales take the IEEE division.
+// The quotient: y = RN(1/scale) per lane, then per element q0 = |x|*y,
+// r = fma(-q0, scale, |x|) (the exact remainder), q = fma(r, y, q0) with x's
+// sign -- the reciprocal-and-remainder correction step of IA-64-style
+// division (Markstein).  Checked exhaustively on the CPU: over every pair of
+// bf16 values x, amax with |x| <= amax and scale >= 2^-90 it yields the same
+// e4m3fn byte as IEEE division (its fp32 result can differ only below 2^-10,
+// where both encode to a signed zero).  y itself is v_rcp_f32 (within 1 ulp)
+// plus one Newton step with fma, which gives RN(1/scale) for every scale a
+// bf16 amax can produce (checked on gfx950 against the IEEE reciprocal).
+// There |q| < 448.0001, which v_cvt_pk_fp8_f32 rounds to +-448 (it returns
+// NaN only from 464 up), so this path needs no clamp.  Smaller (or
+// non-finite) scales take the IEEE division and the saturating clamp.
 __device__ __forceinline__ uint2 quantise_e4m3fn_block8(uint4 v, float& scale)
 {
     float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
@@ -79,12 +97,13 @@ __device__ __forceinline__ uint2 quantise_e4m3fn_block8(uint4 v, float& scale)
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
     amax = row16_max(amax);
-    scale = amax / kE4m3Max;
+    scale = block_scale(amax);
     uint2 q = make_uint2(0u, 0u);
     if (amax != 0.0f) {
-        float d[8];
         if (scale >= kFastQuotientMinScale && scale <= 0x1.fffffep+127f) {
-            const float y = 1.0f / scale;
+            const float y0 = __builtin_amdgcn_rcpf(scale);
+            const float y = __builtin_fmaf(__builtin_fmaf(-scale, y0, 1.0f), y0, y0);
+            float d[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float a = __builtin_fabsf(f[i]);
@@ -92,12 +111,18 @@ __device__ __forceinline__ uint2 quantise_e4m3fn_block8(uint4 v, float& scale)
                 const float r = __builtin_fmaf(-q0, scale, a);
                 d[i] = __builtin_copysignf(__builtin_fmaf(r, y, q0), f[i]);
             }
+            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(d[0], d[1], 0, false);
+            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(d[2], d[3], w0, true);
+            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(d[4], d[5], 0, false);
+            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(d[6], d[7], w1, true);
+            q = make_uint2((uint32_t)w0, (uint32_t)w1);
         } else {
+            float d[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) d[i] = f[i] / scale;
+            q.x = pack4_e4m3fn(d[0], d[1], d[2], d[3]);
+            q.y = pack4_e4m3fn(d[4], d[5], d[6], d[7]);
         }
-        q.x = pack4_e4m3fn(d[0], d[1], d[2], d[3]);
-        q.y = pack4_e4m3fn(d[4], d[5], d[6], d[7]);
     }
     return q;
 }
