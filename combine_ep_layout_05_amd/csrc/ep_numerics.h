@@ -29,9 +29,14 @@ __device__ __forceinline__ uint32_t pack4_e4m3fn(float a, float b, float c, floa
     return (uint32_t)w;
 }
 
+// One value, as the dispatch encodes it: below 464 in magnitude the bare
+// instruction (the quotient fast path), from 464 up and for NaN after the
+// clamp (the IEEE-division path) -- so a range check of this function covers
+// the instruction's rounding of (448, 464) to 448 that the fast path relies on.
 __device__ __forceinline__ uint8_t encode_e4m3fn_one(float a)
 {
-    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(a), 0.0f, 0, false);
+    const float c = (__builtin_fabsf(a) < 464.0f) ? a : clamp_e4m3(a);
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false);
     return (uint8_t)(w & 0xFF);
 }
 

@@ -308,9 +308,11 @@ int ep_graph_destroy(void* graph);
 
 /*
  * Encode n fp32 values with the same e4m3fn encoder the fp8 dispatch uses
- * (round to nearest even, saturating, NaN -> 0x7F|sign).  in: fp32 [n],
- * out: uint8 [n], both device pointers (4 B / 1 B aligned).  For checking
- * the encoder against the format definition over whole ranges of inputs.
+ * (round to nearest even, saturating, NaN -> 0x7F|sign; below 464 in
+ * magnitude the conversion instruction alone, from there on after a clamp to
+ * +-448).  in: fp32 [n], out: uint8 [n], both device pointers (4 B / 1 B
+ * aligned).  For checking the encoder against the format definition over
+ * whole ranges of inputs.
  */
 int ep_e4m3fn_encode(const float* in, int64_t n, uint8_t* out, void* stream);
 

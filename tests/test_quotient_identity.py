@@ -1,8 +1,10 @@
 """The fp8 dispatch kernel divides by the block scale with a reciprocal and one
 remainder-correction step instead of an IEEE division per element.  This
 checks, exhaustively over every bf16 input pair, that the shortcut yields the
-same e4m3fn byte as the IEEE-rounded quotient the method specifies (the GPU
-parity tests then compare the kernel itself against the oracle)."""
+same e4m3fn byte as the IEEE-rounded quotient the method specifies, with the
+reciprocal correctly rounded and also one ulp below or above it (the device
+takes it from v_rcp_f32 and a Newton step; the GPU parity tests then compare
+the kernel itself against the oracle)."""
 import os
 import subprocess
 
@@ -23,12 +25,12 @@ def checker(tmp_path_factory):
 
 @pytest.mark.slow
 def test_all_positive_pairs(checker):
-    r = subprocess.run([checker, "1", "0"], capture_output=True, text=True)
+    r = subprocess.run([checker, "1", "0", "1"], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout
     assert "differing bytes 0" in r.stdout
 
 
 def test_negative_pairs_strided(checker):
-    r = subprocess.run([checker, "37", "1"], capture_output=True, text=True)
+    r = subprocess.run([checker, "37", "1", "1"], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout
     assert "differing bytes 0" in r.stdout
