@@ -43,20 +43,20 @@ __device__ __forceinline__ uint8_t encode_e4m3fn_one(float a)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// Max over the 16 lanes of this lane's DPP row of non-negative fp32 values,
-// taken on their bit patterns (which order like the values); NaN enters as
-// -1, below every pattern, so it survives only where all 16 lanes hold it --
-// the IEEE maxNum of the row.  Integer max lets each step be one DPP-fused
-// v_max_i32 (a float max would first have to quiet the moved operand).
+// Max over the 16 lanes of this lane's DPP row of non-negative, non-NaN fp32
+// values (per-lane maxima that start from 0 and take fmaxf, which drops NaN),
+// taken on their bit patterns, which order like the values.  Integer max
+// lets each step be one DPP-fused v_max_i32 (a float max would first have to
+// quiet the moved operand).
 __device__ __forceinline__ float row16_max(float a)
 {
-    int k = (a == a) ? __builtin_bit_cast(int, a) : -1;
+    int k = __builtin_bit_cast(int, a);
     // the DPP control must be a constant expression, hence the spelled-out steps
     k = __builtin_elementwise_max(k, __builtin_amdgcn_update_dpp(0, k, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
     k = __builtin_elementwise_max(k, __builtin_amdgcn_update_dpp(0, k, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
     k = __builtin_elementwise_max(k, __builtin_amdgcn_update_dpp(0, k, 0x141, 0xF, 0xF, false));  // row_half_mirror
     k = __builtin_elementwise_max(k, __builtin_amdgcn_update_dpp(0, k, 0x140, 0xF, 0xF, false));  // row_mirror
-    return k < 0 ? __builtin_nanf("") : __builtin_bit_cast(float, k);
+    return __builtin_bit_cast(float, k);
 }
 
 // amax / 448 correctly rounded without a division: with c = RN(1/448),

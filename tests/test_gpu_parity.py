@@ -182,6 +182,53 @@ def test_fp8_quotient_sweep():
     _case(wl, d=d)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_fp8_non_finite_inputs(fused):
+    """Non-finite hidden values (outside the parity workloads; the documented
+    reading of the pages' silence): amax is a NaN-ignoring max starting from
+    0, so a NaN element leaves its block's scale finite and encodes to NaN
+    itself, and an all-NaN block gets scale 0 and zero bytes; an infinite
+    element makes the scale infinite, the other elements of its block encode
+    to signed zero and the infinite one (inf / inf) to NaN.  Layout, scales
+    and bytes match the oracle bit for bit, except that the sign of a NaN
+    byte is not compared: the host's and the device's default NaN differ in
+    sign."""
+    T, H, K, E, P = 64, 1024, 2, 8, 2
+    wl = WORKLOADS["tiny_4x1024"].with_(name="fp8_non_finite", T=T, H=H, K=K, E=E, P=P)
+    d = generate(wl, seed=31)
+    x = d["x"].copy().reshape(T, H // 128, 128)
+    rng = np.random.default_rng(31)
+    NAN, NNAN, INF, NINF = 0x7FC0, 0xFFC0, 0x7F80, 0xFF80
+    for t in range(T):
+        j = rng.integers(0, 128, size=4)
+        x[t, 0, j[0]] = NAN if t % 2 else NNAN       # one NaN among finite values
+        x[t, 1, :] = NAN                             # all NaN
+        x[t, 2, j[1]] = INF                          # one +inf
+        x[t, 3, j[2]] = NINF                         # one -inf
+        x[t, 4, j[0]] = NNAN                         # NaN and inf together
+        x[t, 4, j[3]] = INF if j[3] != j[0] else x[t, 4, j[3]]
+        x[t, 5, :] = 0                               # NaN among zeros: amax 0
+        x[t, 5, j[1]] = NAN
+        x[t, 6, j[2]] = INF                          # +inf and -inf
+        x[t, 6, (j[2] + 1) % 128] = NINF
+    d["x"] = x.reshape(T, H)
+    got = run_gpu(wl, d, fused=fused)
+    ref = run_oracle(wl, d)
+    for k in ("expert_count", "expert_offset", "part_count", "part_offset", "row_of_pair",
+              "src_pair"):
+        np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+    N = int(ref["expert_offset"][E])
+    gx, rx = got["recv_x"][:N].astype(np.int32), ref["recv_x"][:N].astype(np.int32)
+    nan_ref = (rx & 0x7F) == 0x7F
+    assert np.array_equal(nan_ref, (gx & 0x7F) == 0x7F), "NaN bytes at different places"
+    assert np.array_equal(gx[~nan_ref], rx[~nan_ref]), "finite bytes differ"
+    assert nan_ref.any() and (rx[~nan_ref] & 0x7F == 0).any()
+    gs, rs = got["recv_scales"][:N], ref["recv_scales"][:N]
+    both_nan = np.isnan(gs) & np.isnan(rs)
+    assert np.array_equal(gs.view(np.uint32)[~both_nan], rs.view(np.uint32)[~both_nan])
+    assert np.isinf(rs).any() and (rs == 0).any()
+
+
 def test_bound_step_matches_oracle():
     """BoundStep (arguments marshalled once) gives the same outputs as the
     oracle, call after call."""
