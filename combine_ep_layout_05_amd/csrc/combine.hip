@@ -78,7 +78,7 @@ __device__ __forceinline__ uint4 reduce_rows(const uint4 (&v)[kMaxK], int myrow,
 // taken in ascending p), reduces the entries of kmask[t*P+p] into row
 // tp_row[t*P+p] of `out`: every expert row is read once, as in the plain
 // combine, and no wave is spent on (token, partition) couples without a copy.
-template <int kMaxK, bool kStream, int kMode>
+template <int kMaxK, bool kStream, int kMode, bool kOnce>
 __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
     const uint16_t* __restrict__ y, const int32_t* __restrict__ row_of_pair,
     const float* __restrict__ topk_w, int H, int K, uint16_t* __restrict__ out,
@@ -92,8 +92,7 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
     // the XCD that wrote its metadata; streaming regime: launch order (there
     // the contiguous order measured slower, 88 -> 97 us at 4096 x 7168)
     const int block = kStream ? (int)blockIdx.x : xcd_block(blockIdx.x, gridDim.x);
-    for (int item = block * waves + wave_uniform(threadIdx.x / kWave); item < n_items;
-         item += stride) {                   // n_items + stride < 2^31 (checked by the launcher)
+    auto run = [&](int item) {
         const int t = item / steps_per_token;
         const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
         const bool active = col0 < H;
@@ -135,6 +134,13 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
             const uint4 o = reduce_rows<kMaxK>(v, myrow, myw, K, ~0u);
             if (active) store16<kStream>(out + (int64_t)t * H + col0, o);
         }
+    };
+    int item = block * waves + wave_uniform(threadIdx.x / kWave);
+    if constexpr (kOnce) {               // the grid covers every item: no loop
+        if (item < n_items) run(item);
+    } else {
+        for (; item < n_items; item += stride)   // n_items + stride < 2^31 (checked by the launcher)
+            run(item);
     }
 }
 
@@ -175,8 +181,14 @@ hipError_t launch_combine_mode(const uint16_t* y, const int32_t* row_of_pair,
     if (g.max_blocks > 0 && blocks > g.max_blocks) blocks = g.max_blocks;
     if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
     const bool stream_policy = combine_streams(gathered_rows, H);
-    auto k = K <= 8 ? (stream_policy ? combine_kernel<8, true, kMode> : combine_kernel<8, false, kMode>)
-                    : (stream_policy ? combine_kernel<16, true, kMode> : combine_kernel<16, false, kMode>);
+    const bool once = blocks * g.waves >= items;
+    using Kernel = decltype(&combine_kernel<8, true, kMode, true>);
+    const Kernel table[2][2][2] = {
+        {{combine_kernel<8, false, kMode, false>, combine_kernel<8, false, kMode, true>},
+         {combine_kernel<8, true, kMode, false>, combine_kernel<8, true, kMode, true>}},
+        {{combine_kernel<16, false, kMode, false>, combine_kernel<16, false, kMode, true>},
+         {combine_kernel<16, true, kMode, false>, combine_kernel<16, true, kMode, true>}}};
+    const Kernel k = table[K <= 8 ? 0 : 1][stream_policy ? 1 : 0][once ? 1 : 0];
     hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(g.waves * kWave), 0, stream, y, row_of_pair,
                        topk_w, H, K, out, steps, (int)items, n_rows, tp_row, kmask, P, out_rows);
     return hipGetLastError();

@@ -80,7 +80,7 @@ __device__ __forceinline__ uint2 prepare_item(uint4 v, float& scale)
     return make_uint2(0u, 0u);
 }
 
-template <int kPayload, bool kStream>
+template <int kPayload, bool kStream, bool kOnce>
 __global__ __launch_bounds__(kMaxMoveWaves * kWave) void dispatch_kernel(
     const uint16_t* __restrict__ x, int H, int K, const int32_t* __restrict__ row_of_pair,
     uint8_t* __restrict__ recv_x, float* __restrict__ recv_scales,
@@ -104,6 +104,13 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void dispatch_kernel(
     int myrow, col0;
     uint4 v;
     load_item(item, myrow, v, col0);
+    if constexpr (kOnce) {               // the grid covers every item: no prefetch loop
+        float scale;
+        const uint2 q = prepare_item<kPayload>(v, scale);
+        store_item<kPayload, kStream>(v, q, scale, myrow, 0, col0, lane, H, K, n_rows, recv_x,
+                                      recv_scales);
+        return;
+    }
 
     while (true) {
         const int next = item + stride;      // n_items + stride < 2^31 (checked by the launcher)
@@ -477,8 +484,14 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, const int32_t
     if (g.max_blocks > 0 && blocks > g.max_blocks) blocks = g.max_blocks;
     if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
     const bool st = dispatch_streams(T, H, K, payload);
-    auto k = payload == 0 ? (st ? dispatch_kernel<0, true> : dispatch_kernel<0, false>)
-                          : (st ? dispatch_kernel<1, true> : dispatch_kernel<1, false>);
+    const bool once = blocks * g.waves >= items;
+    using Kernel = decltype(&dispatch_kernel<0, true, true>);
+    const Kernel table[2][2][2] = {
+        {{dispatch_kernel<0, false, false>, dispatch_kernel<0, false, true>},
+         {dispatch_kernel<0, true, false>, dispatch_kernel<0, true, true>}},
+        {{dispatch_kernel<1, false, false>, dispatch_kernel<1, false, true>},
+         {dispatch_kernel<1, true, false>, dispatch_kernel<1, true, true>}}};
+    const Kernel k = table[payload == 0 ? 0 : 1][st ? 1 : 0][once ? 1 : 0];
     hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(g.waves * kWave), 0, stream, x, H, K,
                        row_of_pair, (uint8_t*)recv_x, payload == 0 ? recv_scales : nullptr, steps,
                        (int)items, T * K);
