@@ -354,8 +354,10 @@ int oracle_dedup_layout(const int32_t* idx, int T, int K, int E, int P,
 /*
  * Two-level combine, level 1 (at the destination): for every present (t,p),
  * acc = 0.0f, then acc = fmaf(w[t,k], y[row_of_pair[t,k], c], acc) for the k
- * of kmask[t*P+p] in ascending order; partial[tp_row[t,p], c] = bf16_rne(acc).
- * y is in the pair-row layout of the plain dispatch.
+ * of kmask[t*P+p] in ascending order whose row is a receive row (>= 0; a
+ * masked entry contributes nothing, as in the plain combine);
+ * partial[tp_row[t,p], c] = bf16_rne(acc).  y is in the pair-row layout of
+ * the plain dispatch.
  */
 int oracle_combine_partial(const uint16_t* y, const int32_t* row_of_pair, const float* w,
                            const int32_t* tp_row, const uint32_t* kmask,
@@ -373,6 +375,7 @@ int oracle_combine_partial(const uint16_t* y, const int32_t* row_of_pair, const 
                 for (int k = 0; k < K; ++k) {
                     if (!(kmask[i] >> k & 1u)) continue;
                     int32_t r = row_of_pair[(int64_t)t * K + k];
+                    if (r < 0) continue;
                     acc = fmaf(w[(int64_t)t * K + k], oracle_bf16_to_f32(y[(int64_t)r * H + c]), acc);
                 }
                 partial[(int64_t)dst * H + c] = oracle_bf16_rne(acc);

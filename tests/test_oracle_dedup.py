@@ -142,6 +142,29 @@ def test_single_partition_tokens_equal_plain_combine():
     np.testing.assert_array_equal(out[single], plain[single])
 
 
+def test_partial_with_every_entry_is_the_plain_combine():
+    """Level 1 with one copy per token whose mask holds all K entries --
+    masked ones (row -1) included -- is the plain combine: the same fmaf
+    sequence over the entries that have a receive row, masked entries
+    contributing nothing."""
+    wl = WORKLOADS["masked_16384x4096_bf16"].with_(name="partial_all", T=96, H=256)
+    d = generate(wl, seed=5)
+    lo = oracle.layout(d["idx"], wl.E, wl.P)
+    assert (lo["row_of_pair"] < 0).any()
+    # every weight nonzero, and a row of ones just before y in memory, so an
+    # entry with row -1 that were not skipped would change the sums
+    w = np.random.default_rng(5).random((wl.T, wl.K)).astype(np.float32) + 0.5
+    ybig = np.empty((d["y"].shape[0] + 1, wl.H), np.uint16)
+    ybig[0] = 0x3F80
+    ybig[1:] = d["y"]
+    y = ybig[1:]
+    plain = oracle.combine(y, lo["row_of_pair"], w, wl.T, wl.H, wl.K)
+    tp_row = np.arange(wl.T, dtype=np.int32)
+    kmask = np.full(wl.T, (1 << wl.K) - 1, np.uint32)
+    part = oracle.combine_partial(y, lo["row_of_pair"], w, tp_row, kmask, wl.T, wl.H, wl.K, 1)
+    np.testing.assert_array_equal(part, plain)
+
+
 def test_dedup_dispatch_rows_hold_the_token():
     """Dedup dispatch is the plain fp8 dispatch with one row per (token,
     partition): every row carries its token's quantised bytes and scales."""
