@@ -71,6 +71,82 @@ __device__ __forceinline__ uint4 reduce_rows(const uint4 (&v)[kMaxK], int myrow,
     return o;
 }
 
+// Combine level 1 for one item when every entry is in at most one partition's
+// mask: lane k < K holds the entry's receive row `myrow`, weight `myw` and
+// partition `pk` (-1: in no mask), lane p < P the couple's partial row `prow`
+// (-1: no copy).  Entries are ranked by (partition, k); the rows are loaded in
+// that order, so the reduction runs through them once with static register
+// indices, storing a partition's bf16 sum after its last entry.  The fmaf
+// order within a partition is ascending k, as in the general loop.  A copy
+// none of whose entries has a row gets +0, as there.
+template <int kMaxK, bool kStream>
+__device__ __forceinline__ void partial_in_order(const uint16_t* __restrict__ y,
+                                                 uint16_t* __restrict__ out, int H, int col0,
+                                                 bool active, int lane, int myrow, float myw,
+                                                 int pk, int prow)
+{
+    const bool valid = pk >= 0 && myrow >= 0;            // lanes >= K have pk = -1
+    const int key = valid ? (pk << 5) | lane : 0x7FFFFFFF;
+    int rank = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) rank += (read_lane(key, k) < key) ? 1 : 0;
+    const int nv = __builtin_popcountll(__ballot(valid));
+    uint4 v[kMaxK];
+    float w[kMaxK];
+    int part[kMaxK + 1];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        v[j] = make_uint4(0, 0, 0, 0);
+        w[j] = 0.0f;
+        part[j] = -1;
+        if (j < nv) {
+            const int k = __builtin_ctzll(__ballot(valid && rank == j));
+            const int r = read_lane(myrow, k);
+            w[j] = __builtin_bit_cast(float, read_lane(__builtin_bit_cast(int, myw), k));
+            part[j] = read_lane(pk, k);
+            if (active) v[j] = load16<kStream>(y + (int64_t)r * H + col0);
+        }
+    }
+    part[kMaxK] = -1;
+    uint64_t written = 0;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j < nv) {
+            acc[0] = __builtin_fmaf(w[j], bf16_lo(v[j].x), acc[0]);
+            acc[1] = __builtin_fmaf(w[j], bf16_hi(v[j].x), acc[1]);
+            acc[2] = __builtin_fmaf(w[j], bf16_lo(v[j].y), acc[2]);
+            acc[3] = __builtin_fmaf(w[j], bf16_hi(v[j].y), acc[3]);
+            acc[4] = __builtin_fmaf(w[j], bf16_lo(v[j].z), acc[4]);
+            acc[5] = __builtin_fmaf(w[j], bf16_hi(v[j].z), acc[5]);
+            acc[6] = __builtin_fmaf(w[j], bf16_lo(v[j].w), acc[6]);
+            acc[7] = __builtin_fmaf(w[j], bf16_hi(v[j].w), acc[7]);
+            if (j + 1 >= nv || part[j + 1] != part[j]) {     // last entry of this partition
+                const int orow = read_lane(prow, part[j]);
+                uint4 o;
+                o.x = pack2_bf16(acc[0], acc[1]);
+                o.y = pack2_bf16(acc[2], acc[3]);
+                o.z = pack2_bf16(acc[4], acc[5]);
+                o.w = pack2_bf16(acc[6], acc[7]);
+                if (active) store16<kStream>(out + (int64_t)orow * H + col0, o);
+                written |= 1ull << part[j];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+            }
+        }
+    }
+    // copies with no entry that has a row: +0
+    uint64_t empty = __ballot(prow >= 0) & ~written;
+    while (empty) {
+        const int p = __builtin_ctzll(empty);
+        empty &= empty - 1;
+        if (active) store16<kStream>(out + (int64_t)read_lane(prow, p) * H + col0,
+                                     make_uint4(0, 0, 0, 0));
+    }
+}
+
 // An item is (token t, 512-column step).  Its K source rows are
 // row_of_pair[t*K ..] (tp_row with K = P for reduce, weight 1).
 // Plain and reduce write row t of `out`.  Partial loads the token's K expert
@@ -109,6 +185,30 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
                 pmask = kmask[(int64_t)t * P + lane];
             }
             if (prow >= out_rows) prow = -1;
+        }
+
+        if constexpr (kMode == kPartial) {
+            // The entry -> partition map, transposed out of the masks by one
+            // ballot per entry.  When no entry is in two masks (always, for
+            // the masks of ep_dedup_layout), the K rows are loaded in
+            // (partition, k) order and reduced in one pass, closing a
+            // partition's sum at its last entry -- no per-(partition, entry)
+            // tests.  Overlapping masks take the general loop below.
+            int pk = -1;
+            bool overlap = false;
+#pragma unroll
+            for (int k = 0; k < kMaxK; ++k) {
+                if (k < K) {
+                    const uint64_t m = __ballot(prow >= 0 && ((pmask >> k) & 1u));
+                    overlap |= (m & (m - 1)) != 0;
+                    if (lane == k && m != 0) pk = __builtin_ctzll(m);
+                }
+            }
+            if (!overlap) {
+                partial_in_order<kMaxK, kStream>(y, out, H, col0, active, lane, myrow, myw, pk,
+                                                 prow);
+                return;
+            }
         }
 
         uint4 v[kMaxK];

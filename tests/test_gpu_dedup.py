@@ -138,3 +138,57 @@ def test_dedup_empty_batch():
     assert np.all(db.part_tokens.cpu().numpy() == 0)
     assert np.all(db.part_token_offset.cpu().numpy() == 0)
     assert int(db.status.cpu()[0]) == 0
+
+
+@pytest.mark.parametrize("overlap", [False, True])
+def test_combine_partial_hand_built_masks(overlap):
+    """ep_combine_partial on masks built by hand rather than by the dedup
+    layout: present couples with several entries, a single entry, no entry,
+    or only entries whose receive row is -1 (each gets +0), bits at or above
+    K (ignored), and -- with overlap=True -- an entry in two partitions' masks
+    for some tokens (summed into both).  Partial rows of present couples
+    bit-exact against the oracle, absent couples' rows untouched; then the
+    reduce on the same couples."""
+    import torch
+    import combine_ep_layout_05_amd as ep
+    import oracle
+    from tests.pathrun import to_dev
+    T, H, K, P = 53, 1536, 8, 6
+    rng = np.random.default_rng(977 + overlap)
+    n = T * K
+    rop = rng.permutation(n).astype(np.int32)
+    rop[rng.random(n) < 0.1] = -1
+    y = (rng.standard_normal((n, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    w = rng.random((T, K)).astype(np.float32)
+    present = rng.random((T, P)) < 0.6
+    tp_row = np.full((T, P), -1, np.int32)
+    tp_row[present] = rng.permutation(int(present.sum())).astype(np.int32)
+    kmask = np.zeros((T, P), np.uint32)
+    for t in range(T):
+        ps = np.nonzero(present[t])[0]
+        if ps.size == 0:
+            continue
+        owner = rng.choice(ps, size=K)                  # each entry in one present partition
+        for k in range(K):
+            kmask[t, owner[k]] |= np.uint32(1 << k)
+        if t % 5 == 0:
+            kmask[t, ps[0]] = 0                         # a present couple with no entry
+        if t % 7 == 1:
+            kmask[t, ps[-1]] |= np.uint32(1 << K)       # a bit above K: ignored
+        if overlap and t % 3 == 0 and ps.size > 1:
+            kmask[t, ps[1]] |= kmask[t, ps[0]] | np.uint32(1)   # entries in two masks
+    M = int(present.sum())
+    ref = oracle.combine_partial(y, rop, w, tp_row, kmask, T, H, K, P, rows=T * P)
+    part = torch.full((T * P, H), 0x5A5A, dtype=torch.int16, device="cuda")
+    ep.ep_combine_partial(to_dev(y.view(np.int16), torch.bfloat16), to_dev(rop), to_dev(w),
+                          to_dev(tp_row.reshape(-1)), to_dev(kmask.reshape(-1).view(np.int32)), P,
+                          part)
+    torch.cuda.synchronize()
+    got = part.cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got[:M], ref[:M])
+    assert np.all(got[M:] == 0x5A5A)
+    out = torch.full((T, H), 0x5A5A, dtype=torch.int16, device="cuda")
+    ep.ep_combine_reduce(part, to_dev(tp_row.reshape(-1)), T, P, out)
+    torch.cuda.synchronize()
+    want = oracle.combine_reduce(ref, tp_row, T, H, P)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), want)
