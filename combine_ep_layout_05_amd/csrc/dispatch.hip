@@ -447,6 +447,122 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
         src_pair[r] = -1;
 }
 
+// ---------------------------------------------------------------------------
+// Layout fused into the dispatch for tiny batches (T*K <= kTinyPairs).
+//
+// With at most 128 ids every wave holds all of them (two per lane) and ranks
+// its own token's entries by itself: the slot of entry (e, p) is the number
+// of valid entries before it in (expert, entry) order, i.e. the count of keys
+// e'*2^12 + p' below e*2^12 + p -- one ballot and popcount per own entry and
+// round.  No LDS and no barrier stand between the id load and the payload
+// stores, where the general fused kernel spends three barriers and the LDS
+// histogram and scan.  One extra workgroup (launch block 0, dispatched first)
+// builds the per-expert histogram of the same ids in LDS within one wave (its
+// LDS operations complete in program order, so it needs no barrier either)
+// and writes the counts, offsets, partition sums and status.  Outputs are
+// those of the general kernel.
+constexpr int kTinyPairs = 2 * kWave;
+
+template <int kPayload>
+__global__ __launch_bounds__(kMoveThreads) void layout_dispatch_tiny_kernel(
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, int n, int H, int K, int E,
+    int P, int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
+    int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair,
+    uint32_t* __restrict__ status, uint8_t* __restrict__ recv_x, float* __restrict__ recv_scales,
+    int steps_per_token, int n_items)
+{
+    constexpr int kPerLane = kMaxExperts / kWave;          // experts per lane in the scan
+    __shared__ int32_t cnt[kMaxExperts];
+    const int lane = threadIdx.x % kWave;
+    const int w = wave_uniform(threadIdx.x / kWave);
+    // every id, two per lane (addresses clamped, so both loads issue at once)
+    const int p0 = lane, p1 = kWave + lane;
+    const int id0 = idx[p0 < n ? p0 : n - 1];
+    const int id1 = idx[p1 < n ? p1 : n - 1];
+    const bool v0 = p0 < n && id0 >= 0 && id0 < E;
+    const bool v1 = p1 < n && id1 >= 0 && id1 < E;
+
+    if (blockIdx.x == 0) {
+        if (w != 0) return;
+        // counts, offsets, partition sums and status, by one wave
+        const bool bad = (p0 < n && id0 >= E) || (p1 < n && id1 >= E);
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const int e = lane * kPerLane + j;
+            if (e < E) cnt[e] = 0;
+        }
+        if (v0) atomicAdd(&cnt[id0], 1);
+        if (v1) atomicAdd(&cnt[id1], 1);
+        int c[kPerLane], sum = 0;
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const int e = lane * kPerLane + j;
+            c[j] = (e < E) ? cnt[e] : 0;
+            sum += c[j];
+        }
+        const int incl = wave_inclusive_scan(sum);
+        const int N = read_lane(incl, kWave - 1);
+        int o = incl - sum;
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const int e = lane * kPerLane + j;
+            if (e < E) {
+                expert_count[e] = c[j];
+                expert_offset[e] = o;
+                cnt[e] = o;                      // offsets, for the partition sums below
+            }
+            o += c[j];
+        }
+        const int L = E / P;
+        for (int p = lane; p < P; p += kWave) {
+            const int lo = cnt[p * L];
+            const int hi = (p + 1 < P) ? cnt[(p + 1) * L] : N;
+            part_offset[p] = lo;
+            part_count[p] = hi - lo;
+        }
+        const bool anybad = __ballot(bad) != 0;
+        if (lane == 0) {
+            expert_offset[E] = N;
+            part_offset[P] = N;
+            *status = anybad ? 1u : 0u;
+        }
+        return;
+    }
+
+    const int waves = blockDim.x / kWave;
+    const int item = xcd_block(blockIdx.x - 1, gridDim.x - 1) * waves + w;
+    if (item >= n_items) return;
+    const int t = item / steps_per_token;
+    const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (col0 < H) v = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + col0);
+    const int me = (lane < K) ? idx[t * K + lane] : -1;       // this token's entries
+    const uint32_t key0 = v0 ? ((uint32_t)id0 << 12) | (uint32_t)p0 : 0xFFFFFFFFu;
+    const uint32_t key1 = v1 ? ((uint32_t)id1 << 12) | (uint32_t)p1 : 0xFFFFFFFFu;
+    const bool mvalid = lane < K && me >= 0 && me < E;
+    const uint32_t mkey = mvalid ? ((uint32_t)me << 12) | (uint32_t)(t * K + lane) : 0u;
+
+    float scale;
+    const uint2 q = prepare_item<kPayload>(v, scale);
+    int myrow = -1;
+    for (int k = 0; k < K; ++k) {                // slot of entry k: valid keys below its key
+        const uint32_t qk = (uint32_t)read_lane((int)mkey, k);
+        int c = __builtin_popcountll(__ballot(key0 < qk));
+        if (n > kWave) c += __builtin_popcountll(__ballot(key1 < qk));
+        if (lane == k) myrow = c;
+    }
+    if (!mvalid) myrow = -1;
+    store_item<kPayload, false>(v, q, scale, myrow, 0, col0, lane, H, K, n, recv_x, recv_scales);
+
+    if (item == t * steps_per_token && lane < K) {   // the token's first step writes its entries
+        row_of_pair[t * K + lane] = myrow;
+        if (myrow >= 0) src_pair[myrow] = t * K + lane;
+    }
+    const int N = __builtin_popcountll(__ballot(v0)) + __builtin_popcountll(__ballot(v1));
+    for (int r = N + item * kWave + lane; r < n; r += n_items * kWave) src_pair[r] = -1;
+}
+
 __global__ __launch_bounds__(256) void e4m3fn_encode_kernel(const float* __restrict__ in, int64_t n,
                                                             uint8_t* __restrict__ out)
 {
@@ -558,6 +674,15 @@ hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, in
     const int64_t items = (int64_t)T * steps;
     const int n = T * K;
     if (T == 0 || n > kFusedMaxPairs || items > kMaxGridBlocks) return hipErrorInvalidValue;
+    if (n <= kTinyPairs) {
+        const unsigned blocks = (unsigned)((items + kMoveWaves - 1) / kMoveWaves) + 1;
+        auto k = payload == 0 ? layout_dispatch_tiny_kernel<0> : layout_dispatch_tiny_kernel<1>;
+        hipLaunchKernelGGL(k, dim3(blocks), dim3(kMoveThreads), 0, stream, topk_idx, x, n, H, K, E,
+                           P, expert_count, expert_offset, part_count, part_offset, row_of_pair,
+                           src_pair, status, (uint8_t*)recv_x, payload == 0 ? recv_scales : nullptr,
+                           steps, (int)items);
+        return hipGetLastError();
+    }
     const int W = fused_waves(items, steps, K);
     const DedupOutputs none{};
     return payload == 0

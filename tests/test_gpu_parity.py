@@ -70,6 +70,15 @@ FUSED_EDGE = {
     "w8_one_step_8_tokens_per_wg": dict(T=2048, K=1, H=128),
     "w8_two_steps": dict(T=1024, K=2, H=1024),
     "w8_bf16_ragged": dict(payload="bf16", T=200, H=5000 // 8 * 8 + 8),
+    # at most 128 entries: the barrier-free kernel (every wave ranks its own token)
+    "tiny_n1": dict(T=1, K=1),
+    "tiny_n64_one_round": dict(T=8),
+    "tiny_n65_two_rounds_odd_K": dict(T=13, K=5, E=40, P=8),
+    "tiny_n128_K16": dict(T=8, K=16, E=64, P=8),
+    "tiny_E1024": dict(T=4, E=1024, P=8),
+    "tiny_bf16": dict(payload="bf16", T=4, H=1024),
+    "tiny_K3_one_step_tokens": dict(T=40, K=3, H=128),
+    "general_n136": dict(T=17),
 }
 
 
@@ -83,6 +92,20 @@ def test_fused_masked_duplicate_and_bad_ids():
     wl = WORKLOADS["tiny_4x1024"].with_(name="fused_ids", T=40, H=256, E=16, P=4, K=6)
     d = generate(wl, seed=6)
     rng = np.random.default_rng(6)
+    idx = rng.integers(-3, 20, size=(wl.T, wl.K)).astype(np.int32)
+    idx[3] = 7
+    idx[4] = -1
+    d["idx"] = idx
+    got, ref, _ = _case(wl, d=d, fused=True)
+    assert int(got["status"][0]) == 1
+
+
+def test_fused_tiny_masked_duplicate_and_bad_ids():
+    """The barrier-free kernel (T*K <= 128) on masked, repeated and
+    out-of-range ids."""
+    wl = WORKLOADS["tiny_4x1024"].with_(name="fused_tiny_ids", T=20, H=256, E=16, P=4, K=6)
+    d = generate(wl, seed=16)
+    rng = np.random.default_rng(16)
     idx = rng.integers(-3, 20, size=(wl.T, wl.K)).astype(np.int32)
     idx[3] = 7
     idx[4] = -1
