@@ -211,16 +211,56 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
             }
         }
 
-        uint4 v[kMaxK];
+        if constexpr (kMode != kPartial) {
+            // the K rows and weights moved to scalar registers once, then
+            // every row load issued before the first fmaf
+            int rows[kMaxK];
+            float wts[kMaxK];
 #pragma unroll
-        for (int k = 0; k < kMaxK; ++k) {
-            v[k] = make_uint4(0, 0, 0, 0);
-            if (k < K) {
-                const int r = read_lane(myrow, k);
-                if (r >= 0 && active) v[k] = load16<kStream>(y + (int64_t)r * H + col0);
+            for (int k = 0; k < kMaxK; ++k) {
+                rows[k] = (k < K) ? read_lane(myrow, k) : -1;
+                wts[k] = __builtin_bit_cast(float, read_lane(__builtin_bit_cast(int, myw), k));
             }
-        }
-        if constexpr (kMode == kPartial) {
+            uint4 v[kMaxK];
+#pragma unroll
+            for (int k = 0; k < kMaxK; ++k) {
+                v[k] = make_uint4(0, 0, 0, 0);
+                if (rows[k] >= 0 && active) v[k] = load16<kStream>(y + (int64_t)rows[k] * H + col0);
+            }
+            float acc[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kMaxK; ++k) {
+                if (rows[k] >= 0) {
+                    acc[0] = __builtin_fmaf(wts[k], bf16_lo(v[k].x), acc[0]);
+                    acc[1] = __builtin_fmaf(wts[k], bf16_hi(v[k].x), acc[1]);
+                    acc[2] = __builtin_fmaf(wts[k], bf16_lo(v[k].y), acc[2]);
+                    acc[3] = __builtin_fmaf(wts[k], bf16_hi(v[k].y), acc[3]);
+                    acc[4] = __builtin_fmaf(wts[k], bf16_lo(v[k].z), acc[4]);
+                    acc[5] = __builtin_fmaf(wts[k], bf16_hi(v[k].z), acc[5]);
+                    acc[6] = __builtin_fmaf(wts[k], bf16_lo(v[k].w), acc[6]);
+                    acc[7] = __builtin_fmaf(wts[k], bf16_hi(v[k].w), acc[7]);
+                }
+            }
+            uint4 o;
+            o.x = pack2_bf16(acc[0], acc[1]);
+            o.y = pack2_bf16(acc[2], acc[3]);
+            o.z = pack2_bf16(acc[4], acc[5]);
+            o.w = pack2_bf16(acc[6], acc[7]);
+            if (active) store16<kStream>(out + (int64_t)t * H + col0, o);
+        } else {
+            // level 1 with overlapping masks: for each copy in ascending p, the
+            // entries of its mask in ascending k
+            uint4 v[kMaxK];
+#pragma unroll
+            for (int k = 0; k < kMaxK; ++k) {
+                v[k] = make_uint4(0, 0, 0, 0);
+                if (k < K) {
+                    const int r = read_lane(myrow, k);
+                    if (r >= 0 && active) v[k] = load16<kStream>(y + (int64_t)r * H + col0);
+                }
+            }
             uint64_t present = __ballot(prow >= 0);   // lanes < P only: prow is -1 elsewhere
             while (present) {
                 const int p = __builtin_ctzll(present);
@@ -230,9 +270,6 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
                 const uint4 o = reduce_rows<kMaxK>(v, myrow, myw, K, use);
                 if (active) store16<kStream>(out + (int64_t)orow * H + col0, o);
             }
-        } else {
-            const uint4 o = reduce_rows<kMaxK>(v, myrow, myw, K, ~0u);
-            if (active) store16<kStream>(out + (int64_t)t * H + col0, o);
         }
     };
     int item = block * waves + wave_uniform(threadIdx.x / kWave);
