@@ -137,8 +137,9 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void dispatch_kernel(
 // At a few tokens the step is paced by launches and latency, not bytes (MoRI
 // PR #614, view-cache paragraph: latency flat over hidden 1024..6144 and over
 // 4/8/16 tokens).  Here every dispatch workgroup derives, from all T*K ids (at
-// most 8 KB, read from L2), exactly the layout values it needs, so no
-// separate layout launch precedes the dispatch:
+// most 16 KB, read from L2), exactly the layout values it needs, so no
+// separate layout launch precedes the dispatch (up to 128 ids the barrier-free
+// kernel further below takes over):
 //   - the per-expert totals (LDS atomics: integer sums, order-free), and per
 //     expert the number of entries before this workgroup's first token;
 //   - the exclusive scan of the totals (1024 / threads consecutive experts per
