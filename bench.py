@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE EP low-latency dispatch + combine path on one MI355X.
 
-One step = ep_layout -> ep_dispatch -> ep_combine over one batch of seeded
-synthetic inputs already resident in HBM (the expert computation between
+One step = layout -> dispatch -> combine (ep_layout_dispatch, one launch for
+small batches, then ep_combine) over one batch of seeded synthetic inputs
+already resident in HBM (the expert computation between
 dispatch and combine is outside the path; combine reads synthetic expert
 outputs).  Default workload: 128 tokens x hidden 7168, top-8 of 288 experts
 in 16 destination partitions, fp8 e4m3fn dispatch with per-128 scales, bf16
