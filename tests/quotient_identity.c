@@ -6,10 +6,10 @@
  * scale = amax / 448 in IEEE fp32: if scale >= 2^-90, the shortcut
  *     y = 1/scale, q0 = |x|*y, r = fma(-q0, scale, |x|), q = sign(x)*fma(r, y, q0)
  * must give the same OCP e4m3fn byte as the IEEE-rounded quotient x / scale.
- * With argv[3] = 1 the same is checked for y one ulp below and one ulp
- * above RN(1/scale) as well, so any reciprocal within one ulp of the correctly
- * rounded one (a faithful v_rcp_f32, or one refined by a Newton step) gives
- * the same bytes.
+ * argv[3] = -1 or +1 runs the same check with y one ulp below or above
+ * RN(1/scale); passing for -1, 0 and +1 shows that any reciprocal within one
+ * ulp of the correctly rounded one (a faithful v_rcp_f32, or one refined by a
+ * Newton step) gives the same bytes.
  * Prints the pair count and the number of differing bytes; exit status 1 if
  * any byte differs.  argv[1] = stride over amax codes (1 = all), argv[2] = 1
  * to also run the negative x values.
@@ -28,7 +28,7 @@ int main(int argc, char** argv)
 {
     const unsigned stride = argc > 1 ? (unsigned)atoi(argv[1]) : 1u;
     const int negatives = argc > 2 ? atoi(argv[2]) : 0;
-    const int neighbours = argc > 3 ? atoi(argv[3]) : 0;
+    const int yoff = argc > 3 ? atoi(argv[3]) : 0;
     long long pairs = 0, bad = 0, fast_blocks = 0;
     for (uint32_t m = 1; m <= 0x7F7Fu; m += stride) {
         const float amax = from_bf16(m);
@@ -37,24 +37,19 @@ int main(int argc, char** argv)
         ++fast_blocks;
         volatile float one = 1.0f;
         const float yrn = one / scale;
-        const float ys[3] = {yrn, nextafterf(yrn, 0.0f), nextafterf(yrn, INFINITY)};
-        const int ny = neighbours ? 3 : 1;
+        const float y = yoff < 0 ? nextafterf(yrn, 0.0f) : yoff > 0 ? nextafterf(yrn, INFINITY) : yrn;
         for (uint32_t a16 = 0; a16 <= m; ++a16) {
             for (int sg = 0; sg <= negatives; ++sg) {
                 const float x = from_bf16(a16 | (sg ? 0x8000u : 0u));
-                const uint8_t want = oracle_e4m3fn_encode(x / scale);
                 const float a = fabsf(x);
-                for (int v = 0; v < ny; ++v) {
-                    const float y = ys[v];
-                    const float q0 = a * y;
-                    const float r = fmaf(-q0, scale, a);
-                    const float q = copysignf(fmaf(r, y, q0), x);
-                    ++pairs;
-                    if (oracle_e4m3fn_encode(q) != want) {
-                        if (++bad <= 5)
-                            printf("differs: amax=%a x=%a y=%a ieee=%a shortcut=%a\n", amax, x, y,
-                                   x / scale, q);
-                    }
+                const float q0 = a * y;
+                const float r = fmaf(-q0, scale, a);
+                const float q = copysignf(fmaf(r, y, q0), x);
+                ++pairs;
+                if (oracle_e4m3fn_encode(q) != oracle_e4m3fn_encode(x / scale)) {
+                    if (++bad <= 5)
+                        printf("differs: amax=%a x=%a y=%a ieee=%a shortcut=%a\n", amax, x, y,
+                               x / scale, q);
                 }
             }
         }

@@ -60,24 +60,39 @@ def test_round_trip_all_finite_codes():
     np.testing.assert_array_equal(got, codes)
 
 
+def _exhaustive_chunk(b0, b1):
+    """First disagreement in fp32 bit patterns [b0, b1), or None."""
+    bits = np.arange(b0, b1, dtype=np.uint32)
+    v = bits.view(np.float32)
+    got = oracle.e4m3fn_encode(v)
+    ref = table_encode_e4m3fn(v)
+    bad = np.nonzero(got != ref)[0]
+    if bad.size:
+        return ("table", hex(int(bits[bad[0]])), int(got[bad[0]]), int(ref[bad[0]]))
+    m = np.abs(v) <= 464.0
+    tv = torch.from_numpy(v[m]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    bad = np.nonzero(got[m] != tv)[0]
+    if bad.size:
+        return ("torch", hex(int(bits[m][bad[0]])), int(got[m][bad[0]]), int(tv[bad[0]]))
+    return None
+
+
 @pytest.mark.slow
 def test_exhaustive_against_table_and_torch():
     """Every fp32 bit pattern with magnitude in [2^-12, 512): the oracle equals
     the nearest-value table encoder; where |v| <= 464 it also equals torch's
-    float8_e4m3fn cast (which is round-to-nearest-even but not saturating)."""
-    lo = np.float32(2.0 ** -12).view(np.uint32)
-    hi = np.float32(512.0).view(np.uint32)
-    step = 1 << 24
-    for b0 in range(int(lo), int(hi), step):
-        bits = np.arange(b0, min(b0 + step, int(hi)), dtype=np.uint32)
-        v = bits.view(np.float32)
-        got = oracle.e4m3fn_encode(v)
-        ref = table_encode_e4m3fn(v)
-        bad = np.nonzero(got != ref)[0]
-        assert bad.size == 0, (hex(int(bits[bad[0]])), got[bad[0]], ref[bad[0]])
-        m = np.abs(v) <= 464.0
-        tv = torch.from_numpy(v[m]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-        np.testing.assert_array_equal(got[m], tv)
+    float8_e4m3fn cast (which is round-to-nearest-even but not saturating).
+    Chunks run in a few worker processes."""
+    import concurrent.futures
+    import multiprocessing
+    lo = int(np.float32(2.0 ** -12).view(np.uint32))
+    hi = int(np.float32(512.0).view(np.uint32))
+    step = 1 << 23
+    chunks = [(b0, min(b0 + step, hi)) for b0 in range(lo, hi, step)]
+    ctx = multiprocessing.get_context("fork")
+    with concurrent.futures.ProcessPoolExecutor(max_workers=4, mp_context=ctx) as ex:
+        for res in ex.map(_exhaustive_chunk, *zip(*chunks)):
+            assert res is None, res
     # below 2^-12 everything rounds to zero with its sign
     tiny = np.array([2.0 ** -13, 1e-20, 1e-45, 2.0 ** -126], np.float32)
     np.testing.assert_array_equal(oracle.e4m3fn_encode(tiny), np.zeros(4, np.uint8))
