@@ -358,8 +358,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the EP traffic; runs on more than one GPU "
-              "are not part of this build (asked for --gpus %d)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU's share of the EP traffic and runs on one GPU only; "
+              "the multi-GPU exchange is not implemented (asked for --gpus %d)" % args.gpus,
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
