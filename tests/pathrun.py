@@ -24,11 +24,12 @@ def to_dev(a, dtype=None):
     return t.cuda()
 
 
-def run_gpu(wl, d, stream=None, poison=True, fused=False):
+def run_gpu(wl, d, stream=None, poison=True, fused=False, geometry=None):
     """Layout + dispatch + combine on the GPU; returns numpy copies of every output.
-    fused=True runs ep_layout_dispatch instead of ep_layout then ep_dispatch."""
+    fused=True runs ep_layout_dispatch instead of ep_layout then ep_dispatch;
+    geometry is EpBuffers' launch geometry (None: the library default)."""
     ep = gpu_lib()
-    buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload, geometry=geometry)
     if poison:
         buf.recv_x.view(torch.uint8).fill_(POISON_BYTE)
         if buf.recv_scales is not None:

@@ -45,6 +45,24 @@ def test_large_workloads(name):
     _case(wl, wl.seed)
 
 
+BENCH_WORKLOADS = ["ll_128x7168", "sweep_4x6144", "sweep_8x6144", "sweep_16x6144",
+                   "bw_4096x7168_zipf", "masked_16384x4096_bf16"]
+
+
+@pytest.mark.parametrize("name", BENCH_WORKLOADS)
+def test_bench_launch_configuration(name):
+    """Every workload bench.py times, in the launch configuration it times:
+    ep_layout_dispatch then ep_combine with the saved tuned geometry, at full
+    size, against the oracle."""
+    import bench
+    wl = WORKLOADS[name]
+    d = generate(wl, seed=wl.seed)
+    print("bench configuration %s (geometry %s)" % (name, bench.GEOMETRY), flush=True)
+    got = run_gpu(wl, d, fused=True, geometry=bench.GEOMETRY)
+    ref = run_oracle(wl, d)
+    assert compare(wl, got, ref) == 0
+
+
 @pytest.mark.parametrize("name", SMALL + LARGE)
 def test_fused_layout_dispatch(name):
     """ep_layout_dispatch: one launch up to 2048 entries, layout + dispatch
