@@ -59,6 +59,9 @@ MUTANTS = [
     ("dedup level 1 multiply then add",
      "                    acc = fmaf(w[(int64_t)t * K + k], oracle_bf16_to_f32(y[(int64_t)r * H + c]), acc);\n                }\n                partial",
      "                    acc = w[(int64_t)t * K + k] * oracle_bf16_to_f32(y[(int64_t)r * H + c]) + acc;\n                }\n                partial"),
+    ("dedup level 1 keeps masked entries",
+     "                    if (r < 0) continue;\n                    acc = fmaf(w[(int64_t)t * K + k]",
+     "                    if (r < 0) r = 0;\n                    acc = fmaf(w[(int64_t)t * K + k]"),
 ]
 
 BATTERY = [
@@ -85,6 +88,7 @@ BATTERY = [
     lambda: tdd.test_two_level_combine_exact("ll_128x7168"),
     tdd.test_single_partition_tokens_equal_plain_combine,
     tdd.test_reduce_order_hand_worked,
+    tdd.test_partial_with_every_entry_is_the_plain_combine,
 ]
 
 
