@@ -477,16 +477,15 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_tiny_kernel(
     __shared__ int32_t cnt[kMaxExperts];
     const int lane = threadIdx.x % kWave;
     const int w = wave_uniform(threadIdx.x / kWave);
-    // every id, two per lane (addresses clamped, so both loads issue at once)
     const int p0 = lane, p1 = kWave + lane;
-    const int id0 = idx[p0 < n ? p0 : n - 1];
-    const int id1 = idx[p1 < n ? p1 : n - 1];
-    const bool v0 = p0 < n && id0 >= 0 && id0 < E;
-    const bool v1 = p1 < n && id1 >= 0 && id1 < E;
 
     if (blockIdx.x == 0) {
         if (w != 0) return;
         // counts, offsets, partition sums and status, by one wave
+        const int id0 = idx[p0 < n ? p0 : n - 1];
+        const int id1 = idx[p1 < n ? p1 : n - 1];
+        const bool v0 = p0 < n && id0 >= 0 && id0 < E;
+        const bool v1 = p1 < n && id1 >= 0 && id1 < E;
         const bool bad = (p0 < n && id0 >= E) || (p1 < n && id1 >= E);
 #pragma unroll
         for (int j = 0; j < kPerLane; ++j) {
@@ -536,9 +535,15 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_tiny_kernel(
     if (item >= n_items) return;
     const int t = item / steps_per_token;
     const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
+    // all loads issued before any result is used: the x vector, this token's
+    // entries, and every id (two per lane, addresses clamped)
     uint4 v = make_uint4(0, 0, 0, 0);
     if (col0 < H) v = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + col0);
-    const int me = (lane < K) ? idx[t * K + lane] : -1;       // this token's entries
+    const int me = idx[t * K + (lane < K ? lane : 0)];
+    const int id0 = idx[p0 < n ? p0 : n - 1];
+    const int id1 = idx[p1 < n ? p1 : n - 1];
+    const bool v0 = p0 < n && id0 >= 0 && id0 < E;
+    const bool v1 = p1 < n && id1 >= 0 && id1 < E;
     const uint32_t key0 = v0 ? ((uint32_t)id0 << 12) | (uint32_t)p0 : 0xFFFFFFFFu;
     const uint32_t key1 = v1 ? ((uint32_t)id1 << 12) | (uint32_t)p1 : 0xFFFFFFFFu;
     const bool mvalid = lane < K && me >= 0 && me < E;
