@@ -552,11 +552,14 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_tiny_kernel(
     float scale;
     const uint2 q = prepare_item<kPayload>(v, scale);
     int myrow = -1;
-    for (int k = 0; k < K; ++k) {                // slot of entry k: valid keys below its key
-        const uint32_t qk = (uint32_t)read_lane((int)mkey, k);
-        int c = __builtin_popcountll(__ballot(key0 < qk));
-        if (n > kWave) c += __builtin_popcountll(__ballot(key1 < qk));
-        if (lane == k) myrow = c;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {         // slot of entry k: valid keys below its key
+        if (k < K) {
+            const uint32_t qk = (uint32_t)read_lane((int)mkey, k);
+            int c = __builtin_popcountll(__ballot(key0 < qk));
+            if (n > kWave) c += __builtin_popcountll(__ballot(key1 < qk));
+            if (lane == k) myrow = c;
+        }
     }
     if (!mvalid) myrow = -1;
     store_item<kPayload, false>(v, q, scale, myrow, 0, col0, lane, H, K, n, recv_x, recv_scales);
