@@ -286,6 +286,97 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Tiny batches (n <= kTinyLayoutPairs = 128 entries): one wave does it all.
+// A wave's LDS operations complete in program order, so the single-workgroup
+// kernel's barriers are not needed: match-any groups add their sizes to the
+// LDS histogram, a DPP wave scan over the experts (kMaxExperts / 64 per lane)
+// turns it into offsets that stay in LDS as per-expert cursors, and each
+// round's rows are cursor + in-wave rank, the group leaders then moving the
+// cursor past their group.
+constexpr int kTinyLayoutPairs = 2 * kWave;
+
+template <class Entries>
+__global__ __launch_bounds__(kWave) void layout_tiny_kernel(
+    const Entries src, int n, int E, int P,
+    int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
+    int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair,
+    uint32_t* __restrict__ status)
+{
+    constexpr int kPerLane = kMaxExperts / kWave;
+    __shared__ int32_t cur[kMaxExperts];
+    const int lane = threadIdx.x;
+    const int nbits = id_bits(E);
+    bool bad = false;
+    const int e0 = lane < n ? src.load(lane, E, bad) : -1;
+    const int e1 = kWave + lane < n ? src.load(kWave + lane, E, bad) : -1;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const int e = lane * kPerLane + j;
+        if (e < E) cur[e] = 0;
+    }
+    const bool v0 = e0 >= 0 && e0 < E;
+    const bool v1 = e1 >= 0 && e1 < E;
+    const uint64_t peers0 = match_peers(e0, v0, nbits);
+    const uint64_t peers1 = (n > kWave) ? match_peers(e1, v1, nbits) : 0ull;
+    const int rank0 = lanes_below(peers0), rank1 = lanes_below(peers1);
+    if (v0 && rank0 == 0) atomicAdd(&cur[e0], (int)__popcll(peers0));
+    if (v1 && rank1 == 0) atomicAdd(&cur[e1], (int)__popcll(peers1));
+
+    int c[kPerLane], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const int e = lane * kPerLane + j;
+        c[j] = (e < E) ? cur[e] : 0;
+        sum += c[j];
+    }
+    const int incl = wave_inclusive_scan(sum);
+    const int N = read_lane(incl, kWave - 1);
+    int o = incl - sum;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const int e = lane * kPerLane + j;
+        if (e < E) {
+            expert_count[e] = c[j];
+            expert_offset[e] = o;
+            cur[e] = o;                          // per-expert cursor: first free row
+        }
+        o += c[j];
+    }
+    if (part_count) {
+        const int L = E / P;
+        for (int p = lane; p < P; p += kWave) {
+            const int lo = cur[p * L];
+            const int hi = (p + 1 < P) ? cur[(p + 1) * L] : N;
+            part_offset[p] = lo;
+            part_count[p] = hi - lo;
+        }
+    }
+    const bool anybad = __ballot(bad) != 0ull;
+    if (lane == 0) {
+        expert_offset[E] = N;
+        if (part_count) part_offset[P] = N;
+        *status = anybad ? 1u : 0u;
+    }
+
+    // rows: round 0, then its group leaders move the cursors past their
+    // groups (after every lane of the wave has read them), then round 1
+    const int row0 = v0 ? cur[e0] + rank0 : -1;
+    if (v0 && rank0 == 0) cur[e0] = row0 + (int)__popcll(peers0);
+    const int row1 = v1 ? cur[e1] + rank1 : -1;
+    if (lane < n) {
+        row_of_pair[lane] = row0;
+        if (v0 && src_pair) src_pair[row0] = lane;
+    }
+    if (kWave + lane < n) {
+        row_of_pair[kWave + lane] = row1;
+        if (v1 && src_pair) src_pair[row1] = kWave + lane;
+    }
+    if (src_pair)
+        for (int r = N + lane; r < n; r += kWave) src_pair[r] = -1;
+}
+
+// ---------------------------------------------------------------------------
 // Large batches, pass 1: one workgroup per chunk of kChunkPairs entries
 // writes the chunk's histogram into ws_hist[chunk][E] and a bad-id flag into
 // ws_bad[chunk] (ballot-aggregated LDS atomics: a hot expert costs one atomic
@@ -470,6 +561,12 @@ hipError_t launch_layout_entries(const Entries& src, int64_t n, int E, int P,
                                  int32_t* row_of_pair, int32_t* src_pair, uint32_t* status,
                                  void* ws, hipStream_t stream)
 {
+    if (n <= kTinyLayoutPairs) {
+        hipLaunchKernelGGL(layout_tiny_kernel<Entries>, dim3(1), dim3(kWave), 0, stream, src,
+                           (int)n, E, P, expert_count, expert_offset, part_count, part_offset,
+                           row_of_pair, src_pair, status);
+        return hipGetLastError();
+    }
     if (n <= kSmallMaxPairs) {
         hipLaunchKernelGGL(layout_single_kernel<Entries>, dim3(1), dim3(kLayoutThreads), 0, stream,
                            src, n, E, P, expert_count, expert_offset, part_count, part_offset,

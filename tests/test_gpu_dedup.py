@@ -114,8 +114,9 @@ def test_dedup_fused_masked_duplicate_and_bad_ids():
     assert int(got["status"][0]) == 1
 
 
-def test_dedup_masked_duplicate_and_bad_ids():
-    wl = WORKLOADS["tiny_4x1024"].with_(name="dedup_ids", T=40, H=256, E=16, P=4, K=6)
+@pytest.mark.parametrize("T", [40, 20])      # 160 couples; 80: the one-wave layout
+def test_dedup_masked_duplicate_and_bad_ids(T):
+    wl = WORKLOADS["tiny_4x1024"].with_(name="dedup_ids", T=T, H=256, E=16, P=4, K=6)
     d = generate(wl, seed=8)
     rng = np.random.default_rng(8)
     idx = rng.integers(-3, 20, size=(wl.T, wl.K)).astype(np.int32)

@@ -155,8 +155,9 @@ def test_edge_shapes(edge):
     _case(wl, 77)
 
 
-def test_masked_duplicate_and_bad_ids():
-    wl = WORKLOADS["tiny_4x1024"].with_(name="edge_ids", T=40, H=256, E=16, P=4, K=6)
+@pytest.mark.parametrize("T", [40, 20])      # 240 entries; 120: the one-wave layout
+def test_masked_duplicate_and_bad_ids(T):
+    wl = WORKLOADS["tiny_4x1024"].with_(name="edge_ids", T=T, H=256, E=16, P=4, K=6)
     d = generate(wl, seed=5)
     rng = np.random.default_rng(5)
     idx = rng.integers(-3, 20, size=(wl.T, wl.K)).astype(np.int32)   # masks, bad ids >= 16
