@@ -33,6 +33,8 @@
 // item's quantise-and-store work, so each wave keeps one load in flight
 // while its stores drain (the prefetch idea of DeepEP PR #693, with a
 // register double buffer instead of shared-memory TMA staging).
+#include <algorithm>
+#include <numeric>
 #include <type_traits>
 
 #include "ep_device.h"
@@ -572,6 +574,174 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_tiny_kernel(
     for (int r = N + item * kWave + lane; r < n; r += n_items * kWave) src_pair[r] = -1;
 }
 
+// ---------------------------------------------------------------------------
+// Layout fused into the dispatch for medium batches (128 < T*K <= 1024) by
+// counting instead of a histogram.
+//
+// The slot of entry (e, p) is the number of valid entries before it in
+// (expert, entry) order -- keys e*2^12 + p below its own.  Each wave holds
+// its share of the ids (kIds per lane) and counts, for each of the
+// workgroup's own entries, the keys below that entry's with one ballot and
+// popcount per round; one barrier later the waves' counts are summed in LDS.
+// That replaces the general kernel's histogram atomics, scan and three
+// barriers.  Workgroups of kW waves are chosen so none straddles a token when
+// kW divides the 512-column steps per token (7 at hidden 7168: a workgroup
+// holds half a token, its own entries are one token's K), which keeps the
+// counting to K entries.  One extra workgroup (launch block 0, dispatched
+// first) builds the histogram in LDS and writes the counts, offsets,
+// partition sums, status and the src_pair tail.  Outputs are those of the
+// general kernel.
+constexpr int kCountMaxPairs = 1024;
+
+template <int kPayload, int kW, int kOwn>
+__global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, int n, int H, int K, int E,
+    int P, int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
+    int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair,
+    uint32_t* __restrict__ status, uint8_t* __restrict__ recv_x, float* __restrict__ recv_scales,
+    int steps_per_token, int n_items)
+{
+    constexpr int kThreads = kW * kWave;
+    constexpr int kIds = (kCountMaxPairs + kThreads - 1) / kThreads;     // rounds of ids
+    constexpr int kPer = (kMaxExperts + kThreads - 1) / kThreads;        // experts per thread
+    __shared__ int32_t part[kOwn][kW];       // own entry q: keys below it, per wave
+    __shared__ int32_t cnt[kMaxExperts];
+    __shared__ int32_t wsum[kW];
+    __shared__ uint32_t sbad;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int w = wave_uniform(tid / kWave);
+
+    if (blockIdx.x == 0) {
+        // counts, offsets, partition sums, status and the src_pair tail
+        int ids[kIds];
+        bool bad = false;
+#pragma unroll
+        for (int j = 0; j < kIds; ++j) {
+            const int p = j * kThreads + tid;
+            ids[j] = (p < n) ? idx[p] : -1;
+            bad |= (p < n) && ids[j] >= E;
+        }
+        for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
+        if (tid == 0) sbad = 0u;
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < kIds; ++j)
+            if (ids[j] >= 0 && ids[j] < E) atomicAdd(&cnt[ids[j]], 1);
+        if (bad) sbad = 1u;
+        lds_barrier();
+        int c[kPer], sum = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int e = tid * kPer + j;
+            c[j] = (e < E) ? cnt[e] : 0;
+            sum += c[j];
+        }
+        const int incl = wave_inclusive_scan(sum);
+        if (lane == kWave - 1) wsum[w] = incl;
+        lds_barrier();
+        int base = 0, N = 0;
+#pragma unroll
+        for (int u = 0; u < kW; ++u) {
+            const int ws = wsum[u];
+            base += (u < w) ? ws : 0;
+            N += ws;
+        }
+        int o = base + incl - sum;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int e = tid * kPer + j;
+            if (e < E) {
+                expert_count[e] = c[j];
+                expert_offset[e] = o;
+                cnt[e] = o;                  // this thread read cnt[e] above: no other reader
+            }
+            o += c[j];
+        }
+        if (tid == 0) {
+            expert_offset[E] = N;
+            part_offset[P] = N;
+            *status = sbad ? 1u : 0u;
+        }
+        lds_barrier();
+        const int L = E / P;
+        for (int p = tid; p < P; p += kThreads) {
+            const int lo = cnt[p * L];
+            const int hi = (p + 1 < P) ? cnt[(p + 1) * L] : N;
+            part_offset[p] = lo;
+            part_count[p] = hi - lo;
+        }
+        for (int r = N + tid; r < n; r += kThreads) src_pair[r] = -1;
+        return;
+    }
+
+    const int item0 = xcd_block(blockIdx.x - 1, gridDim.x - 1) * kW;
+    const int item = item0 + w;
+    const int last = (item0 + kW - 1 < n_items) ? item0 + kW - 1 : n_items - 1;
+    const int t_lo = item0 / steps_per_token;
+    const int t_hi = last / steps_per_token;
+    const int nq = (t_hi - t_lo + 1) * K;    // own entries, <= kOwn (the launcher's choice)
+    const int p_lo = t_lo * K;
+
+    // every load issued before any result is used: the x vector, the own
+    // entries' ids, this wave's share of all ids (addresses clamped)
+    int t = 0, col0 = H;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (item < n_items) {
+        t = item / steps_per_token;
+        col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
+        if (col0 < H) v = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + col0);
+    }
+    const int me = idx[p_lo + (lane < nq ? lane : 0)];
+    int id[kIds];
+#pragma unroll
+    for (int j = 0; j < kIds; ++j) {
+        const int p = j * kThreads + tid;
+        id[j] = idx[p < n ? p : n - 1];
+    }
+    float scale = 0.0f;
+    uint2 q = make_uint2(0u, 0u);
+    if (item < n_items) q = prepare_item<kPayload>(v, scale);
+    uint32_t key[kIds];
+#pragma unroll
+    for (int j = 0; j < kIds; ++j) {
+        const int p = j * kThreads + tid;
+        key[j] = (p < n && id[j] >= 0 && id[j] < E) ? (((uint32_t)id[j] << 12) | (uint32_t)p)
+                                                     : 0xFFFFFFFFu;
+    }
+    const bool mvalid = lane < nq && me >= 0 && me < E;
+    const uint32_t mkey = mvalid ? (((uint32_t)me << 12) | (uint32_t)(p_lo + lane)) : 0u;
+    int below = 0;
+#pragma unroll
+    for (int j = 0; j < kOwn; ++j) {
+        if (j < nq) {
+            const uint32_t qk = (uint32_t)read_lane((int)mkey, j);
+            int c = 0;
+#pragma unroll
+            for (int r = 0; r < kIds; ++r) c += __builtin_popcountll(__ballot(key[r] < qk));
+            if (lane == j) below = c;
+        }
+    }
+    if (lane < kOwn) part[lane][w] = below;
+    lds_barrier();
+    int myrow = 0;
+#pragma unroll
+    for (int u = 0; u < kW; ++u) myrow += part[lane < kOwn ? lane : 0][u];
+    if (!mvalid) myrow = -1;
+    if (item < n_items)
+        store_item<kPayload, false>(v, q, scale, myrow, (t - t_lo) * K, col0, lane, H, K, n,
+                                    recv_x, recv_scales);
+    if (w == 0 && lane < nq) {
+        const int tt = t_lo + lane / K;
+        if (tt * steps_per_token >= item0) {   // this workgroup holds the token's first step
+            const int p = p_lo + lane;
+            row_of_pair[p] = myrow;
+            if (myrow >= 0) src_pair[myrow] = p;
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void e4m3fn_encode_kernel(const float* __restrict__ in, int64_t n,
                                                             uint8_t* __restrict__ out)
 {
@@ -638,6 +808,21 @@ int max_own_tokens(int W, int steps)
     return m < W ? m : W;
 }
 
+// The same, exactly, for workgroups of W consecutive items out of n_items
+// (workgroup b holds items W*b .. W*b+W-1).
+int max_own_tokens_exact(int W, int steps, int n_items)
+{
+    int most = 0;
+    const int period = (W * steps) / std::gcd(W, steps) / W;   // item0 mod steps repeats
+    const int blocks = (n_items + W - 1) / W;
+    for (int b = 0; b < period && b < blocks; ++b) {
+        const int first = W * b;
+        const int last = std::min(first + W - 1, n_items - 1);
+        most = std::max(most, last / steps - first / steps + 1);
+    }
+    return most;
+}
+
 // Waves per fused workgroup.  Every workgroup redoes the whole histogram, so
 // once 4-wave workgroups would outnumber the 256 CUs, 8-wave ones (half as
 // many) finish sooner: measured at 128 x 7168, 5.8 against 6.1 us per
@@ -691,6 +876,34 @@ hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, in
                            src_pair, status, (uint8_t*)recv_x, payload == 0 ? recv_scales : nullptr,
                            steps, (int)items);
         return hipGetLastError();
+    }
+    if (n <= kCountMaxPairs) {
+        // workgroups of 8, 7 or 6 waves, the largest that divides the steps
+        // per token (a workgroup then holds part of one token, or whole
+        // tokens), else 8; own entries at most 16
+        int W = 8;
+        for (int c = 8; c >= 6; --c)
+            if (steps % c == 0 || c % steps == 0) { W = c; break; }
+        const int own = max_own_tokens_exact(W, steps, (int)items) * K;
+        if (own <= 16) {
+            const unsigned blocks = (unsigned)((items + W - 1) / W) + 1;
+            using Kernel = decltype(&layout_dispatch_count_kernel<0, 8, 8>);
+            Kernel k = nullptr;
+            const bool own8 = own <= 8;
+            if (payload == 0)
+                k = W == 8 ? (own8 ? layout_dispatch_count_kernel<0, 8, 8> : layout_dispatch_count_kernel<0, 8, 16>)
+                  : W == 7 ? (own8 ? layout_dispatch_count_kernel<0, 7, 8> : layout_dispatch_count_kernel<0, 7, 16>)
+                           : (own8 ? layout_dispatch_count_kernel<0, 6, 8> : layout_dispatch_count_kernel<0, 6, 16>);
+            else
+                k = W == 8 ? (own8 ? layout_dispatch_count_kernel<1, 8, 8> : layout_dispatch_count_kernel<1, 8, 16>)
+                  : W == 7 ? (own8 ? layout_dispatch_count_kernel<1, 7, 8> : layout_dispatch_count_kernel<1, 7, 16>)
+                           : (own8 ? layout_dispatch_count_kernel<1, 6, 8> : layout_dispatch_count_kernel<1, 6, 16>);
+            hipLaunchKernelGGL(k, dim3(blocks), dim3(W * kWave), 0, stream, topk_idx, x, n, H, K,
+                               E, P, expert_count, expert_offset, part_count, part_offset,
+                               row_of_pair, src_pair, status, (uint8_t*)recv_x,
+                               payload == 0 ? recv_scales : nullptr, steps, (int)items);
+            return hipGetLastError();
+        }
     }
     const int W = fused_waves(items, steps, K);
     const DedupOutputs none{};

@@ -97,6 +97,15 @@ FUSED_EDGE = {
     "tiny_bf16": dict(payload="bf16", T=4, H=1024),
     "tiny_K3_one_step_tokens": dict(T=40, K=3, H=128),
     "general_n136": dict(T=17),
+    # 128 < T*K <= 1024: the counting kernel (workgroups of 8, 7 or 6 waves)
+    "count_w7_half_token": dict(T=100, H=7168),
+    "count_w6": dict(T=64, H=6144),
+    "count_w8_two_tokens": dict(T=120, H=2048),
+    "count_w8_straddling_11_steps": dict(T=90, H=5632),
+    "count_bf16": dict(payload="bf16", T=64, H=7168),
+    "count_K3_w6_two_tokens": dict(T=300, K=3, H=1536),
+    "count_E1024": dict(T=100, E=1024, P=8, H=7168),
+    "general_just_over_1024": dict(T=129, H=7168),
 }
 
 
@@ -110,6 +119,20 @@ def test_fused_masked_duplicate_and_bad_ids():
     wl = WORKLOADS["tiny_4x1024"].with_(name="fused_ids", T=40, H=256, E=16, P=4, K=6)
     d = generate(wl, seed=6)
     rng = np.random.default_rng(6)
+    idx = rng.integers(-3, 20, size=(wl.T, wl.K)).astype(np.int32)
+    idx[3] = 7
+    idx[4] = -1
+    d["idx"] = idx
+    got, ref, _ = _case(wl, d=d, fused=True)
+    assert int(got["status"][0]) == 1
+
+
+def test_fused_count_masked_duplicate_and_bad_ids():
+    """The counting kernel (128 < T*K <= 1024) on masked, repeated and
+    out-of-range ids."""
+    wl = WORKLOADS["tiny_4x1024"].with_(name="fused_count_ids", T=100, H=7168, E=16, P=4, K=6)
+    d = generate(wl, seed=26)
+    rng = np.random.default_rng(26)
     idx = rng.integers(-3, 20, size=(wl.T, wl.K)).astype(np.int32)
     idx[3] = 7
     idx[4] = -1
