@@ -714,14 +714,12 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(
     const uint32_t mkey = mvalid ? (((uint32_t)me << 12) | (uint32_t)(p_lo + lane)) : 0u;
     int below = 0;
 #pragma unroll
-    for (int j = 0; j < kOwn; ++j) {
-        if (j < nq) {
-            const uint32_t qk = (uint32_t)read_lane((int)mkey, j);
-            int c = 0;
+    for (int j = 0; j < kOwn; ++j) {         // lanes past nq hold key 0: nothing below it
+        const uint32_t qk = (uint32_t)read_lane((int)mkey, j);
+        int c = 0;
 #pragma unroll
-            for (int r = 0; r < kIds; ++r) c += __builtin_popcountll(__ballot(key[r] < qk));
-            if (lane == j) below = c;
-        }
+        for (int r = 0; r < kIds; ++r) c += __builtin_popcountll(__ballot(key[r] < qk));
+        if (lane == j) below = c;
     }
     if (lane < kOwn) part[lane][w] = below;
     lds_barrier();
