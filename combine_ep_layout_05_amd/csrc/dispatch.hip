@@ -466,7 +466,7 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
 // those of the general kernel.
 constexpr int kTinyPairs = 2 * kWave;
 
-template <int kPayload>
+template <int kPayload, int kOwn>
 __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_tiny_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, int n, int H, int K, int E,
     int P, int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
@@ -555,13 +555,11 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_tiny_kernel(
     const uint2 q = prepare_item<kPayload>(v, scale);
     int myrow = -1;
 #pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {         // slot of entry k: valid keys below its key
-        if (k < K) {
-            const uint32_t qk = (uint32_t)read_lane((int)mkey, k);
-            int c = __builtin_popcountll(__ballot(key0 < qk));
-            if (n > kWave) c += __builtin_popcountll(__ballot(key1 < qk));
-            if (lane == k) myrow = c;
-        }
+    for (int k = 0; k < kOwn; ++k) {             // slot of entry k: valid keys below its key
+        const uint32_t qk = (uint32_t)read_lane((int)mkey, k);   // lanes >= K: key 0
+        const int c = __builtin_popcountll(__ballot(key0 < qk)) +
+                      __builtin_popcountll(__ballot(key1 < qk));
+        if (lane == k) myrow = c;
     }
     if (!mvalid) myrow = -1;
     store_item<kPayload, false>(v, q, scale, myrow, 0, col0, lane, H, K, n, recv_x, recv_scales);
@@ -868,7 +866,8 @@ hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, in
     if (T == 0 || n > kFusedMaxPairs || items > kMaxGridBlocks) return hipErrorInvalidValue;
     if (n <= kTinyPairs) {
         const unsigned blocks = (unsigned)((items + kMoveWaves - 1) / kMoveWaves) + 1;
-        auto k = payload == 0 ? layout_dispatch_tiny_kernel<0> : layout_dispatch_tiny_kernel<1>;
+        auto k = payload == 0 ? (K <= 8 ? layout_dispatch_tiny_kernel<0, 8> : layout_dispatch_tiny_kernel<0, 16>)
+                              : (K <= 8 ? layout_dispatch_tiny_kernel<1, 8> : layout_dispatch_tiny_kernel<1, 16>);
         hipLaunchKernelGGL(k, dim3(blocks), dim3(kMoveThreads), 0, stream, topk_idx, x, n, H, K, E,
                            P, expert_count, expert_offset, part_count, part_offset, row_of_pair,
                            src_pair, status, (uint8_t*)recv_x, payload == 0 ? recv_scales : nullptr,
