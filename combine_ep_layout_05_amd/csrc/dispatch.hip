@@ -612,14 +612,20 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(
     const int w = wave_uniform(tid / kWave);
 
     if (blockIdx.x == 0) {
-        // counts, offsets, partition sums, status and the src_pair tail
+        // counts, offsets, partition sums, status and the src_pair tail (the id
+        // loads all issued first: addresses clamped rather than guarded)
         int ids[kIds];
         bool bad = false;
 #pragma unroll
         for (int j = 0; j < kIds; ++j) {
             const int p = j * kThreads + tid;
-            ids[j] = (p < n) ? idx[p] : -1;
-            bad |= (p < n) && ids[j] >= E;
+            ids[j] = idx[p < n ? p : n - 1];
+        }
+#pragma unroll
+        for (int j = 0; j < kIds; ++j) {
+            const int p = j * kThreads + tid;
+            if (p >= n) ids[j] = -1;
+            bad |= ids[j] >= E;
         }
         for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
         if (tid == 0) sbad = 0u;
