@@ -589,16 +589,45 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_tiny_kernel(
 // first) builds the histogram in LDS and writes the counts, offsets,
 // partition sums, status and the src_pair tail.  Outputs are those of the
 // general kernel.
+//
+// The per-destination (dedup) variant needs every workgroup to hold part of
+// exactly one token and K to divide 64 (a token's entries are then K aligned
+// lanes of one wave, in every round).  An entry counts its token once for its
+// partition when no lower entry of the token has the same partition (a DPP
+// prefix OR over the K-lane group): it adds 1 to the partition's token total
+// in LDS, and to the total before this workgroup's token when its token comes
+// earlier.  The counters are cleared behind one extra barrier while the loads
+// are in flight, and the barrier above makes the sums visible.  The couple
+// rows are the partition offsets (a wave scan of the totals) plus the tokens
+// before; the payload goes once to each of them.  Block 0 also writes the
+// per-partition token totals and offsets and the tp_src tail.
 constexpr int kCountMaxPairs = 1024;
 
-template <int kPayload, int kW, int kOwn>
+// Within each aligned group of K consecutive lanes (K = 1, 2, 4, 8 or 16,
+// so a group lies inside one 16-lane DPP row): the OR of v over the group's
+// lanes below this one (0 for the group's first lane).  Inclusive steps
+// row_shr 1, 2, 4, 8 taken only from sources inside the group, then one more
+// row_shr 1 for the exclusive value.
+__device__ __forceinline__ uint32_t group_excl_or(uint32_t v, int K, int lane)
+{
+    const int r = lane & (K - 1);            // position in the group
+    int x = (int)v;
+    if (K >= 2) { const int y = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false); x |= r >= 1 ? y : 0; }
+    if (K >= 4) { const int y = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false); x |= r >= 2 ? y : 0; }
+    if (K >= 8) { const int y = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false); x |= r >= 4 ? y : 0; }
+    if (K >= 16) { const int y = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false); x |= r >= 8 ? y : 0; }
+    const int y = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);        // row_shr:1
+    return r >= 1 ? (uint32_t)y : 0u;
+}
+
+template <int kPayload, bool kDedup, int kW, int kOwn>
 __global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, int n, int H, int K, int E,
     int P, int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
     int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair,
     uint32_t* __restrict__ status, uint8_t* __restrict__ recv_x, float* __restrict__ recv_scales,
-    int steps_per_token, int n_items)
+    int steps_per_token, int n_items, DedupOutputs dd)
 {
     constexpr int kThreads = kW * kWave;
     constexpr int kIds = (kCountMaxPairs + kThreads - 1) / kThreads;     // rounds of ids
@@ -607,9 +636,35 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t wsum[kW];
     __shared__ uint32_t sbad;
+    // dedup, per partition: tokens with an expert in it (all / before the workgroup's)
+    __shared__ int32_t ptok[kDedup ? 2 : 1][kDedup ? kMaxTopK : 1];
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int w = wave_uniform(tid / kWave);
+
+    // dedup: partition of expert e, e / L = (e * magic) >> 20, exact for
+    // e < 1024 and L <= 1024 (the multiply-shift bound worked in the general
+    // kernel)
+    auto partition_of = [&](int e) {
+        const uint32_t magic = (1u << 20) / (uint32_t)(E / P) + 1u;
+        return ((uint32_t)e * magic) >> 20;
+    };
+    // dedup: each valid entry that is its token's first in its partition adds
+    // the token to that partition's total (and to the total before this
+    // workgroup's token when its entries lie below p_lo)
+    auto count_tokens = [&](const int (&ids)[kIds], int p_lo) {
+#pragma unroll
+        for (int j = 0; j < kIds; ++j) {
+            const bool ok = ids[j] >= 0 && ids[j] < E;
+            const uint32_t pp = partition_of(ids[j]);
+            const uint32_t bit = ok ? 1u << pp : 0u;
+            const uint32_t lower = group_excl_or(bit, K, lane);   // every lane: DPP sources
+            if (ok && !(lower & bit)) {
+                atomicAdd(&ptok[0][pp], 1);
+                if (j * kThreads + tid < p_lo) atomicAdd(&ptok[1][pp], 1);
+            }
+        }
+    };
 
     if (blockIdx.x == 0) {
         // counts, offsets, partition sums, status and the src_pair tail (the id
@@ -629,12 +684,28 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(
         }
         for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
         if (tid == 0) sbad = 0u;
+        if constexpr (kDedup) {
+            if (tid < kMaxTopK) ptok[0][tid] = 0;
+        }
         lds_barrier();
 #pragma unroll
         for (int j = 0; j < kIds; ++j)
             if (ids[j] >= 0 && ids[j] < E) atomicAdd(&cnt[ids[j]], 1);
         if (bad) sbad = 1u;
+        if constexpr (kDedup) count_tokens(ids, 0);
         lds_barrier();
+        if constexpr (kDedup) {
+            // tokens per partition and their offsets; couple rows from M on are empty
+            const int dtot = lane < P ? ptok[0][lane] : 0;
+            const int pincl = wave_inclusive_scan(dtot);
+            const int M = read_lane(pincl, P - 1);
+            if (w == 0 && lane < P) {
+                dd.part_tokens[lane] = dtot;
+                dd.part_token_offset[lane] = pincl - dtot;
+                if (lane == P - 1) dd.part_token_offset[P] = M;
+            }
+            for (int r = M + tid; r < (n / K) * P; r += kThreads) dd.tp_src[r] = -1;
+        }
         int c[kPer], sum = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -704,6 +775,10 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(
         const int p = j * kThreads + tid;
         id[j] = idx[p < n ? p : n - 1];
     }
+    if constexpr (kDedup) {                  // while the loads are in flight
+        if (tid < 2 * kMaxTopK) ptok[tid / kMaxTopK][tid % kMaxTopK] = 0;
+        lds_barrier();
+    }
     float scale = 0.0f;
     uint2 q = make_uint2(0u, 0u);
     if (item < n_items) q = prepare_item<kPayload>(v, scale);
@@ -711,8 +786,8 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
         const int p = j * kThreads + tid;
-        key[j] = (p < n && id[j] >= 0 && id[j] < E) ? (((uint32_t)id[j] << 12) | (uint32_t)p)
-                                                     : 0xFFFFFFFFu;
+        if (p >= n) id[j] = -1;
+        key[j] = (id[j] >= 0 && id[j] < E) ? (((uint32_t)id[j] << 12) | (uint32_t)p) : 0xFFFFFFFFu;
     }
     const bool mvalid = lane < nq && me >= 0 && me < E;
     const uint32_t mkey = mvalid ? (((uint32_t)me << 12) | (uint32_t)(p_lo + lane)) : 0u;
@@ -726,14 +801,37 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(
         if (lane == j) below = c;
     }
     if (lane < kOwn) part[lane][w] = below;
+    if constexpr (kDedup) count_tokens(id, p_lo);
     lds_barrier();
     int myrow = 0;
 #pragma unroll
     for (int u = 0; u < kW; ++u) myrow += part[lane < kOwn ? lane : 0][u];
     if (!mvalid) myrow = -1;
-    if (item < n_items)
-        store_item<kPayload, false>(v, q, scale, myrow, (t - t_lo) * K, col0, lane, H, K, n,
-                                    recv_x, recv_scales);
+    if constexpr (kDedup) {
+        // couple (t, lane) for lanes < P: the workgroup holds one token, t_lo
+        const int dtot = lane < P ? ptok[0][lane] : 0;
+        const int dbef = lane < P ? ptok[1][lane] : 0;
+        const int pincl = wave_inclusive_scan(dtot);
+        const int mpart = mvalid ? (int)partition_of(me) : -1;
+        uint32_t m = 0u;                     // top-k mask of the couple
+#pragma unroll
+        for (int k = 0; k < kOwn; ++k)
+            if (read_lane(mpart, k) == lane) m |= 1u << k;
+        const int drow = (lane < P && m != 0u) ? pincl - dtot + dbef : -1;
+        if (item < n_items)
+            store_item<kPayload, false>(v, q, scale, drow, 0, col0, lane, H, P, (n / K) * P,
+                                        recv_x, recv_scales);
+        if (w == 1 && lane < P && t_lo * steps_per_token == item0) {   // the token's first workgroup
+            const int j = t_lo * P + lane;
+            dd.tp_row[j] = drow;
+            dd.kmask[j] = m;
+            if (drow >= 0) dd.tp_src[drow] = j;
+        }
+    } else {
+        if (item < n_items)
+            store_item<kPayload, false>(v, q, scale, myrow, (t - t_lo) * K, col0, lane, H, K, n,
+                                        recv_x, recv_scales);
+    }
     if (w == 0 && lane < nq) {
         const int tt = t_lo + lane / K;
         if (tt * steps_per_token >= item0) {   // this workgroup holds the token's first step
@@ -857,6 +955,33 @@ hipError_t launch_fused(int W, const int32_t* topk_idx, const uint16_t* x, int n
     return hipGetLastError();
 }
 
+// The counting kernel's instance for a payload, workgroup size (8, 7 or 6
+// waves) and own-entry bound (8 or 16); one extra workgroup, launch block 0.
+template <bool kDedup>
+hipError_t launch_count(int payload, int W, bool own8, const int32_t* topk_idx, const uint16_t* x,
+                        int n, int H, int K, int E, int P, int32_t* expert_count,
+                        int32_t* expert_offset, int32_t* part_count, int32_t* part_offset,
+                        int32_t* row_of_pair, int32_t* src_pair, uint32_t* status, void* recv_x,
+                        float* recv_scales, int steps, int items, const DedupOutputs& dd,
+                        hipStream_t stream)
+{
+    using Kernel = decltype(&layout_dispatch_count_kernel<0, kDedup, 8, 8>);
+    const Kernel table[2][3][2] = {
+        {{layout_dispatch_count_kernel<0, kDedup, 8, 8>, layout_dispatch_count_kernel<0, kDedup, 8, 16>},
+         {layout_dispatch_count_kernel<0, kDedup, 7, 8>, layout_dispatch_count_kernel<0, kDedup, 7, 16>},
+         {layout_dispatch_count_kernel<0, kDedup, 6, 8>, layout_dispatch_count_kernel<0, kDedup, 6, 16>}},
+        {{layout_dispatch_count_kernel<1, kDedup, 8, 8>, layout_dispatch_count_kernel<1, kDedup, 8, 16>},
+         {layout_dispatch_count_kernel<1, kDedup, 7, 8>, layout_dispatch_count_kernel<1, kDedup, 7, 16>},
+         {layout_dispatch_count_kernel<1, kDedup, 6, 8>, layout_dispatch_count_kernel<1, kDedup, 6, 16>}}};
+    const Kernel k = table[payload == 0 ? 0 : 1][8 - W][own8 ? 0 : 1];
+    const unsigned blocks = (unsigned)((items + W - 1) / W) + 1;
+    hipLaunchKernelGGL(k, dim3(blocks), dim3(W * kWave), 0, stream, topk_idx, x, n, H, K, E, P,
+                       expert_count, expert_offset, part_count, part_offset, row_of_pair, src_pair,
+                       status, (uint8_t*)recv_x, payload == 0 ? recv_scales : nullptr, steps,
+                       items, dd);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
@@ -888,25 +1013,11 @@ hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, in
         for (int c = 8; c >= 6; --c)
             if (steps % c == 0 || c % steps == 0) { W = c; break; }
         const int own = max_own_tokens_exact(W, steps, (int)items) * K;
-        if (own <= 16) {
-            const unsigned blocks = (unsigned)((items + W - 1) / W) + 1;
-            using Kernel = decltype(&layout_dispatch_count_kernel<0, 8, 8>);
-            Kernel k = nullptr;
-            const bool own8 = own <= 8;
-            if (payload == 0)
-                k = W == 8 ? (own8 ? layout_dispatch_count_kernel<0, 8, 8> : layout_dispatch_count_kernel<0, 8, 16>)
-                  : W == 7 ? (own8 ? layout_dispatch_count_kernel<0, 7, 8> : layout_dispatch_count_kernel<0, 7, 16>)
-                           : (own8 ? layout_dispatch_count_kernel<0, 6, 8> : layout_dispatch_count_kernel<0, 6, 16>);
-            else
-                k = W == 8 ? (own8 ? layout_dispatch_count_kernel<1, 8, 8> : layout_dispatch_count_kernel<1, 8, 16>)
-                  : W == 7 ? (own8 ? layout_dispatch_count_kernel<1, 7, 8> : layout_dispatch_count_kernel<1, 7, 16>)
-                           : (own8 ? layout_dispatch_count_kernel<1, 6, 8> : layout_dispatch_count_kernel<1, 6, 16>);
-            hipLaunchKernelGGL(k, dim3(blocks), dim3(W * kWave), 0, stream, topk_idx, x, n, H, K,
-                               E, P, expert_count, expert_offset, part_count, part_offset,
-                               row_of_pair, src_pair, status, (uint8_t*)recv_x,
-                               payload == 0 ? recv_scales : nullptr, steps, (int)items);
-            return hipGetLastError();
-        }
+        if (own <= 16)
+            return launch_count<false>(payload, W, own <= 8, topk_idx, x, n, H, K, E, P,
+                                       expert_count, expert_offset, part_count, part_offset,
+                                       row_of_pair, src_pair, status, recv_x, recv_scales, steps,
+                                       (int)items, DedupOutputs{}, stream);
     }
     const int W = fused_waves(items, steps, K);
     const DedupOutputs none{};
@@ -933,8 +1044,19 @@ hipError_t launch_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t*
     const int n = T * K;
     if (T == 0 || n > kFusedMaxPairs || P > kMaxTopK || items > kMaxGridBlocks)
         return hipErrorInvalidValue;
-    const int W = fused_waves(items, steps, K);
     const DedupOutputs dd{tp_row, part_tokens, part_token_offset, tp_src, kmask};
+    if (n <= kCountMaxPairs && (K & (K - 1)) == 0) {
+        // the counting kernel: every workgroup inside one token (8, 7 or 6
+        // waves dividing the steps per token), a token's K entries on K
+        // aligned lanes (K a power of two, so K divides 64)
+        for (int W = 8; W >= 6; --W)
+            if (steps % W == 0)
+                return launch_count<true>(payload, W, K <= 8, topk_idx, x, n, H, K, E, P,
+                                          expert_count, expert_offset, part_count, part_offset,
+                                          row_of_pair, src_pair, status, recv_x, recv_scales,
+                                          steps, (int)items, dd, stream);
+    }
+    const int W = fused_waves(items, steps, K);
     return payload == 0
         ? launch_fused<0, true>(W, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
                                 part_count, part_offset, row_of_pair, src_pair, status, recv_x,

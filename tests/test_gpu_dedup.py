@@ -92,6 +92,18 @@ FUSED_EDGE = {
     "bf16": dict(payload="bf16", T=50, H=512),
     "w8_K16_T128": dict(T=128, K=16, E=64, P=16, H=7168),
     "w8_two_steps": dict(T=1024, K=2, H=1024),
+    # T*K <= 1024, K a power of two, 8/7/6 waves dividing the steps per token:
+    # the counting kernel (one token per workgroup)
+    "count_T1": dict(T=1, H=7168),
+    "count_w7_P1": dict(T=100, H=7168, E=32, P=1),
+    "count_w6_K16_P16": dict(T=64, K=16, E=64, P=16, H=6144),
+    "count_w8_K4": dict(T=256, K=4, E=64, P=8, H=4096),
+    "count_w6_K1": dict(T=500, K=1, E=32, P=4, H=3072),
+    "count_w7_K2_E1024_P16": dict(T=300, K=2, E=1024, P=16, H=3584),
+    "count_E1024_P1": dict(T=40, E=1024, P=1, H=3584),
+    "count_P3": dict(T=100, E=96, P=3, H=7168),
+    "count_ragged_H6016": dict(T=60, H=6016),         # 12 steps, the last one 384 columns
+    "count_bf16": dict(payload="bf16", T=64, H=6144),
 }
 
 
@@ -101,8 +113,9 @@ def test_dedup_layout_dispatch_edges(edge):
     _case(wl, 80, fused=True)
 
 
-def test_dedup_fused_masked_duplicate_and_bad_ids():
-    wl = WORKLOADS["tiny_4x1024"].with_(name="dedup_fused_ids", T=40, H=256, E=16, P=4, K=6)
+@pytest.mark.parametrize("K,H", [(6, 256), (8, 3584)])    # general kernel; counting kernel
+def test_dedup_fused_masked_duplicate_and_bad_ids(K, H):
+    wl = WORKLOADS["tiny_4x1024"].with_(name="dedup_fused_ids", T=40, H=H, E=16, P=4, K=K)
     d = generate(wl, seed=9)
     rng = np.random.default_rng(9)
     idx = rng.integers(-3, 20, size=(wl.T, wl.K)).astype(np.int32)
