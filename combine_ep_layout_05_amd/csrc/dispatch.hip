@@ -751,37 +751,48 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(
         return;
     }
 
-    const int item0 = xcd_block(blockIdx.x - 1, gridDim.x - 1) * kW;
-    const int item = item0 + w;
-    const int last = (item0 + kW - 1 < n_items) ? item0 + kW - 1 : n_items - 1;
-    const int t_lo = item0 / steps_per_token;
-    const int t_hi = last / steps_per_token;
-    const int nq = (t_hi - t_lo + 1) * K;    // own entries, <= kOwn (the launcher's choice)
-    const int p_lo = t_lo * K;
-
-    // every load issued before any result is used: the x vector, the own
-    // entries' ids, this wave's share of all ids (addresses clamped)
-    int t = 0, col0 = H;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (item < n_items) {
-        t = item / steps_per_token;
-        col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
-        if (col0 < H) v = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + col0);
-    }
-    const int me = idx[p_lo + (lane < nq ? lane : 0)];
+    // every load issued before any result is used, the ids first (they need
+    // no index arithmetic): this wave's share of all ids (addresses clamped;
+    // they come from L2), then the own entries' ids and the x vector.  Loads
+    // complete in issue order, so the counting below runs while x is still in
+    // flight; the quantise follows.  The x load is unconditional (its address
+    // clamped into x, the value unused where the item or the column is out of
+    // range): a load under a branch would make the wait for the ids include it.
     int id[kIds];
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
         const int p = j * kThreads + tid;
         id[j] = idx[p < n ? p : n - 1];
     }
+    const int item0 = xcd_block(blockIdx.x - 1, gridDim.x - 1) * kW;
+    const int item = item0 + w;
+    const int last = (item0 + kW - 1 < n_items) ? item0 + kW - 1 : n_items - 1;
+    const int t_lo = item0 / steps_per_token;
+    const int r_lo = item0 - t_lo * steps_per_token;
+    // token and step of item item0 + d (d < kW): one division for the
+    // workgroup, then at most kW uniform subtractions
+    auto token_of = [&](int d, int& r) {
+        int tt = t_lo;
+        r = r_lo + d;
+        while (r >= steps_per_token) { r -= steps_per_token; ++tt; }
+        return tt;
+    };
+    int r_hi;
+    const int t_hi = token_of(last - item0, r_hi);
+    const int nq = (t_hi - t_lo + 1) * K;    // own entries, <= kOwn (the launcher's choice)
+    const int p_lo = t_lo * K;
+    const int me = idx[p_lo + (lane < nq ? lane : 0)];
+    int t = 0, col0 = H;
+    if (item < n_items) {
+        int r;
+        t = token_of(w, r);
+        col0 = r * kStepCols + lane * kColsPerLane;
+    }
+    const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + (col0 < H ? col0 : 0));
     if constexpr (kDedup) {                  // while the loads are in flight
         if (tid < 2 * kMaxTopK) ptok[tid / kMaxTopK][tid % kMaxTopK] = 0;
         lds_barrier();
     }
-    float scale = 0.0f;
-    uint2 q = make_uint2(0u, 0u);
-    if (item < n_items) q = prepare_item<kPayload>(v, scale);
     uint32_t key[kIds];
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
@@ -802,6 +813,9 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(
     }
     if (lane < kOwn) part[lane][w] = below;
     if constexpr (kDedup) count_tokens(id, p_lo);
+    float scale = 0.0f;
+    uint2 q = make_uint2(0u, 0u);
+    if (item < n_items) q = prepare_item<kPayload>(v, scale);
     lds_barrier();
     int myrow = 0;
 #pragma unroll
