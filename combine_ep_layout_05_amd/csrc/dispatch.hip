@@ -537,13 +537,17 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_tiny_kernel(
     if (item >= n_items) return;
     const int t = item / steps_per_token;
     const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
-    // all loads issued before any result is used: the x vector, this token's
-    // entries, and every id (two per lane, addresses clamped)
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (col0 < H) v = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + col0);
-    const int me = idx[t * K + (lane < K ? lane : 0)];
+    // all loads issued before any result is used, the ids first: every id
+    // (two per lane, addresses clamped), this token's entries, then the x
+    // vector -- loads complete in issue order, so the ranking runs while x is
+    // in flight.  The x load is unconditional (column clamped; the values of
+    // columns >= H are never stored, and with fp8 they fill whole 16-lane
+    // scale blocks): a load under a branch would make the wait for the ids
+    // include it.
     const int id0 = idx[p0 < n ? p0 : n - 1];
     const int id1 = idx[p1 < n ? p1 : n - 1];
+    const int me = idx[t * K + (lane < K ? lane : 0)];
+    const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + (col0 < H ? col0 : 0));
     const bool v0 = p0 < n && id0 >= 0 && id0 < E;
     const bool v1 = p1 < n && id1 >= 0 && id1 < E;
     const uint32_t key0 = v0 ? ((uint32_t)id0 << 12) | (uint32_t)p0 : 0xFFFFFFFFu;
@@ -551,8 +555,6 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_tiny_kernel(
     const bool mvalid = lane < K && me >= 0 && me < E;
     const uint32_t mkey = mvalid ? ((uint32_t)me << 12) | (uint32_t)(t * K + lane) : 0u;
 
-    float scale;
-    const uint2 q = prepare_item<kPayload>(v, scale);
     int myrow = -1;
 #pragma unroll
     for (int k = 0; k < kOwn; ++k) {             // slot of entry k: valid keys below its key
@@ -562,6 +564,8 @@ __global__ __launch_bounds__(kMoveThreads) void layout_dispatch_tiny_kernel(
         if (lane == k) myrow = c;
     }
     if (!mvalid) myrow = -1;
+    float scale;
+    const uint2 q = prepare_item<kPayload>(v, scale);
     store_item<kPayload, false>(v, q, scale, myrow, 0, col0, lane, H, K, n, recv_x, recv_scales);
 
     if (item == t * steps_per_token && lane < K) {   // the token's first step writes its entries
