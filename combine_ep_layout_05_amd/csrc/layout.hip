@@ -494,11 +494,23 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
         const int groups = kLayoutThreads / E;
         const int g = tid / E, e = tid - g * E;
         if (g < groups) {
+            // kScanBatch loads in flight per batch (addresses clamped, values
+            // masked: no branch around a load, so one wait covers the batch)
             int tot = 0, bef = 0;
-            for (int c = g; c < nchunks; c += groups) {
-                const int h = ws_hist[(int64_t)c * E + e];
-                tot += h;
-                if (c < chunk) bef += h;
+            for (int cb = g; cb < nchunks; cb += groups * kScanBatch) {
+                int h[kScanBatch];
+#pragma unroll
+                for (int j = 0; j < kScanBatch; ++j) {
+                    const int c = cb + j * groups;
+                    h[j] = ws_hist[(int64_t)(c < nchunks ? c : nchunks - 1) * E + e];
+                }
+#pragma unroll
+                for (int j = 0; j < kScanBatch; ++j) {
+                    const int c = cb + j * groups;
+                    const int v = c < nchunks ? h[j] : 0;
+                    tot += v;
+                    bef += c < chunk ? v : 0;
+                }
             }
             atomicAdd(&s.hist[e], tot);
             atomicAdd(&s.cursor[e], bef);
