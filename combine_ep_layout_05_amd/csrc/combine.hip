@@ -172,20 +172,29 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
         const int t = item / steps_per_token;
         const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
         const bool active = col0 < H;
-        int myrow = (lane < K) ? row_of_pair[(int64_t)t * K + lane] : -1;
-        if (myrow >= n_rows) myrow = -1;     // not a receive row: treated as masked
-        float myw = 0.0f;
-        if constexpr (kMode == kReduce) myw = 1.0f;
-        else myw = (lane < K) ? topk_w[(int64_t)t * K + lane] : 0.0f;
+        // metadata loads without a branch around them (lanes past K or P read
+        // a valid entry, whose value is then dropped): a load under a branch
+        // costs its own wait for the argument pointer and for the data.  One
+        // empty asm statement takes every loaded value as an operand after
+        // all are issued, so the compiler neither sinks a load into the lanes
+        // that use it nor waits for one before issuing the next.
+        const int kl = lane < K ? lane : 0;
+        int myrow = row_of_pair[(int64_t)t * K + kl];
+        float myw = 1.0f;
+        if constexpr (kMode != kReduce) myw = topk_w[(int64_t)t * K + kl];
         int prow = -1;
         uint32_t pmask = 0u;
         if constexpr (kMode == kPartial) {
-            if (lane < P) {
-                prow = tp_row[(int64_t)t * P + lane];
-                pmask = kmask[(int64_t)t * P + lane];
-            }
-            if (prow >= out_rows) prow = -1;
+            const int pl = lane < P ? lane : 0;
+            prow = tp_row[(int64_t)t * P + pl];
+            pmask = kmask[(int64_t)t * P + pl];
         }
+        // (y as an input: its argument load is issued with these too)
+        asm volatile("" : "+v"(myrow), "+v"(myw), "+v"(prow), "+v"(pmask) : "s"(y));
+        if (lane >= K || myrow >= n_rows) myrow = -1;   // past n_rows: treated as masked
+        if (lane >= K) myw = 0.0f;
+        if constexpr (kMode == kPartial)
+            if (lane >= P || prow >= out_rows) { prow = -1; pmask = 0u; }
 
         if constexpr (kMode == kPartial) {
             // The entry -> partition map, transposed out of the masks by one
@@ -213,7 +222,13 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
 
         if constexpr (kMode != kPartial) {
             // the K rows and weights moved to scalar registers once, then
-            // every row load issued before the first fmaf
+            // every row load issued before the first fmaf, in k order.  Plain
+            // mode: no branch around them (a missing row reads row 0 and a
+            // column past H column 0, both in bounds, and the fmaf loop skips
+            // what is not a row), so the loads go out back to back and the
+            // loop waits for them one at a time.  Reduce mode skips absent
+            // couples with a uniform branch instead: most of a token's P
+            // couples are absent when P is large.
             int rows[kMaxK];
             float wts[kMaxK];
 #pragma unroll
@@ -221,11 +236,17 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
                 rows[k] = (k < K) ? read_lane(myrow, k) : -1;
                 wts[k] = __builtin_bit_cast(float, read_lane(__builtin_bit_cast(int, myw), k));
             }
+            const int cl = active ? col0 : 0;
             uint4 v[kMaxK];
 #pragma unroll
             for (int k = 0; k < kMaxK; ++k) {
-                v[k] = make_uint4(0, 0, 0, 0);
-                if (rows[k] >= 0 && active) v[k] = load16<kStream>(y + (int64_t)rows[k] * H + col0);
+                if constexpr (kMode == kReduce) {
+                    v[k] = make_uint4(0, 0, 0, 0);
+                    if (rows[k] >= 0) v[k] = load16<kStream>(y + (int64_t)rows[k] * H + cl);
+                } else {
+                    v[k] = load16<kStream>(y + (int64_t)(rows[k] >= 0 ? rows[k] : 0) * H + cl);
+                }
+                __builtin_amdgcn_sched_barrier(0);      // issue in k order, the fmaf order
             }
             float acc[8];
 #pragma unroll
