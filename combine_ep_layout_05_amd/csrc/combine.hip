@@ -94,18 +94,19 @@ __device__ __forceinline__ void partial_in_order(const uint16_t* __restrict__ y,
     uint4 v[kMaxK];
     float w[kMaxK];
     int part[kMaxK + 1];
+    // the loads in rank order with no branch around them (past nv: row 0;
+    // past H: column 0; both in bounds and unused), so the reduction below
+    // waits for one row at a time
+    const int cl = active ? col0 : 0;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
-        v[j] = make_uint4(0, 0, 0, 0);
-        w[j] = 0.0f;
-        part[j] = -1;
-        if (j < nv) {
-            const int k = __builtin_ctzll(__ballot(valid && rank == j));
-            const int r = read_lane(myrow, k);
-            w[j] = __builtin_bit_cast(float, read_lane(__builtin_bit_cast(int, myw), k));
-            part[j] = read_lane(pk, k);
-            if (active) v[j] = load16<kStream>(y + (int64_t)r * H + col0);
-        }
+        const uint64_t b = __ballot(valid && rank == j);
+        const int k = b ? __builtin_ctzll(b) : 0;
+        const int r = j < nv ? read_lane(myrow, k) : 0;
+        w[j] = __builtin_bit_cast(float, read_lane(__builtin_bit_cast(int, myw), k));
+        part[j] = j < nv ? read_lane(pk, k) : -1;
+        v[j] = load16<kStream>(y + (int64_t)r * H + cl);
+        __builtin_amdgcn_sched_barrier(0);
     }
     part[kMaxK] = -1;
     uint64_t written = 0;
@@ -168,6 +169,8 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
     // the XCD that wrote its metadata; streaming regime: launch order (there
     // the contiguous order measured slower, 88 -> 97 us at 4096 x 7168)
     const int block = kStream ? (int)blockIdx.x : xcd_block(blockIdx.x, gridDim.x);
+    // partial mode: per wave, entry k -> partition of the copy whose mask holds it
+    __shared__ int32_t s_pk[kMode == kPartial ? kMaxMoveWaves : 1][kMaxTopK];
     auto run = [&](int item) {
         const int t = item / steps_per_token;
         const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
@@ -197,23 +200,39 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
             if (lane >= P || prow >= out_rows) { prow = -1; pmask = 0u; }
 
         if constexpr (kMode == kPartial) {
-            // The entry -> partition map, transposed out of the masks by one
-            // ballot per entry.  When no entry is in two masks (always, for
-            // the masks of ep_dedup_layout), the K rows are loaded in
-            // (partition, k) order and reduced in one pass, closing a
-            // partition's sum at its last entry -- no per-(partition, entry)
-            // tests.  Overlapping masks take the general loop below.
-            int pk = -1;
-            bool overlap = false;
-#pragma unroll
-            for (int k = 0; k < kMaxK; ++k) {
-                if (k < K) {
-                    const uint64_t m = __ballot(prow >= 0 && ((pmask >> k) & 1u));
-                    overlap |= (m & (m - 1)) != 0;
-                    if (lane == k && m != 0) pk = __builtin_ctzll(m);
-                }
-            }
+            // When no entry is in two masks (always, for the masks of
+            // ep_dedup_layout) the K rows are loaded in (partition, k) order
+            // and reduced in one pass, closing a partition's sum at its last
+            // entry; overlapping masks take the general loop below.  The
+            // masks overlap unless their popcounts add up to the popcount of
+            // their OR, both reduced over the couple lanes p < P <= 16 (one
+            // DPP row: the butterfly leaves the row's total in every lane).
+            // The entry -> partition map is then transposed through LDS: each
+            // couple lane writes its partition into the slot of every entry
+            // of its mask, and lane k reads slot k back -- one wave's LDS
+            // operations complete in program order, so no barrier is needed.
+            const uint32_t kbits = (uint32_t)((1ull << K) - 1ull);
+            uint32_t m = prow >= 0 ? (pmask & kbits) : 0u;
+            int orv = (int)m, cnt = __builtin_popcount(m);
+            orv |= __builtin_amdgcn_update_dpp(0, orv, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+            cnt += __builtin_amdgcn_update_dpp(0, cnt, 0xB1, 0xF, 0xF, false);
+            orv |= __builtin_amdgcn_update_dpp(0, orv, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+            cnt += __builtin_amdgcn_update_dpp(0, cnt, 0x4E, 0xF, 0xF, false);
+            orv |= __builtin_amdgcn_update_dpp(0, orv, 0x141, 0xF, 0xF, false);   // row_half_mirror
+            cnt += __builtin_amdgcn_update_dpp(0, cnt, 0x141, 0xF, 0xF, false);
+            orv |= __builtin_amdgcn_update_dpp(0, orv, 0x140, 0xF, 0xF, false);   // row_mirror
+            cnt += __builtin_amdgcn_update_dpp(0, cnt, 0x140, 0xF, 0xF, false);
+            const bool overlap =
+                read_lane(cnt, 0) != __builtin_popcount((uint32_t)read_lane(orv, 0));
             if (!overlap) {
+                int32_t* const slot = s_pk[threadIdx.x / kWave];
+                if (lane < kMaxTopK) slot[lane] = -1;
+                while (m) {                       // this couple's entries
+                    const int k = __builtin_ctz(m);
+                    m &= m - 1u;
+                    slot[k] = lane;
+                }
+                const int pk = lane < K ? slot[lane] : -1;
                 partial_in_order<kMaxK, kStream>(y, out, H, col0, active, lane, myrow, myw, pk,
                                                  prow);
                 return;
