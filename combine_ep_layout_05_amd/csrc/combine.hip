@@ -83,7 +83,7 @@ template <int kMaxK, bool kStream>
 __device__ __forceinline__ void partial_in_order(const uint16_t* __restrict__ y,
                                                  uint16_t* __restrict__ out, int H, int col0,
                                                  bool active, int lane, int myrow, float myw,
-                                                 int pk, int prow)
+                                                 int pk, int prow, int4* __restrict__ ord)
 {
     const bool valid = pk >= 0 && myrow >= 0;            // lanes >= K have pk = -1
     const int key = valid ? (pk << 5) | lane : 0x7FFFFFFF;
@@ -97,14 +97,17 @@ __device__ __forceinline__ void partial_in_order(const uint16_t* __restrict__ y,
     // the loads in rank order with no branch around them (past nv: row 0;
     // past H: column 0; both in bounds and unused), so the reduction below
     // waits for one row at a time
+    // The entries in that order through LDS (`ord`, this wave's kMaxTopK
+    // slots): lane k writes its row, weight and partition to slot rank, lane
+    // j reads slot j back (one wave's LDS operations complete in order).
+    if (valid) ord[rank] = make_int4(myrow, __builtin_bit_cast(int, myw), pk, 0);
+    const int4 o = lane < nv ? ord[lane] : make_int4(0, 0, -1, 0);
     const int cl = active ? col0 : 0;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
-        const uint64_t b = __ballot(valid && rank == j);
-        const int k = b ? __builtin_ctzll(b) : 0;
-        const int r = j < nv ? read_lane(myrow, k) : 0;
-        w[j] = __builtin_bit_cast(float, read_lane(__builtin_bit_cast(int, myw), k));
-        part[j] = j < nv ? read_lane(pk, k) : -1;
+        const int r = read_lane(o.x, j);
+        w[j] = __builtin_bit_cast(float, read_lane(o.y, j));
+        part[j] = read_lane(o.z, j);
         v[j] = load16<kStream>(y + (int64_t)r * H + cl);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -113,17 +116,20 @@ __device__ __forceinline__ void partial_in_order(const uint16_t* __restrict__ y,
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    // The fmaf runs for every slot, so no load is sunk into a branch that
+    // uses it (which would issue it last): slots past nv come after every
+    // entry, and what they add is never stored.
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
+        acc[0] = __builtin_fmaf(w[j], bf16_lo(v[j].x), acc[0]);
+        acc[1] = __builtin_fmaf(w[j], bf16_hi(v[j].x), acc[1]);
+        acc[2] = __builtin_fmaf(w[j], bf16_lo(v[j].y), acc[2]);
+        acc[3] = __builtin_fmaf(w[j], bf16_hi(v[j].y), acc[3]);
+        acc[4] = __builtin_fmaf(w[j], bf16_lo(v[j].z), acc[4]);
+        acc[5] = __builtin_fmaf(w[j], bf16_hi(v[j].z), acc[5]);
+        acc[6] = __builtin_fmaf(w[j], bf16_lo(v[j].w), acc[6]);
+        acc[7] = __builtin_fmaf(w[j], bf16_hi(v[j].w), acc[7]);
         if (j < nv) {
-            acc[0] = __builtin_fmaf(w[j], bf16_lo(v[j].x), acc[0]);
-            acc[1] = __builtin_fmaf(w[j], bf16_hi(v[j].x), acc[1]);
-            acc[2] = __builtin_fmaf(w[j], bf16_lo(v[j].y), acc[2]);
-            acc[3] = __builtin_fmaf(w[j], bf16_hi(v[j].y), acc[3]);
-            acc[4] = __builtin_fmaf(w[j], bf16_lo(v[j].z), acc[4]);
-            acc[5] = __builtin_fmaf(w[j], bf16_hi(v[j].z), acc[5]);
-            acc[6] = __builtin_fmaf(w[j], bf16_lo(v[j].w), acc[6]);
-            acc[7] = __builtin_fmaf(w[j], bf16_hi(v[j].w), acc[7]);
             if (j + 1 >= nv || part[j + 1] != part[j]) {     // last entry of this partition
                 const int orow = read_lane(prow, part[j]);
                 uint4 o;
@@ -171,6 +177,8 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
     const int block = kStream ? (int)blockIdx.x : xcd_block(blockIdx.x, gridDim.x);
     // partial mode: per wave, entry k -> partition of the copy whose mask holds it
     __shared__ int32_t s_pk[kMode == kPartial ? kMaxMoveWaves : 1][kMaxTopK];
+    // partial mode: per wave, the entries in (partition, k) order
+    __shared__ int4 s_ord[kMode == kPartial ? kMaxMoveWaves : 1][kMaxTopK];
     auto run = [&](int item) {
         const int t = item / steps_per_token;
         const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
                 }
                 const int pk = lane < K ? slot[lane] : -1;
                 partial_in_order<kMaxK, kStream>(y, out, H, col0, active, lane, myrow, myw, pk,
-                                                 prow);
+                                                 prow, s_ord[threadIdx.x / kWave]);
                 return;
             }
         }
