@@ -94,19 +94,25 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void dispatch_kernel(
     int item = blockIdx.x * waves + wave_uniform(threadIdx.x / kWave);
     if (item >= n_items) return;
 
-    // load stage of one item: row ids (lanes < K) and this lane's 16 bytes of x
+    // load stage of one item: row ids (lanes < K) and this lane's 16 bytes of
+    // x, both loads without a branch around them (lanes past K read entry 0,
+    // columns past H read column 0; the values are dropped)
     auto load_item = [&](int it, int& myrow, uint4& v, int& col0) {
         const int t = it / steps_per_token;
         col0 = (it - t * steps_per_token) * kStepCols + lane * kColsPerLane;
-        myrow = (lane < K) ? row_of_pair[(int64_t)t * K + lane] : -1;
-        v = (col0 < H) ? *reinterpret_cast<const uint4*>(x + (int64_t)t * H + col0)
-                       : make_uint4(0, 0, 0, 0);
+        myrow = row_of_pair[(int64_t)t * K + (lane < K ? lane : 0)];
+        v = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + (col0 < H ? col0 : 0));
     };
 
     int myrow, col0;
     uint4 v;
     load_item(item, myrow, v, col0);
     if constexpr (kOnce) {               // the grid covers every item: no prefetch loop
+        // the row ids pinned where they are loaded, so the compiler does not
+        // sink the load into the lanes < K (with a lazy argument load and a
+        // wait of its own); x is waited for next anyway
+        asm volatile("" : "+v"(myrow));
+        if (lane >= K) myrow = -1;
         float scale;
         const uint2 q = prepare_item<kPayload>(v, scale);
         store_item<kPayload, kStream>(v, q, scale, myrow, 0, col0, lane, H, K, n_rows, recv_x,
@@ -114,11 +120,15 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void dispatch_kernel(
         return;
     }
 
+    if (lane >= K) myrow = -1;
     while (true) {
         const int next = item + stride;      // n_items + stride < 2^31 (checked by the launcher)
         int nrow = -1, ncol0 = 0;
         uint4 nv = make_uint4(0, 0, 0, 0);
-        if (next < n_items) load_item(next, nrow, nv, ncol0);
+        if (next < n_items) {
+            load_item(next, nrow, nv, ncol0);
+            if (lane >= K) nrow = -1;
+        }
 
         float scale;
         const uint2 q = prepare_item<kPayload>(v, scale);
