@@ -861,7 +861,11 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(
                                         recv_x, recv_scales);
     }
     if (w == 0 && lane < nq) {
-        const int tt = t_lo + lane / K;
+        // lane / K for lane < nq <= 16: (lane + 1/2) / K lies at least 1/32
+        // from an integer and the reciprocal's error is below 2^-19, so the
+        // truncated product is exact (a float reciprocal instead of an
+        // integer division in the wave's tail)
+        const int tt = t_lo + (int)(((float)lane + 0.5f) * __builtin_amdgcn_rcpf((float)K));
         if (tt * steps_per_token >= item0) {   // this workgroup holds the token's first step
             const int p = p_lo + lane;
             row_of_pair[p] = myrow;
