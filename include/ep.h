@@ -161,7 +161,9 @@ int ep_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H,
  * even; NaN stays NaN.
  *
  *   expert_out  bf16 bits y [T*K, H] in the receive-row layout of
- *               ep_dispatch (read in place, no staging copy), 16-B aligned.
+ *               ep_dispatch (read in place, no staging copy), 16-B aligned;
+ *               all T*K rows must be readable (for a masked entry the kernel
+ *               reads row 0 instead and does not use it).
  *   topk_w      fp32 [T, K].   out  bf16 bits [T, H], 16-B aligned.
  * Errors: EP_EINVAL for T < 0, H <= 0 or H % 8 != 0, K outside 1..16,
  * T*K >= 2^31, NULL or misaligned pointers when T > 0.
@@ -245,7 +247,9 @@ int ep_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, 
  * acc = fmaf(topk_w[t*K+k], expert_out[r, c], acc).  Rows of absent couples
  * are not written.
  *   expert_out  bf16 [T*K, H] in the receive-row layout of ep_layout (the
- *               per-expert rows the experts computed), 16-B aligned.
+ *               per-expert rows the experts computed), 16-B aligned; all T*K
+ *               rows must be readable (row 0 is read, unused, in place of
+ *               entries without a row).
  *   row_of_pair int32 [T*K] from ep_layout; topk_w fp32 [T, K];
  *   tp_row, kmask from ep_dedup_layout;  partial bf16 [T*P, H], 16-B aligned.
  * Errors: EP_EINVAL for T < 0, K outside 1..16, P outside 1..16, T*K or
