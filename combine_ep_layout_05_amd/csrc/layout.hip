@@ -286,6 +286,75 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Medium batches of plain entries (kTinyLayoutPairs < n <= kCountLayoutPairs):
+// the slot of entry (e, p) is the number of valid entries before it in
+// (expert, entry) order -- keys e*2^12 + p below its own -- counted with
+// ballots, so the ranking spreads over many workgroups instead of one.
+// Launch block 0 builds the histogram (match-any groups into LDS) and writes
+// the counts, offsets, partition sums, status and the src_pair tail; every
+// other workgroup ranks kCountLayoutOwn consecutive entries: each of its 16
+// waves holds one round of the ids (one per lane) and counts, for each own
+// entry, the keys below it with one ballot and popcount; one barrier later
+// wave 0 sums the waves' counts and writes the rows.  Outputs equal those of
+// the single-workgroup kernel.
+constexpr int kCountLayoutPairs = kLayoutThreads;   // one id per thread
+constexpr int kCountLayoutOwn = 8;
+
+__global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
+    const int32_t* __restrict__ idx, int n, int E, int P,
+    int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
+    int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair,
+    uint32_t* __restrict__ status)
+{
+    __shared__ LayoutSmem s;
+    __shared__ int32_t part[kCountLayoutOwn][kLayoutWaves];   // own entry q: keys below, per wave
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int w = wave_uniform(tid / kWave);
+    const int id = idx[tid < n ? tid : n - 1];                 // address clamped, masked below
+
+    if (blockIdx.x == 0) {
+        const int e = tid < n ? id : -1;
+        zero_smem(s, E);
+        lds_barrier();
+        (void)hist_round(e, E, id_bits(E), s.hist);
+        if (e >= E) s.bad = 1u;
+        lds_barrier();
+        finish_counts(tid < E ? s.hist[tid] : 0, E, P, s.bad, s, true, expert_count,
+                      expert_offset, part_count, part_offset, status);
+        lds_barrier();
+        for (int r = s.total + tid; r < n; r += kLayoutThreads) src_pair[r] = -1;
+        return;
+    }
+
+    const int p0 = (int)(blockIdx.x - 1) * kCountLayoutOwn;
+    const int nq = n - p0 < kCountLayoutOwn ? n - p0 : kCountLayoutOwn;
+    const int me = idx[p0 + (lane < nq ? lane : 0)];
+    const uint32_t key = (tid < n && id >= 0 && id < E) ? (((uint32_t)id << 12) | (uint32_t)tid)
+                                                        : 0xFFFFFFFFu;
+    const bool mvalid = lane < nq && me >= 0 && me < E;
+    const uint32_t mkey = mvalid ? (((uint32_t)me << 12) | (uint32_t)(p0 + lane)) : 0u;
+    int below = 0;
+#pragma unroll
+    for (int q = 0; q < kCountLayoutOwn; ++q) {   // lanes past nq hold key 0: nothing below it
+        const uint32_t qk = (uint32_t)read_lane((int)mkey, q);
+        const int c = __builtin_popcountll(__ballot(key < qk));
+        if (lane == q) below = c;
+    }
+    if (lane < kCountLayoutOwn) part[lane][w] = below;
+    lds_barrier();
+    if (w == 0 && lane < nq) {
+        int row = 0;
+#pragma unroll
+        for (int u = 0; u < kLayoutWaves; ++u) row += part[lane][u];
+        if (!mvalid) row = -1;
+        row_of_pair[p0 + lane] = row;
+        if (row >= 0) src_pair[row] = p0 + lane;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Tiny batches (n <= kTinyLayoutPairs = 128 entries): one wave does it all.
 // A wave's LDS operations complete in program order, so the single-workgroup
 // kernel's barriers are not needed: match-any groups add their sizes to the
@@ -578,6 +647,15 @@ hipError_t launch_layout_entries(const Entries& src, int64_t n, int E, int P,
                            (int)n, E, P, expert_count, expert_offset, part_count, part_offset,
                            row_of_pair, src_pair, status);
         return hipGetLastError();
+    }
+    if constexpr (std::is_same_v<Entries, PlainEntries>) {
+        if (n <= kCountLayoutPairs) {
+            const unsigned blocks = (unsigned)((n + kCountLayoutOwn - 1) / kCountLayoutOwn) + 1;
+            hipLaunchKernelGGL(layout_count_kernel, dim3(blocks), dim3(kLayoutThreads), 0, stream,
+                               src.idx, (int)n, E, P, expert_count, expert_offset, part_count,
+                               part_offset, row_of_pair, src_pair, status);
+            return hipGetLastError();
+        }
     }
     if (n <= kSmallMaxPairs) {
         hipLaunchKernelGGL(layout_single_kernel<Entries>, dim3(1), dim3(kLayoutThreads), 0, stream,
