@@ -286,20 +286,20 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Medium batches of plain entries (kTinyLayoutPairs < n <= kCountLayoutPairs):
+// Medium batches of plain entries (kTinyLayoutPairs < n <= kSmallMaxPairs):
 // the slot of entry (e, p) is the number of valid entries before it in
 // (expert, entry) order -- keys e*2^12 + p below its own -- counted with
 // ballots, so the ranking spreads over many workgroups instead of one.
 // Launch block 0 builds the histogram (match-any groups into LDS) and writes
 // the counts, offsets, partition sums, status and the src_pair tail; every
 // other workgroup ranks kCountLayoutOwn consecutive entries: each of its 16
-// waves holds one round of the ids (one per lane) and counts, for each own
-// entry, the keys below it with one ballot and popcount; one barrier later
-// wave 0 sums the waves' counts and writes the rows.  Outputs equal those of
-// the single-workgroup kernel.
-constexpr int kCountLayoutPairs = kLayoutThreads;   // one id per thread
+// waves holds kIds rounds of the ids (one id per lane and round) and counts,
+// for each own entry, the keys below it with one ballot and popcount per
+// round; one barrier later wave 0 sums the waves' counts and writes the rows.
+// Outputs equal those of the single-workgroup kernel.
 constexpr int kCountLayoutOwn = 8;
 
+template <int kIds>
 __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     const int32_t* __restrict__ idx, int n, int E, int P,
     int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
@@ -307,19 +307,32 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     int32_t* __restrict__ row_of_pair, int32_t* __restrict__ src_pair,
     uint32_t* __restrict__ status)
 {
+    static_assert(kIds * kLayoutThreads <= kSmallMaxPairs, "keys hold entries below 2^12");
     __shared__ LayoutSmem s;
     __shared__ int32_t part[kCountLayoutOwn][kLayoutWaves];   // own entry q: keys below, per wave
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int w = wave_uniform(tid / kWave);
-    const int id = idx[tid < n ? tid : n - 1];                 // address clamped, masked below
+    int id[kIds];                                              // addresses clamped, masked below
+#pragma unroll
+    for (int j = 0; j < kIds; ++j) {
+        const int p = j * kLayoutThreads + tid;
+        id[j] = idx[p < n ? p : n - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kIds; ++j)
+        if (j * kLayoutThreads + tid >= n) id[j] = -1;
 
     if (blockIdx.x == 0) {
-        const int e = tid < n ? id : -1;
         zero_smem(s, E);
         lds_barrier();
-        (void)hist_round(e, E, id_bits(E), s.hist);
-        if (e >= E) s.bad = 1u;
+        bool bad = false;
+#pragma unroll
+        for (int j = 0; j < kIds; ++j) {
+            (void)hist_round(id[j], E, id_bits(E), s.hist);
+            bad |= id[j] >= E;
+        }
+        if (bad) s.bad = 1u;
         lds_barrier();
         finish_counts(tid < E ? s.hist[tid] : 0, E, P, s.bad, s, true, expert_count,
                       expert_offset, part_count, part_offset, status);
@@ -331,15 +344,21 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     const int p0 = (int)(blockIdx.x - 1) * kCountLayoutOwn;
     const int nq = n - p0 < kCountLayoutOwn ? n - p0 : kCountLayoutOwn;
     const int me = idx[p0 + (lane < nq ? lane : 0)];
-    const uint32_t key = (tid < n && id >= 0 && id < E) ? (((uint32_t)id << 12) | (uint32_t)tid)
-                                                        : 0xFFFFFFFFu;
+    uint32_t key[kIds];
+#pragma unroll
+    for (int j = 0; j < kIds; ++j)
+        key[j] = (id[j] >= 0 && id[j] < E)
+                     ? (((uint32_t)id[j] << 12) | (uint32_t)(j * kLayoutThreads + tid))
+                     : 0xFFFFFFFFu;
     const bool mvalid = lane < nq && me >= 0 && me < E;
     const uint32_t mkey = mvalid ? (((uint32_t)me << 12) | (uint32_t)(p0 + lane)) : 0u;
     int below = 0;
 #pragma unroll
     for (int q = 0; q < kCountLayoutOwn; ++q) {   // lanes past nq hold key 0: nothing below it
         const uint32_t qk = (uint32_t)read_lane((int)mkey, q);
-        const int c = __builtin_popcountll(__ballot(key < qk));
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < kIds; ++j) c += __builtin_popcountll(__ballot(key[j] < qk));
         if (lane == q) below = c;
     }
     if (lane < kCountLayoutOwn) part[lane][w] = below;
@@ -649,11 +668,12 @@ hipError_t launch_layout_entries(const Entries& src, int64_t n, int E, int P,
         return hipGetLastError();
     }
     if constexpr (std::is_same_v<Entries, PlainEntries>) {
-        if (n <= kCountLayoutPairs) {
+        if (n <= kSmallMaxPairs) {
             const unsigned blocks = (unsigned)((n + kCountLayoutOwn - 1) / kCountLayoutOwn) + 1;
-            hipLaunchKernelGGL(layout_count_kernel, dim3(blocks), dim3(kLayoutThreads), 0, stream,
-                               src.idx, (int)n, E, P, expert_count, expert_offset, part_count,
-                               part_offset, row_of_pair, src_pair, status);
+            hipLaunchKernelGGL(n <= kLayoutThreads ? layout_count_kernel<1> : layout_count_kernel<2>,
+                               dim3(blocks), dim3(kLayoutThreads), 0, stream, src.idx, (int)n, E,
+                               P, expert_count, expert_offset, part_count, part_offset,
+                               row_of_pair, src_pair, status);
             return hipGetLastError();
         }
     }

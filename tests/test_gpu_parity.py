@@ -164,7 +164,10 @@ EDGE = {
     "H640_ragged_step": dict(H=640),
     "H1152": dict(H=1152),
     "E1024": dict(E=1024, P=8, T=64),
-    "single_wg_limit": dict(T=256, H=256),            # 2048 pairs: one layout workgroup
+    "count_layout_n136": dict(T=17, H=256),           # ep_layout by ballot counting, ragged 8
+    "count_layout_n1024_E1024": dict(T=128, H=256, E=1024, P=16),
+    "count_layout_n1032": dict(T=129, H=256),         # two ids per thread
+    "single_wg_limit": dict(T=256, H=256),            # 2048 pairs: the counting layout at its limit
     "just_over_single_wg": dict(T=257, H=256),        # 2056 pairs -> chunked path, ragged chunk
     "chunked_4104": dict(T=513, H=256),
     "chunked_ragged": dict(T=700, H=384, E=96, P=4),
