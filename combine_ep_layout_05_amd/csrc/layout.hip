@@ -27,6 +27,9 @@
 //     workspace; each ranking workgroup derives its chunk's per-expert bases
 //     from all chunk histograms (a separate scan launch only above 256
 //     chunks).
+// Plain entries up to 2048 skip the histogram-and-scan ranks: an entry's
+// slot is the number of valid (expert, entry) keys below its own, counted
+// with ballots by many workgroups at once (layout_count_kernel).
 // Every id is loaded once, up front, and the match-any peers found while
 // building the histogram are reused for the ranks.  Scans use DPP wave scans.
 // No atomic's return value ever decides a slot, so the result is the same on
@@ -236,7 +239,8 @@ __device__ __forceinline__ void finish_counts(int count, int E, int P, uint32_t 
 }
 
 // ---------------------------------------------------------------------------
-// Small batches (T*K <= kSmallMaxPairs): one workgroup does everything.
+// Small batches of dedup couples (T*P <= kSmallMaxPairs): one workgroup does
+// everything (plain entries take the counting kernel below).
 template <class Entries>
 __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(
     const Entries src, int64_t n, int E, int P,
@@ -676,12 +680,13 @@ hipError_t launch_layout_entries(const Entries& src, int64_t n, int E, int P,
                                row_of_pair, src_pair, status);
             return hipGetLastError();
         }
-    }
-    if (n <= kSmallMaxPairs) {
-        hipLaunchKernelGGL(layout_single_kernel<Entries>, dim3(1), dim3(kLayoutThreads), 0, stream,
-                           src, n, E, P, expert_count, expert_offset, part_count, part_offset,
-                           row_of_pair, src_pair, status);
-        return hipGetLastError();
+    } else {
+        if (n <= kSmallMaxPairs) {
+            hipLaunchKernelGGL(layout_single_kernel<Entries>, dim3(1), dim3(kLayoutThreads), 0,
+                               stream, src, n, E, P, expert_count, expert_offset, part_count,
+                               part_offset, row_of_pair, src_pair, status);
+            return hipGetLastError();
+        }
     }
     const int64_t c = num_chunks(n);
     const size_t hist = (size_t)c * E * sizeof(int32_t);
