@@ -672,6 +672,9 @@ hipError_t launch_layout_entries(const Entries& src, int64_t n, int E, int P,
         return hipGetLastError();
     }
     if constexpr (std::is_same_v<Entries, PlainEntries>) {
+        // here n > kTinyLayoutPairs: the counting kernel clamps its id
+        // addresses to n - 1 and must never see the empty batch, whose
+        // topk_idx may be null
         if (n <= kSmallMaxPairs) {
             const unsigned blocks = (unsigned)((n + kCountLayoutOwn - 1) / kCountLayoutOwn) + 1;
             hipLaunchKernelGGL(n <= kLayoutThreads ? layout_count_kernel<1> : layout_count_kernel<2>,
