@@ -100,7 +100,7 @@ def pick(results, incumbent=DEFAULT, margin=None):
 
 
 def confirm(new_samples, old_samples, margin=None):
-    """A/B verdict: adopt the new geometry only if its mean beats the
+    """A/B decision: adopt the new geometry only if its mean beats the
     incumbent's, measured in the same interleaved rounds, by the margin."""
     margin = MARGIN if margin is None else margin
     return beats(score(new_samples), score(old_samples), margin)
