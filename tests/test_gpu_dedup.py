@@ -206,3 +206,21 @@ def test_combine_partial_hand_built_masks(overlap):
     torch.cuda.synchronize()
     want = oracle.combine_reduce(ref, tp_row, T, H, P)
     np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), want)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_dedup_masked_entries_never_use_row0(fused):
+    """The partial combine reads row 0 of the expert outputs for the slots past
+    a token's entries (an in-bounds stand-in) and never stores what they add:
+    with row 0 at +inf and a quarter of the entries masked, partials and
+    outputs still equal the oracle's."""
+    wl = WORKLOADS["tiny_4x1024"].with_(name="dedup_row0_inf", T=40, H=1024, E=64, P=8, K=8)
+    d = generate(wl, seed=32)
+    rng = np.random.default_rng(32)
+    idx = d["idx"].copy()
+    idx[rng.random(idx.shape) < 0.25] = -1
+    d["idx"] = idx
+    y = d["y"].copy()
+    y[0, :] = 0x7F80                                    # bf16 +inf
+    d["y"] = y
+    _case(wl, d=d, fused=fused)

@@ -11,6 +11,7 @@ import sys
 import numpy as np
 import pytest
 
+from tests.helpers import bf16_to_f32
 from tests.pathrun import compare, run_gpu, run_oracle
 from workloads import WORKLOADS, generate
 
@@ -316,3 +317,25 @@ def test_bound_step_matches_oracle():
         bs.step()
         torch.cuda.synchronize()
         assert compare(wl, collect(buf), ref, check_poison=False) == 0
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_masked_entries_never_use_row0(fused):
+    """For a masked entry the combine reads row 0 of the expert outputs (an
+    in-bounds stand-in) and must not add it: row 0 is +inf here, so a token
+    that used it for a masked entry would come out infinite.  Only tokens
+    that own row 0 through a valid entry may be infinite, exactly as in the
+    oracle."""
+    wl = WORKLOADS["tiny_4x1024"].with_(name="row0_inf", T=40, H=1024, E=64, P=8, K=8)
+    d = generate(wl, seed=31)
+    rng = np.random.default_rng(31)
+    idx = d["idx"].copy()
+    idx[rng.random(idx.shape) < 0.25] = -1
+    d["idx"] = idx
+    y = d["y"].copy()
+    y[0, :] = 0x7F80                                    # bf16 +inf
+    d["y"] = y
+    got, ref, _ = _case(wl, d=d, fused=fused)
+    owner = np.nonzero(ref["row_of_pair"] == 0)[0] // wl.K
+    inf_tok = np.nonzero(np.isinf(bf16_to_f32(got["out"])).any(axis=1))[0]
+    assert set(inf_tok.tolist()) <= set(owner.tolist())
