@@ -23,7 +23,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libep_mi355x.so")
 
-EP_OK, EP_EINVAL, EP_ENOTSUP, EP_EHIP = 0, -1, -2, -3
+EP_OK, EP_EINVAL, EP_ENOTSUP, EP_EHIP, EP_ESCRATCH = 0, -1, -2, -3, -4
+EP_NOALLOC_SCRATCH_BYTES = 4 << 20
 EP_PAYLOAD_FP8_E4M3FN, EP_PAYLOAD_BF16 = 0, 1
 EP_STATUS_BAD_EXPERT_ID = 1
 PAYLOADS = {"fp8": EP_PAYLOAD_FP8_E4M3FN, "bf16": EP_PAYLOAD_BF16}
@@ -41,6 +42,7 @@ _SIGS = {
     "ep_combine": ([_P, _P, _P, _I, _I, _I, _P, _P], _I),
     "ep_layout_dispatch": ([_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                             _P, _P, _P], _I),
+    "ep_layout_dispatch_noalloc": ([_P, _P, _I, _I, _I, _I, _I, _I] + [_P] * 10, _I),
     "ep_graph_begin": ([_P], _I),
     "ep_graph_end": ([_P, ctypes.POINTER(_P)], _I),
     "ep_graph_launch": ([_P, _P], _I),
@@ -152,6 +154,22 @@ def ep_layout_dispatch(topk_idx, x, E, P, payload, expert_count, expert_offset, 
         _ptr(topk_idx), _ptr(x), T, H, K, E, P, payload, _ptr(expert_count), _ptr(expert_offset),
         _ptr(part_count), _ptr(part_offset), _ptr(row_of_pair), _ptr(src_pair), _ptr(status),
         _ptr(ws), ws_bytes, _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
+
+
+def ep_layout_dispatch_noalloc(topk_idx, x, E, P, payload, expert_count, expert_offset,
+                               part_count, part_offset, row_of_pair, src_pair, status, recv_x,
+                               recv_scales=None, stream=None):
+    """ep_layout_dispatch with the library's own per-device scratch buffer as
+    the layout workspace: the call allocates nothing (see include/ep.h)."""
+    _dt(topk_idx, torch.int32)
+    _dt(x, torch.bfloat16, torch.int16, torch.uint16)
+    payload = PAYLOADS.get(payload, payload)
+    T, K = topk_idx.shape
+    H = x.shape[1]
+    _check("ep_layout_dispatch_noalloc", _lib.ep_layout_dispatch_noalloc(
+        _ptr(topk_idx), _ptr(x), T, H, K, E, P, payload, _ptr(expert_count), _ptr(expert_offset),
+        _ptr(part_count), _ptr(part_offset), _ptr(row_of_pair), _ptr(src_pair), _ptr(status),
+        _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
 
 
 def ep_combine(expert_out, row_of_pair, topk_w, out, stream=None, geometry=None):

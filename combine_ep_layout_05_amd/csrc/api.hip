@@ -5,6 +5,8 @@
 // call leaves the stream untouched (configuration errors are refused early
 // and loudly, as the tuning CLI of MoRI PR #614 "perf(ep): InterNodeV1LL
 // low-token latency on MI300X + CX7" does for its environment knobs).
+#include <mutex>
+
 #include "ep.h"
 #include "ep_device.h"
 #include "ep_launch.h"
@@ -75,11 +77,38 @@ int ep_dispatch(const uint16_t* x, int T, int H, int K, const int32_t* row_of_pa
                                         (hipStream_t)stream));
 }
 
-int ep_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
-                       int P, int payload, int32_t* expert_count, int32_t* expert_offset,
-                       int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
-                       int32_t* src_pair, uint32_t* status, void* ws, size_t ws_bytes,
-                       void* recv_x, float* recv_scales, void* stream)
+}  // extern "C"
+
+namespace {
+
+// The checks and launches of ep_layout_dispatch, for a workspace ws of
+// ws_bytes (the caller's, or the library's scratch buffer).
+int layout_dispatch_checked(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
+                            int P, int payload, int32_t* expert_count, int32_t* expert_offset,
+                            int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
+                            int32_t* src_pair, uint32_t* status, void* ws, size_t ws_bytes,
+                            void* recv_x, float* recv_scales, void* stream)
+{
+    const size_t need = ep::layout_workspace_bytes(T, K, E);
+    if (need > 0 && (ws_bytes < need || !ptr_ok(ws, 16))) return EP_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (T > 0 && ep::fused_layout_dispatch_fits(T, H, K))
+        return from_hip(ep::launch_layout_dispatch(topk_idx, x, T, H, K, E, P, payload, expert_count,
+                                                   expert_offset, part_count, part_offset,
+                                                   row_of_pair, src_pair, status, recv_x,
+                                                   recv_scales, s));
+    int rc = from_hip(ep::launch_layout(topk_idx, T, K, E, P, expert_count, expert_offset,
+                                        part_count, part_offset, row_of_pair, src_pair, status,
+                                        ws, s));
+    if (rc != EP_OK || T == 0) return rc;
+    return from_hip(ep::launch_dispatch(x, T, H, K, row_of_pair, payload, recv_x, recv_scales, s));
+}
+
+// Argument checks of ep_layout_dispatch that do not involve the workspace.
+int layout_dispatch_args(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
+                         int P, int payload, int32_t* expert_count, int32_t* expert_offset,
+                         int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
+                         int32_t* src_pair, uint32_t* status, void* recv_x, float* recv_scales)
 {
     if (payload != EP_PAYLOAD_FP8_E4M3FN && payload != EP_PAYLOAD_BF16) return EP_ENOTSUP;
     if (!routing_ok(T, K) || E < 1 || E > EP_MAX_EXPERTS || P < 1 || E % P != 0 || H <= 0)
@@ -95,19 +124,92 @@ int ep_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H,
             return EP_EINVAL;
         if (payload == EP_PAYLOAD_FP8_E4M3FN && !ptr_ok(recv_scales, 4)) return EP_EINVAL;
     }
+    return EP_OK;
+}
+
+}  // namespace
+
+// ---- the no-allocation variant's scratch buffer ----------------------------
+// The layout workspace of ep_layout_dispatch_noalloc: a device array of the
+// library's own, one copy per device (each at its own address), held until
+// the process ends.  Host code never uses the name `scratch` as an address
+// (on the host it is only a stand-in for the symbol): the device address is
+// looked up once per device with hipGetSymbolAddress and kept in
+// g_scratch_addr, and only that address reaches a kernel.
+static __device__ __align__(256) unsigned char scratch[EP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices];       // null: not looked up on that device yet
+
+// Device address of `scratch` on the current device, which must be the
+// stream's device; looked up on the first call for that device.
+int scratch_address(void* stream, void** addr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return from_hip(e);
+    if (dev < 0 || dev >= kMaxDevices) return EP_EINVAL;
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+        if (e != hipSuccess) return from_hip(e);
+        if (sdev != dev) return EP_EINVAL;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return from_hip(e);
+        if (p == nullptr) return EP_EINVAL;
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
+                       int P, int payload, int32_t* expert_count, int32_t* expert_offset,
+                       int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
+                       int32_t* src_pair, uint32_t* status, void* ws, size_t ws_bytes,
+                       void* recv_x, float* recv_scales, void* stream)
+{
+    const int rc = layout_dispatch_args(topk_idx, x, T, H, K, E, P, payload, expert_count,
+                                        expert_offset, part_count, part_offset, row_of_pair,
+                                        src_pair, status, recv_x, recv_scales);
+    if (rc != EP_OK) return rc;
+    return layout_dispatch_checked(topk_idx, x, T, H, K, E, P, payload, expert_count,
+                                   expert_offset, part_count, part_offset, row_of_pair, src_pair,
+                                   status, ws, ws_bytes, recv_x, recv_scales, stream);
+}
+
+int ep_layout_dispatch_noalloc(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
+                               int E, int P, int payload, int32_t* expert_count,
+                               int32_t* expert_offset, int32_t* part_count, int32_t* part_offset,
+                               int32_t* row_of_pair, int32_t* src_pair, uint32_t* status,
+                               void* recv_x, float* recv_scales, void* stream)
+{
+    int rc = layout_dispatch_args(topk_idx, x, T, H, K, E, P, payload, expert_count,
+                                  expert_offset, part_count, part_offset, row_of_pair, src_pair,
+                                  status, recv_x, recv_scales);
+    if (rc != EP_OK) return rc;
     const size_t need = ep::layout_workspace_bytes(T, K, E);
-    if (need > 0 && (ws_bytes < need || !ptr_ok(ws, 16))) return EP_EINVAL;
-    hipStream_t s = (hipStream_t)stream;
-    if (T > 0 && ep::fused_layout_dispatch_fits(T, H, K))
-        return from_hip(ep::launch_layout_dispatch(topk_idx, x, T, H, K, E, P, payload, expert_count,
-                                                   expert_offset, part_count, part_offset,
-                                                   row_of_pair, src_pair, status, recv_x,
-                                                   recv_scales, s));
-    int rc = from_hip(ep::launch_layout(topk_idx, T, K, E, P, expert_count, expert_offset,
-                                        part_count, part_offset, row_of_pair, src_pair, status,
-                                        ws, s));
-    if (rc != EP_OK || T == 0) return rc;
-    return from_hip(ep::launch_dispatch(x, T, H, K, row_of_pair, payload, recv_x, recv_scales, s));
+    if (need > EP_NOALLOC_SCRATCH_BYTES) return EP_ESCRATCH;     // before any HIP call
+    void* ws = nullptr;
+    if (need > 0) {
+        rc = scratch_address(stream, &ws);
+        if (rc != EP_OK) return rc;
+    }
+    return layout_dispatch_checked(topk_idx, x, T, H, K, E, P, payload, expert_count,
+                                   expert_offset, part_count, part_offset, row_of_pair, src_pair,
+                                   status, ws, need > 0 ? (size_t)EP_NOALLOC_SCRATCH_BYTES : 0,
+                                   recv_x, recv_scales, stream);
 }
 
 namespace {
@@ -308,6 +410,9 @@ const char* ep_strerror(int code)
     case EP_EINVAL: return "invalid argument (size, divisibility, null or misaligned pointer, workspace)";
     case EP_ENOTSUP: return "unsupported payload";
     case EP_EHIP: return "HIP launch failed (see ep_last_hip_error)";
+    case EP_ESCRATCH:
+        return "batch needs a larger layout workspace than the library's no-allocation scratch "
+               "buffer (EP_NOALLOC_SCRATCH_BYTES); use ep_layout_dispatch with a workspace";
     default: return "unknown ep error code";
     }
 }

@@ -24,14 +24,17 @@
  * Conventions (all entry points):
  *   - Device pointers unless stated.  The caller owns every buffer; the
  *     library allocates nothing, keeps no pointer after a call returns and
- *     holds no global state, so calls on different streams are independent.
+ *     holds no global state, so calls on different streams are independent
+ *     (the one exception, ep_layout_dispatch_noalloc, holds a scratch buffer
+ *     per device).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work; none synchronises the host.  Buffers must stay
  *     alive until the stream has run the work.
  *   - Return 0 on success.  A negative code means a host-side check failed
  *     and NOTHING was enqueued: EP_EINVAL (bad argument), EP_ENOTSUP
  *     (unsupported payload), EP_EHIP (a HIP launch failed; see
- *     ep_last_hip_error()).
+ *     ep_last_hip_error()), EP_ESCRATCH (ep_layout_dispatch_noalloc only:
+ *     the batch needs more scratch than the library holds).
  *   - Every call can be captured into a HIP graph: no call allocates,
  *     memsets or synchronises; counters the kernels need are cleared by
  *     the kernels themselves.
@@ -152,6 +155,36 @@ int ep_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H,
                        int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
                        int32_t* src_pair, uint32_t* status, void* ws, size_t ws_bytes,
                        void* recv_x, float* recv_scales, void* stream);
+
+/*
+ * ep_layout_dispatch without a workspace argument, for callers that cannot
+ * allocate device memory (code recorded into a HIP graph, serving loops that
+ * forbid allocation, harnesses without an allocator).  Same arguments,
+ * results and errors as ep_layout_dispatch minus ws / ws_bytes: batches that
+ * need a layout workspace (ep_layout_workspace_bytes(T, K, E) > 0) use a
+ * buffer of EP_NOALLOC_SCRATCH_BYTES that the library holds on each device
+ * from its first such call until the process ends.  The call allocates
+ * nothing.
+ *   - A batch whose workspace exceeds EP_NOALLOC_SCRATCH_BYTES is rejected
+ *     with EP_ESCRATCH before anything else happens (for E = 1024 that is
+ *     T*K above about 10^6 entries).
+ *   - `stream` must belong to the current device (EP_EINVAL otherwise).
+ *   - The first call on a device that needs the buffer looks up its address
+ *     there (a host call, not stream work): make that first call outside
+ *     stream capture.
+ *   - Every call on one device shares that device's buffer, so calls that
+ *     can overlap on one device (concurrent streams, other host threads)
+ *     race; serialise them.  The buffer needs no initialisation and keeps
+ *     the last call's scratch contents.
+ */
+#define EP_ESCRATCH (-4)
+#define EP_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+
+int ep_layout_dispatch_noalloc(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
+                               int E, int P, int payload, int32_t* expert_count,
+                               int32_t* expert_offset, int32_t* part_count, int32_t* part_offset,
+                               int32_t* row_of_pair, int32_t* src_pair, uint32_t* status,
+                               void* recv_x, float* recv_scales, void* stream);
 
 /*
  * Combine: out[t, c] = bf16_rne(acc), acc = 0.0f, then for k = 0..K-1 with

@@ -142,3 +142,28 @@ def test_geometry_host_side_validation(lib):
     # valid geometry, empty batch: accepted, nothing launched
     assert L.ep_dispatch_geom(None, 0, 1024, 8, None, 0, None, None, 8, 0, None) == 0
     assert L.ep_combine_geom(None, None, None, 0, 1024, 8, None, 1, 256, None) == 0
+
+
+def test_noalloc_host_side_validation(lib):
+    """ep_layout_dispatch_noalloc refuses, before any HIP call, a batch whose
+    layout workspace exceeds EP_NOALLOC_SCRATCH_BYTES (EP_ESCRATCH), and
+    otherwise checks its arguments as ep_layout_dispatch does."""
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L = lib
+    L.ep_layout_dispatch_noalloc.argtypes = [P, P, I, I, I, I, I, I] + [P] * 10
+    L.ep_layout_workspace_bytes.argtypes = [I, I, I]
+    L.ep_layout_workspace_bytes.restype = ctypes.c_size_t
+    L.ep_strerror.restype = ctypes.c_char_p
+    fake = P(0x10000)          # never dereferenced: every case below fails a host check first
+    outs = [fake] * 7
+    assert L.ep_layout_workspace_bytes(73728, 16, 1024) > (4 << 20)
+    assert L.ep_layout_dispatch_noalloc(fake, fake, 73728, 128, 16, 1024, 8, 0, *outs, fake, fake,
+                                        None) == -4
+    assert b"scratch" in L.ep_strerror(-4)
+    # the ordinary argument errors come first
+    assert L.ep_layout_dispatch_noalloc(fake, fake, 4, 1024, 8, 32, 8, 5, *outs, fake, fake,
+                                        None) == -2
+    assert L.ep_layout_dispatch_noalloc(fake, fake, 4, 1000, 8, 32, 8, 0, *outs, fake, fake,
+                                        None) == -1
+    assert L.ep_layout_dispatch_noalloc(fake, fake, 4, 1024, 8, 30, 8, 0, *outs, fake, fake,
+                                        None) == -1
