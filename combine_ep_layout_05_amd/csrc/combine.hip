@@ -335,8 +335,8 @@ constexpr int64_t kMaxGridBlocks = 1 << 20;
 // gathered rows exceed what the caches can usefully hold: measured on MI355X
 // at 4096 x 7168 top-8 right after a dispatch, the combine went 132 -> 96 us
 // because its once-read rows no longer evict the dispatch's fresh lines.
-// EP_FORCE_POLICY (build option for A/B runs): 1 = cached accesses everywhere,
-// 2 = streaming combine only, 3 = streaming dispatch and combine.
+// EP_FORCE_POLICY (build option for A/B runs): 1 = cached combine accesses,
+// 2 or more = streaming ones, whatever the size.
 bool combine_streams(int64_t gathered_rows, int H)
 {
 #if defined(EP_FORCE_POLICY)
