@@ -42,14 +42,17 @@ _SIGS = {
     "ep_combine": ([_P, _P, _P, _I, _I, _I, _P, _P], _I),
     "ep_layout_dispatch": ([_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                             _P, _P, _P], _I),
+    "ep_layout_dispatch_geom": ([_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _SZ, _P, _P, _I, _I, _I, _P], _I),
+    "ep_layout_dispatch_plan": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, _P], _I),
     "ep_layout_dispatch_noalloc": ([_P, _P, _I, _I, _I, _I, _I, _I] + [_P] * 10, _I),
     "ep_graph_begin": ([_P], _I),
     "ep_graph_end": ([_P, ctypes.POINTER(_P)], _I),
     "ep_graph_launch": ([_P, _P], _I),
     "ep_graph_destroy": ([_P], _I),
     "ep_e4m3fn_encode": ([_P, _I64, _P, _P], _I),
-    "ep_dispatch_geom": ([_P, _I, _I, _I, _P, _I, _P, _P, _I, _I, _P], _I),
-    "ep_combine_geom": ([_P, _P, _P, _I, _I, _I, _P, _I, _I, _P], _I),
+    "ep_dispatch_geom": ([_P, _I, _I, _I, _P, _I, _P, _P, _I, _I, _I, _P], _I),
+    "ep_combine_geom": ([_P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _P], _I),
     "ep_dedup_layout_workspace_bytes": ([_I, _I, _I, _I], _SZ),
     "ep_dedup_layout": ([_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "ep_combine_partial": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
@@ -63,6 +66,8 @@ _SIGS = {
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
     _f.argtypes, _f.restype = _args, _res
+
+PLAN_KINDS = {0: "fused_tiny", 1: "fused_count", 2: "fused_general", 3: "layout_then_dispatch"}
 
 
 class EpError(RuntimeError):
@@ -94,10 +99,74 @@ def _dt(t, *dtypes):
         raise TypeError("dtype %s not in %s" % (t.dtype, dtypes))
 
 
+# Shape checks, made before any pointer reaches the library: a tensor smaller
+# than the call assumes would be read or written past its end on the device.
+def _numel(t, n, name):
+    if t is None or t.numel() != n:
+        raise ValueError("%s: expected %d elements, got %s" % (name, n, None if t is None else t.numel()))
+
+
+def _rows(t, min_rows, width, name):
+    if t is None or t.dim() != 2 or t.shape[0] < min_rows or t.shape[1] != width:
+        raise ValueError("%s: expected a 2-D tensor of at least %d rows and %d columns, got %s" % (
+            name, min_rows, width, None if t is None else tuple(t.shape)))
+
+
+def _matrix(t, shape, name):
+    if t is None or tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape),
+                                                             None if t is None else tuple(t.shape)))
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U32 = (torch.int32, torch.uint32)
+
+
+def _layout_outputs(T, K, E, P, expert_count, expert_offset, part_count, part_offset, row_of_pair,
+                    src_pair, status):
+    for t in (expert_count, expert_offset, part_count, part_offset, row_of_pair, src_pair):
+        _dt(t, torch.int32)
+    _dt(status, *_U32)
+    _numel(expert_count, E, "expert_count")
+    _numel(expert_offset, E + 1, "expert_offset")
+    _numel(part_count, P, "part_count")
+    _numel(part_offset, P + 1, "part_offset")
+    _numel(row_of_pair, T * K, "row_of_pair")
+    _numel(src_pair, T * K, "src_pair")
+    if status is None or status.numel() < 1:
+        raise ValueError("status: one element expected")
+
+
+def _receive(payload, rows, H, recv_x, recv_scales):
+    """recv_x / recv_scales for `rows` receive rows of hidden size H."""
+    if payload == EP_PAYLOAD_FP8_E4M3FN:
+        _dt(recv_x, torch.uint8)
+        _dt(recv_scales, torch.float32)
+        _rows(recv_x, rows, H, "recv_x (fp8 bytes)")
+        _rows(recv_scales, rows, H // 128, "recv_scales")
+    elif payload == EP_PAYLOAD_BF16:
+        _dt(recv_x, *_BF16)
+        _rows(recv_x, rows, H, "recv_x (bf16)")
+
+
+def _ws_bytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _geometry(geometry):
+    """(waves_per_block, max_blocks[, slice_cols]) -> three ints."""
+    g = tuple(int(v) for v in geometry)
+    if len(g) == 2:
+        g = g + (0,)
+    if len(g) != 3:
+        raise ValueError("geometry: (waves_per_block, max_blocks[, slice_cols]) expected")
+    return g
 
 
 def library_path() -> str:
@@ -112,48 +181,72 @@ def ep_layout(topk_idx, E, P, expert_count, expert_offset, part_count, part_offs
               row_of_pair, src_pair, status, ws=None, stream=None):
     """topk_idx int32 [T, K] -> the layout outputs (see include/ep.h)."""
     _dt(topk_idx, torch.int32)
-    for t in (expert_count, expert_offset, part_count, part_offset, row_of_pair, src_pair):
-        _dt(t, torch.int32)
-    _dt(status, torch.int32, torch.uint32)
     T, K = topk_idx.shape
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _layout_outputs(T, K, E, P, expert_count, expert_offset, part_count, part_offset, row_of_pair,
+                    src_pair, status)
     _check("ep_layout", _lib.ep_layout(
         _ptr(topk_idx), T, K, E, P, _ptr(expert_count), _ptr(expert_offset), _ptr(part_count),
-        _ptr(part_offset), _ptr(row_of_pair), _ptr(src_pair), _ptr(status), _ptr(ws), ws_bytes,
+        _ptr(part_offset), _ptr(row_of_pair), _ptr(src_pair), _ptr(status), _ptr(ws), _ws_bytes(ws),
         _stream(stream)))
 
 
 def ep_dispatch(x, K, row_of_pair, payload, recv_x, recv_scales=None, stream=None, geometry=None):
     """x bf16 [T, H] -> recv_x (uint8 fp8 bytes or bf16) [T*K, H], recv_scales fp32 [T*K, H/128].
-    geometry: None (library default) or (waves_per_block, max_blocks)."""
-    _dt(x, torch.bfloat16, torch.int16, torch.uint16)
+    geometry: None (library default) or (waves_per_block, max_blocks[, slice_cols])."""
+    _dt(x, *_BF16)
     _dt(row_of_pair, torch.int32)
     payload = PAYLOADS.get(payload, payload)
     T, H = x.shape
+    _numel(row_of_pair, T * K, "row_of_pair")
+    _receive(payload, T * K, H, recv_x, recv_scales)
     if geometry is None:
         _check("ep_dispatch", _lib.ep_dispatch(_ptr(x), T, H, K, _ptr(row_of_pair), payload,
                                                _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
     else:
-        wv, mb = geometry
+        wv, mb, sc = _geometry(geometry)
         _check("ep_dispatch_geom", _lib.ep_dispatch_geom(
             _ptr(x), T, H, K, _ptr(row_of_pair), payload, _ptr(recv_x), _ptr(recv_scales), wv, mb,
-            _stream(stream)))
+            sc, _stream(stream)))
 
 
 def ep_layout_dispatch(topk_idx, x, E, P, payload, expert_count, expert_offset, part_count,
                        part_offset, row_of_pair, src_pair, status, ws, recv_x, recv_scales=None,
-                       stream=None):
-    """ep_layout followed by ep_dispatch, as one launch for small batches."""
+                       stream=None, geometry=None):
+    """ep_layout followed by ep_dispatch, as one launch for small batches.
+    geometry: None (the library's choice) or (waves_per_block, max_blocks[,
+    slice_cols]) as ep_layout_dispatch_geom takes it."""
     _dt(topk_idx, torch.int32)
-    _dt(x, torch.bfloat16, torch.int16, torch.uint16)
+    _dt(x, *_BF16)
     payload = PAYLOADS.get(payload, payload)
     T, K = topk_idx.shape
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x: expected [%d, H], got %s" % (T, tuple(x.shape)))
     H = x.shape[1]
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check("ep_layout_dispatch", _lib.ep_layout_dispatch(
-        _ptr(topk_idx), _ptr(x), T, H, K, E, P, payload, _ptr(expert_count), _ptr(expert_offset),
-        _ptr(part_count), _ptr(part_offset), _ptr(row_of_pair), _ptr(src_pair), _ptr(status),
-        _ptr(ws), ws_bytes, _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
+    _layout_outputs(T, K, E, P, expert_count, expert_offset, part_count, part_offset, row_of_pair,
+                    src_pair, status)
+    _receive(payload, T * K, H, recv_x, recv_scales)
+    args = (_ptr(topk_idx), _ptr(x), T, H, K, E, P, payload, _ptr(expert_count),
+            _ptr(expert_offset), _ptr(part_count), _ptr(part_offset), _ptr(row_of_pair),
+            _ptr(src_pair), _ptr(status), _ptr(ws), _ws_bytes(ws), _ptr(recv_x), _ptr(recv_scales))
+    if geometry is None:
+        _check("ep_layout_dispatch", _lib.ep_layout_dispatch(*args, _stream(stream)))
+    else:
+        _check("ep_layout_dispatch_geom",
+               _lib.ep_layout_dispatch_geom(*args, *_geometry(geometry), _stream(stream)))
+
+
+def ep_layout_dispatch_plan(T, H, K, E, P, payload, geometry=None):
+    """How ep_layout_dispatch(_geom) would run this batch (host only):
+    {"kernel": ..., "waves": ..., "blocks" or "max_blocks": ..., "slice_cols": ...}."""
+    payload = PAYLOADS.get(payload, payload)
+    plan = (ctypes.c_int32 * 4)()
+    wv, mb, sc = _geometry(geometry) if geometry is not None else (0, 0, 0)
+    _check("ep_layout_dispatch_plan", _lib.ep_layout_dispatch_plan(
+        T, H, K, E, P, payload, wv, mb, sc, ctypes.cast(plan, ctypes.c_void_p)))
+    kind = PLAN_KINDS[plan[0]]
+    d = {"kernel": kind, "waves": int(plan[1]), "slice_cols": int(plan[3])}
+    d["max_blocks" if kind == "layout_then_dispatch" else "blocks"] = int(plan[2])
+    return d
 
 
 def ep_layout_dispatch_noalloc(topk_idx, x, E, P, payload, expert_count, expert_offset,
@@ -162,10 +255,15 @@ def ep_layout_dispatch_noalloc(topk_idx, x, E, P, payload, expert_count, expert_
     """ep_layout_dispatch with the library's own per-device scratch buffer as
     the layout workspace: the call allocates nothing (see include/ep.h)."""
     _dt(topk_idx, torch.int32)
-    _dt(x, torch.bfloat16, torch.int16, torch.uint16)
+    _dt(x, *_BF16)
     payload = PAYLOADS.get(payload, payload)
     T, K = topk_idx.shape
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x: expected [%d, H], got %s" % (T, tuple(x.shape)))
     H = x.shape[1]
+    _layout_outputs(T, K, E, P, expert_count, expert_offset, part_count, part_offset, row_of_pair,
+                    src_pair, status)
+    _receive(payload, T * K, H, recv_x, recv_scales)
     _check("ep_layout_dispatch_noalloc", _lib.ep_layout_dispatch_noalloc(
         _ptr(topk_idx), _ptr(x), T, H, K, E, P, payload, _ptr(expert_count), _ptr(expert_offset),
         _ptr(part_count), _ptr(part_offset), _ptr(row_of_pair), _ptr(src_pair), _ptr(status),
@@ -174,26 +272,31 @@ def ep_layout_dispatch_noalloc(topk_idx, x, E, P, payload, expert_count, expert_
 
 def ep_combine(expert_out, row_of_pair, topk_w, out, stream=None, geometry=None):
     """expert_out bf16 [T*K, H] (receive-row layout), topk_w fp32 [T, K] -> out bf16 [T, H].
-    geometry: None (library default) or (waves_per_block, max_blocks)."""
-    _dt(expert_out, torch.bfloat16, torch.int16, torch.uint16)
-    _dt(out, torch.bfloat16, torch.int16, torch.uint16)
+    geometry: None (library default) or (waves_per_block, max_blocks[, slice_cols])."""
+    _dt(expert_out, *_BF16)
+    _dt(out, *_BF16)
     _dt(topk_w, torch.float32)
     _dt(row_of_pair, torch.int32)
     T, K = topk_w.shape
+    if out.dim() != 2 or out.shape[0] != T:
+        raise ValueError("out: expected [%d, H], got %s" % (T, tuple(out.shape)))
     H = out.shape[1]
+    _numel(row_of_pair, T * K, "row_of_pair")
+    _rows(expert_out, T * K, H, "expert_out")
     if geometry is None:
         _check("ep_combine", _lib.ep_combine(_ptr(expert_out), _ptr(row_of_pair), _ptr(topk_w), T,
                                              H, K, _ptr(out), _stream(stream)))
     else:
-        wv, mb = geometry
+        wv, mb, sc = _geometry(geometry)
         _check("ep_combine_geom", _lib.ep_combine_geom(
-            _ptr(expert_out), _ptr(row_of_pair), _ptr(topk_w), T, H, K, _ptr(out), wv, mb,
+            _ptr(expert_out), _ptr(row_of_pair), _ptr(topk_w), T, H, K, _ptr(out), wv, mb, sc,
             _stream(stream)))
 
 
 def ep_e4m3fn_encode(values_f32, out_u8, stream=None):
     _dt(values_f32, torch.float32)
     _dt(out_u8, torch.uint8)
+    _numel(out_u8, values_f32.numel(), "out_u8")
     _check("ep_e4m3fn_encode", _lib.ep_e4m3fn_encode(_ptr(values_f32), values_f32.numel(),
                                                      _ptr(out_u8), _stream(stream)))
 
@@ -202,19 +305,29 @@ def ep_dedup_layout_workspace_bytes(T: int, K: int, E: int, P: int) -> int:
     return int(_lib.ep_dedup_layout_workspace_bytes(T, K, E, P))
 
 
+def _dedup_outputs(T, P, tp_row, part_tokens, part_token_offset, tp_src, kmask, status):
+    for t in (tp_row, part_tokens, part_token_offset, tp_src):
+        _dt(t, torch.int32)
+    _dt(kmask, *_U32)
+    _dt(status, *_U32)
+    _numel(tp_row, T * P, "tp_row")
+    _numel(part_tokens, P, "part_tokens")
+    _numel(part_token_offset, P + 1, "part_token_offset")
+    _numel(tp_src, T * P, "tp_src")
+    _numel(kmask, T * P, "kmask")
+    if status is None or status.numel() < 1:
+        raise ValueError("status: one element expected")
+
+
 def ep_dedup_layout(topk_idx, E, P, tp_row, part_tokens, part_token_offset, tp_src, kmask,
                     status, ws=None, stream=None):
     """topk_idx int32 [T, K] -> per-destination (dedup) layout (see include/ep.h)."""
     _dt(topk_idx, torch.int32)
-    for t in (tp_row, part_tokens, part_token_offset, tp_src):
-        _dt(t, torch.int32)
-    _dt(kmask, torch.int32, torch.uint32)
-    _dt(status, torch.int32, torch.uint32)
     T, K = topk_idx.shape
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _dedup_outputs(T, P, tp_row, part_tokens, part_token_offset, tp_src, kmask, status)
     _check("ep_dedup_layout", _lib.ep_dedup_layout(
         _ptr(topk_idx), T, K, E, P, _ptr(tp_row), _ptr(part_tokens), _ptr(part_token_offset),
-        _ptr(tp_src), _ptr(kmask), _ptr(status), _ptr(ws), ws_bytes, _stream(stream)))
+        _ptr(tp_src), _ptr(kmask), _ptr(status), _ptr(ws), _ws_bytes(ws), _stream(stream)))
 
 
 def ep_dedup_layout_dispatch_workspace_bytes(T: int, K: int, E: int, P: int) -> int:
@@ -227,28 +340,40 @@ def ep_dedup_layout_dispatch(topk_idx, x, E, P, payload, expert_count, expert_of
                              recv_scales=None, stream=None):
     """Per-expert layout + dedup layout + dedup dispatch (one launch for small batches)."""
     _dt(topk_idx, torch.int32)
-    _dt(x, torch.bfloat16, torch.int16, torch.uint16)
+    _dt(x, *_BF16)
     payload = PAYLOADS.get(payload, payload)
     T, K = topk_idx.shape
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x: expected [%d, H], got %s" % (T, tuple(x.shape)))
     H = x.shape[1]
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _layout_outputs(T, K, E, P, expert_count, expert_offset, part_count, part_offset, row_of_pair,
+                    src_pair, status)
+    _dedup_outputs(T, P, tp_row, part_tokens, part_token_offset, tp_src, kmask, status)
+    _receive(payload, T * P, H, recv_x, recv_scales)
     _check("ep_dedup_layout_dispatch", _lib.ep_dedup_layout_dispatch(
         _ptr(topk_idx), _ptr(x), T, H, K, E, P, payload, _ptr(expert_count), _ptr(expert_offset),
         _ptr(part_count), _ptr(part_offset), _ptr(row_of_pair), _ptr(src_pair), _ptr(tp_row),
         _ptr(part_tokens), _ptr(part_token_offset), _ptr(tp_src), _ptr(kmask), _ptr(status),
-        _ptr(ws), ws_bytes, _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
+        _ptr(ws), _ws_bytes(ws), _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
 
 
 def ep_combine_partial(expert_out, row_of_pair, topk_w, tp_row, kmask, P, partial, stream=None):
     """Level 1: expert_out bf16 [T*K, H] -> partial bf16 [T*P, H] (rows of present couples)."""
-    _dt(expert_out, torch.bfloat16, torch.int16, torch.uint16)
-    _dt(partial, torch.bfloat16, torch.int16, torch.uint16)
+    _dt(expert_out, *_BF16)
+    _dt(partial, *_BF16)
     _dt(topk_w, torch.float32)
     _dt(row_of_pair, torch.int32)
     _dt(tp_row, torch.int32)
-    _dt(kmask, torch.int32, torch.uint32)
+    _dt(kmask, *_U32)
     T, K = topk_w.shape
+    if partial.dim() != 2:
+        raise ValueError("partial: a 2-D tensor expected")
     H = partial.shape[1]
+    _rows(partial, T * P, H, "partial")
+    _rows(expert_out, T * K, H, "expert_out")
+    _numel(row_of_pair, T * K, "row_of_pair")
+    _numel(tp_row, T * P, "tp_row")
+    _numel(kmask, T * P, "kmask")
     _check("ep_combine_partial", _lib.ep_combine_partial(
         _ptr(expert_out), _ptr(row_of_pair), _ptr(topk_w), _ptr(tp_row), _ptr(kmask), T, H, K, P,
         _ptr(partial), _stream(stream)))
@@ -256,10 +381,14 @@ def ep_combine_partial(expert_out, row_of_pair, topk_w, tp_row, kmask, P, partia
 
 def ep_combine_reduce(partial, tp_row, T, P, out, stream=None):
     """Level 2: partial bf16 [T*P, H] -> out bf16 [T, H] (partition-order fp32 sum)."""
-    _dt(partial, torch.bfloat16, torch.int16, torch.uint16)
-    _dt(out, torch.bfloat16, torch.int16, torch.uint16)
+    _dt(partial, *_BF16)
+    _dt(out, *_BF16)
     _dt(tp_row, torch.int32)
+    if out.dim() != 2 or out.shape[0] != T:
+        raise ValueError("out: expected [%d, H], got %s" % (T, tuple(out.shape)))
     H = out.shape[1]
+    _rows(partial, T * P, H, "partial")
+    _numel(tp_row, T * P, "tp_row")
     _check("ep_combine_reduce", _lib.ep_combine_reduce(_ptr(partial), _ptr(tp_row), T, H, P,
                                                        _ptr(out), _stream(stream)))
 
@@ -301,14 +430,15 @@ class EpBuffers:
 
     def __init__(self, T, H, K, E, P, payload="fp8", device="cuda", geometry=None):
         """geometry: None (library defaults), "tuned" (the saved rules for this
-        shape, where there are any) or {"dispatch": (waves, max_blocks),
-        "combine": (waves, max_blocks)}."""
+        shape, where there are any) or a dict with any of the keys
+        "layout_dispatch", "dispatch", "combine", each (waves_per_block,
+        max_blocks, slice_cols) as the *_geom entry points take it."""
         self.T, self.H, self.K, self.E, self.P = T, H, K, E, P
         self.payload = payload
         if geometry == "tuned":
             from . import tuning
-            geometry = {ph: tuning.lookup(ph, T, H, K, payload) for ph in ("dispatch", "combine")}
-        self.geometry = {k: v for k, v in (geometry or {}).items() if v is not None}
+            geometry = {ph: tuning.lookup(ph, T, H, K, payload) for ph in tuning.PHASES}
+        self.geometry = {k: _geometry(v) for k, v in (geometry or {}).items() if v is not None}
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         self.expert_count = torch.empty(E, **i32)
@@ -335,7 +465,20 @@ class EpBuffers:
     def layout_dispatch(self, topk_idx, x, stream=None):
         ep_layout_dispatch(topk_idx, x, self.E, self.P, self.payload, self.expert_count,
                            self.expert_offset, self.part_count, self.part_offset, self.row_of_pair,
-                           self.src_pair, self.status, self.ws, self.recv_x, self.recv_scales, stream)
+                           self.src_pair, self.status, self.ws, self.recv_x, self.recv_scales, stream,
+                           self.geometry.get("layout_dispatch"))
+
+    def plan(self):
+        """What layout_dispatch launches for this shape and geometry, and the
+        dispatch / combine geometry (host only)."""
+        d = {"layout_dispatch": ep_layout_dispatch_plan(self.T, self.H, self.K, self.E, self.P,
+                                                        self.payload,
+                                                        self.geometry.get("layout_dispatch"))}
+        for ph in ("dispatch", "combine"):
+            g = self.geometry.get(ph)
+            d[ph] = "library default (4 waves, uncapped, 512 columns)" if g is None else \
+                {"waves": g[0], "max_blocks": g[1], "slice_cols": g[2] or 512}
+        return d
 
     def dispatch(self, x, stream=None):
         ep_dispatch(x, self.K, self.row_of_pair, self.payload, self.recv_x, self.recv_scales, stream,
@@ -414,8 +557,8 @@ class BoundStep:
 
     def __init__(self, buf, topk_idx, x, expert_out, topk_w, stream=None):
         _dt(topk_idx, torch.int32)
-        _dt(x, torch.bfloat16, torch.int16, torch.uint16)
-        _dt(expert_out, torch.bfloat16, torch.int16, torch.uint16)
+        _dt(x, *_BF16)
+        _dt(expert_out, *_BF16)
         _dt(topk_w, torch.float32)
         T, K = topk_idx.shape
         if (T, K) != (buf.T, buf.K) or tuple(x.shape) != (buf.T, buf.H) or \
@@ -428,17 +571,23 @@ class BoundStep:
                     _ptr(buf.expert_count), _ptr(buf.expert_offset), _ptr(buf.part_count),
                     _ptr(buf.part_offset), _ptr(buf.row_of_pair), _ptr(buf.src_pair),
                     _ptr(buf.status), _ptr(buf.ws), ws_bytes, _ptr(buf.recv_x),
-                    _ptr(buf.recv_scales), s)
-        g = buf.geometry.get("combine")
+                    _ptr(buf.recv_scales))
+        g = buf.geometry.get("layout_dispatch")
         if g is None:
-            self._cb = (_ptr(expert_out), _ptr(buf.row_of_pair), _ptr(topk_w), T, buf.H, K,
-                        _ptr(buf.out), s)
+            self._ld = self._ld + (s,)
+            self._f_ld = _lib.ep_layout_dispatch
+        else:
+            self._ld = self._ld + tuple(g) + (s,)
+            self._f_ld = _lib.ep_layout_dispatch_geom
+        g = buf.geometry.get("combine")
+        self._cb = (_ptr(expert_out), _ptr(buf.row_of_pair), _ptr(topk_w), T, buf.H, K,
+                    _ptr(buf.out))
+        if g is None:
+            self._cb = self._cb + (s,)
             self._f_cb = _lib.ep_combine
         else:
-            self._cb = (_ptr(expert_out), _ptr(buf.row_of_pair), _ptr(topk_w), T, buf.H, K,
-                        _ptr(buf.out), int(g[0]), int(g[1]), s)
+            self._cb = self._cb + tuple(g) + (s,)
             self._f_cb = _lib.ep_combine_geom
-        self._f_ld = _lib.ep_layout_dispatch
 
     def layout_dispatch(self):
         rc = self._f_ld(*self._ld)

@@ -11,6 +11,10 @@
 #include "ep_device.h"
 #include "ep_launch.h"
 
+static_assert(ep::kFusedTiny == EP_PLAN_FUSED_TINY && ep::kFusedCount == EP_PLAN_FUSED_COUNT &&
+                  ep::kFusedGeneral == EP_PLAN_FUSED_GENERAL,
+              "the plan codes of the header are the launcher's kernel kinds");
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -73,6 +77,7 @@ int ep_dispatch(const uint16_t* x, int T, int H, int K, const int32_t* row_of_pa
     if (T == 0) return EP_OK;
     if (!ptr_ok(x, 16) || !ptr_ok(row_of_pair, 4) || !ptr_ok(recv_x, 16)) return EP_EINVAL;
     if (payload == EP_PAYLOAD_FP8_E4M3FN && !ptr_ok(recv_scales, 4)) return EP_EINVAL;
+    if (!ep::dispatch_launch_ok(T, H, ep::kDefaultGeometry)) return EP_EINVAL;
     return from_hip(ep::launch_dispatch(x, T, H, K, row_of_pair, payload, recv_x, recv_scales,
                                         (hipStream_t)stream));
 }
@@ -81,27 +86,65 @@ int ep_dispatch(const uint16_t* x, int T, int H, int K, const int32_t* row_of_pa
 
 namespace {
 
-// The checks and launches of ep_layout_dispatch, for a workspace ws of
-// ws_bytes (the caller's, or the library's scratch buffer).
+// Launch geometry from the API's (waves_per_block, max_blocks, slice_cols);
+// 0 means the default for each.  False for values the kernels do not take.
+bool move_geometry(int waves_per_block, int max_blocks, int slice_cols, ep::MoveGeometry* g)
+{
+    if (waves_per_block == 0) waves_per_block = ep::kDefaultGeometry.waves;
+    if (slice_cols == 0) slice_cols = ep::kStepCols;
+    if (waves_per_block != 1 && waves_per_block != 2 && waves_per_block != 4 &&
+        waves_per_block != 8)
+        return false;
+    if (max_blocks < 0) return false;
+    if (slice_cols != ep::kStepCols && slice_cols != ep::kMaxSliceSteps * ep::kStepCols) return false;
+    *g = ep::MoveGeometry{waves_per_block, max_blocks, slice_cols / ep::kStepCols};
+    return true;
+}
+
+// How ep_layout_dispatch(_geom) runs a batch: fused (one launch, plan) or
+// the layout then the dispatch kernel with geometry g.  False when the
+// geometry is not accepted for this batch.
+bool layout_dispatch_route(int T, int H, int K, int waves_per_block, int max_blocks,
+                           int slice_cols, bool* fused, ep::FusedPlan* plan, ep::MoveGeometry* g)
+{
+    *fused = T > 0 && ep::fused_layout_dispatch_fits(T, H, K);
+    if (*fused) {
+        // the fused kernels take only a workgroup size
+        if (max_blocks != 0 || (slice_cols != 0 && slice_cols != ep::kStepCols)) return false;
+        return ep::plan_layout_dispatch(T, H, K, waves_per_block, plan);
+    }
+    if (!move_geometry(waves_per_block, max_blocks, slice_cols, g)) return false;
+    return T == 0 || ep::dispatch_launch_ok(T, H, *g);
+}
+
+// The launches of ep_layout_dispatch(_geom), for a workspace ws of ws_bytes
+// (the caller's, or the library's scratch buffer); every check is made
+// before the first launch.
 int layout_dispatch_checked(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
                             int P, int payload, int32_t* expert_count, int32_t* expert_offset,
                             int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
                             int32_t* src_pair, uint32_t* status, void* ws, size_t ws_bytes,
-                            void* recv_x, float* recv_scales, void* stream)
+                            void* recv_x, float* recv_scales, int waves_per_block, int max_blocks,
+                            int slice_cols, void* stream)
 {
     const size_t need = ep::layout_workspace_bytes(T, K, E);
     if (need > 0 && (ws_bytes < need || !ptr_ok(ws, 16))) return EP_EINVAL;
+    bool fused = false;
+    ep::FusedPlan plan{};
+    ep::MoveGeometry g = ep::kDefaultGeometry;
+    if (!layout_dispatch_route(T, H, K, waves_per_block, max_blocks, slice_cols, &fused, &plan, &g))
+        return EP_EINVAL;
     hipStream_t s = (hipStream_t)stream;
-    if (T > 0 && ep::fused_layout_dispatch_fits(T, H, K))
+    if (fused)
         return from_hip(ep::launch_layout_dispatch(topk_idx, x, T, H, K, E, P, payload, expert_count,
                                                    expert_offset, part_count, part_offset,
                                                    row_of_pair, src_pair, status, recv_x,
-                                                   recv_scales, s));
+                                                   recv_scales, s, plan.waves));
     int rc = from_hip(ep::launch_layout(topk_idx, T, K, E, P, expert_count, expert_offset,
                                         part_count, part_offset, row_of_pair, src_pair, status,
                                         ws, s));
     if (rc != EP_OK || T == 0) return rc;
-    return from_hip(ep::launch_dispatch(x, T, H, K, row_of_pair, payload, recv_x, recv_scales, s));
+    return from_hip(ep::launch_dispatch(x, T, H, K, row_of_pair, payload, recv_x, recv_scales, s, g));
 }
 
 // Argument checks of ep_layout_dispatch that do not involve the workspace.
@@ -186,7 +229,52 @@ int ep_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H,
     if (rc != EP_OK) return rc;
     return layout_dispatch_checked(topk_idx, x, T, H, K, E, P, payload, expert_count,
                                    expert_offset, part_count, part_offset, row_of_pair, src_pair,
-                                   status, ws, ws_bytes, recv_x, recv_scales, stream);
+                                   status, ws, ws_bytes, recv_x, recv_scales, 0, 0, 0, stream);
+}
+
+int ep_layout_dispatch_geom(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
+                            int P, int payload, int32_t* expert_count, int32_t* expert_offset,
+                            int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
+                            int32_t* src_pair, uint32_t* status, void* ws, size_t ws_bytes,
+                            void* recv_x, float* recv_scales, int waves_per_block, int max_blocks,
+                            int slice_cols, void* stream)
+{
+    const int rc = layout_dispatch_args(topk_idx, x, T, H, K, E, P, payload, expert_count,
+                                        expert_offset, part_count, part_offset, row_of_pair,
+                                        src_pair, status, recv_x, recv_scales);
+    if (rc != EP_OK) return rc;
+    return layout_dispatch_checked(topk_idx, x, T, H, K, E, P, payload, expert_count,
+                                   expert_offset, part_count, part_offset, row_of_pair, src_pair,
+                                   status, ws, ws_bytes, recv_x, recv_scales, waves_per_block,
+                                   max_blocks, slice_cols, stream);
+}
+
+int ep_layout_dispatch_plan(int T, int H, int K, int E, int P, int payload, int waves_per_block,
+                            int max_blocks, int slice_cols, int32_t* plan)
+{
+    if (plan == nullptr) return EP_EINVAL;
+    if (payload != EP_PAYLOAD_FP8_E4M3FN && payload != EP_PAYLOAD_BF16) return EP_ENOTSUP;
+    if (!routing_ok(T, K) || E < 1 || E > EP_MAX_EXPERTS || P < 1 || E % P != 0 || H <= 0)
+        return EP_EINVAL;
+    if (payload == EP_PAYLOAD_FP8_E4M3FN && H % ep::kScaleBlock != 0) return EP_EINVAL;
+    if (payload == EP_PAYLOAD_BF16 && H % ep::kColsPerLane != 0) return EP_EINVAL;
+    bool fused = false;
+    ep::FusedPlan fp{};
+    ep::MoveGeometry g = ep::kDefaultGeometry;
+    if (!layout_dispatch_route(T, H, K, waves_per_block, max_blocks, slice_cols, &fused, &fp, &g))
+        return EP_EINVAL;
+    if (fused) {
+        plan[0] = fp.kind;
+        plan[1] = fp.waves;
+        plan[2] = (int32_t)fp.blocks;
+        plan[3] = ep::kStepCols;
+    } else {
+        plan[0] = EP_PLAN_LAYOUT_THEN_DISPATCH;
+        plan[1] = g.waves;
+        plan[2] = g.max_blocks;
+        plan[3] = g.slice_steps * ep::kStepCols;
+    }
+    return EP_OK;
 }
 
 int ep_layout_dispatch_noalloc(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
@@ -209,24 +297,16 @@ int ep_layout_dispatch_noalloc(const int32_t* topk_idx, const uint16_t* x, int T
     return layout_dispatch_checked(topk_idx, x, T, H, K, E, P, payload, expert_count,
                                    expert_offset, part_count, part_offset, row_of_pair, src_pair,
                                    status, ws, need > 0 ? (size_t)EP_NOALLOC_SCRATCH_BYTES : 0,
-                                   recv_x, recv_scales, stream);
+                                   recv_x, recv_scales, 0, 0, 0, stream);
 }
-
-namespace {
-
-bool geometry_ok(int waves_per_block, int max_blocks)
-{
-    return (waves_per_block == 1 || waves_per_block == 2 || waves_per_block == 4 ||
-            waves_per_block == 8) && max_blocks >= 0;
-}
-
-}  // namespace
 
 int ep_dispatch_geom(const uint16_t* x, int T, int H, int K, const int32_t* row_of_pair,
                      int payload, void* recv_x, float* recv_scales, int waves_per_block,
-                     int max_blocks, void* stream)
+                     int max_blocks, int slice_cols, void* stream)
 {
-    if (!geometry_ok(waves_per_block, max_blocks)) return EP_EINVAL;
+    ep::MoveGeometry g;
+    if (waves_per_block == 0 || !move_geometry(waves_per_block, max_blocks, slice_cols, &g))
+        return EP_EINVAL;
     if (payload != EP_PAYLOAD_FP8_E4M3FN && payload != EP_PAYLOAD_BF16) return EP_ENOTSUP;
     if (!routing_ok(T, K) || H <= 0) return EP_EINVAL;
     if (payload == EP_PAYLOAD_FP8_E4M3FN && H % ep::kScaleBlock != 0) return EP_EINVAL;
@@ -234,23 +314,25 @@ int ep_dispatch_geom(const uint16_t* x, int T, int H, int K, const int32_t* row_
     if (T == 0) return EP_OK;
     if (!ptr_ok(x, 16) || !ptr_ok(row_of_pair, 4) || !ptr_ok(recv_x, 16)) return EP_EINVAL;
     if (payload == EP_PAYLOAD_FP8_E4M3FN && !ptr_ok(recv_scales, 4)) return EP_EINVAL;
+    if (!ep::dispatch_launch_ok(T, H, g)) return EP_EINVAL;
     return from_hip(ep::launch_dispatch(x, T, H, K, row_of_pair, payload, recv_x, recv_scales,
-                                        (hipStream_t)stream,
-                                        ep::MoveGeometry{waves_per_block, max_blocks}));
+                                        (hipStream_t)stream, g));
 }
 
 int ep_combine_geom(const uint16_t* expert_out, const int32_t* row_of_pair, const float* topk_w,
                     int T, int H, int K, uint16_t* out, int waves_per_block, int max_blocks,
-                    void* stream)
+                    int slice_cols, void* stream)
 {
-    if (!geometry_ok(waves_per_block, max_blocks)) return EP_EINVAL;
+    ep::MoveGeometry g;
+    if (waves_per_block == 0 || !move_geometry(waves_per_block, max_blocks, slice_cols, &g))
+        return EP_EINVAL;
     if (!routing_ok(T, K) || H <= 0 || H % ep::kColsPerLane != 0) return EP_EINVAL;
     if (T == 0) return EP_OK;
     if (!ptr_ok(expert_out, 16) || !ptr_ok(row_of_pair, 4) || !ptr_ok(topk_w, 4) || !ptr_ok(out, 16))
         return EP_EINVAL;
+    if (!ep::combine_launch_ok(T, H, g)) return EP_EINVAL;
     return from_hip(ep::launch_combine(expert_out, row_of_pair, topk_w, T, H, K, out,
-                                       (hipStream_t)stream,
-                                       ep::MoveGeometry{waves_per_block, max_blocks}));
+                                       (hipStream_t)stream, g));
 }
 
 int ep_combine(const uint16_t* expert_out, const int32_t* row_of_pair, const float* topk_w, int T,
@@ -260,6 +342,7 @@ int ep_combine(const uint16_t* expert_out, const int32_t* row_of_pair, const flo
     if (T == 0) return EP_OK;
     if (!ptr_ok(expert_out, 16) || !ptr_ok(row_of_pair, 4) || !ptr_ok(topk_w, 4) || !ptr_ok(out, 16))
         return EP_EINVAL;
+    if (!ep::combine_launch_ok(T, H, ep::kDefaultGeometry)) return EP_EINVAL;
     return from_hip(ep::launch_combine(expert_out, row_of_pair, topk_w, T, H, K, out,
                                        (hipStream_t)stream));
 }
@@ -322,6 +405,7 @@ int ep_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, 
     }
     const size_t need = ep_dedup_layout_dispatch_workspace_bytes(T, K, E, P);
     if (need > 0 && (ws_bytes < need || !ptr_ok(ws, 16))) return EP_EINVAL;
+    if (!ep::dispatch_launch_ok(T, H, ep::kDefaultGeometry)) return EP_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     if (T > 0 && ep::fused_layout_dispatch_fits(T, H, K))
         return from_hip(ep::launch_dedup_layout_dispatch(
@@ -350,6 +434,7 @@ int ep_combine_partial(const uint16_t* expert_out, const int32_t* row_of_pair,
     if (!ptr_ok(expert_out, 16) || !ptr_ok(row_of_pair, 4) || !ptr_ok(topk_w, 4) ||
         !ptr_ok(tp_row, 4) || !ptr_ok(kmask, 4) || !ptr_ok(partial, 16))
         return EP_EINVAL;
+    if (!ep::combine_launch_ok(T, H, ep::kDefaultGeometry)) return EP_EINVAL;
     return from_hip(ep::launch_combine_partial(expert_out, row_of_pair, topk_w, tp_row, kmask, T, H,
                                                K, P, partial, (hipStream_t)stream));
 }
@@ -360,6 +445,7 @@ int ep_combine_reduce(const uint16_t* partial, const int32_t* tp_row, int T, int
     if (!dedup_ok(T, P) || H <= 0 || H % ep::kColsPerLane != 0) return EP_EINVAL;
     if (T == 0) return EP_OK;
     if (!ptr_ok(partial, 16) || !ptr_ok(tp_row, 4) || !ptr_ok(out, 16)) return EP_EINVAL;
+    if (!ep::combine_launch_ok(T, H, ep::kDefaultGeometry)) return EP_EINVAL;
     return from_hip(ep::launch_combine_reduce(partial, tp_row, T, H, P, out, (hipStream_t)stream));
 }
 

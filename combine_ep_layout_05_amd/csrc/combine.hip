@@ -161,13 +161,16 @@ __device__ __forceinline__ void partial_in_order(const uint16_t* __restrict__ y,
 // taken in ascending p), reduces the entries of kmask[t*P+p] into row
 // tp_row[t*P+p] of `out`: every expert row is read once, as in the plain
 // combine, and no wave is spent on (token, partition) couples without a copy.
-template <int kMaxK, bool kStream, int kMode, bool kOnce>
+// kSub: 512-column steps per item (the slice of the launch geometry, 1 or 2;
+// the partial mode takes 1), items_per_token = ceil(steps / kSub).
+template <int kMaxK, bool kStream, int kMode, int kSub, bool kOnce>
 __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
     const uint16_t* __restrict__ y, const int32_t* __restrict__ row_of_pair,
     const float* __restrict__ topk_w, int H, int K, uint16_t* __restrict__ out,
-    int steps_per_token, int n_items, int n_rows,
+    int items_per_token, int n_items, int n_rows,
     const int32_t* __restrict__ tp_row, const uint32_t* __restrict__ kmask, int P, int out_rows)
 {
+    static_assert(kSub == 1 || kMode != kPartial, "the partial mode takes one step per item");
     const int lane = threadIdx.x % kWave;
     const int waves = blockDim.x / kWave;
     const int stride = gridDim.x * waves;
@@ -180,8 +183,9 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
     // partial mode: per wave, the entries in (partition, k) order
     __shared__ int4 s_ord[kMode == kPartial ? kMaxMoveWaves : 1][kMaxTopK];
     auto run = [&](int item) {
-        const int t = item / steps_per_token;
-        const int col0 = (item - t * steps_per_token) * kStepCols + lane * kColsPerLane;
+        const int t = item / items_per_token;
+        const int col_base = (item - t * items_per_token) * (kSub * kStepCols);
+        const int col0 = col_base + lane * kColsPerLane;
         const bool active = col0 < H;
         // metadata loads without a branch around them (lanes past K or P read
         // a valid entry, whose value is then dropped): a load under a branch
@@ -255,7 +259,8 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
             // what is not a row), so the loads go out back to back and the
             // loop waits for them one at a time.  Reduce mode skips absent
             // couples with a uniform branch instead: most of a token's P
-            // couples are absent when P is large.
+            // couples are absent when P is large.  With kSub = 2 each row's
+            // two 16-byte pieces (columns 512 apart) are loaded together.
             int rows[kMaxK];
             float wts[kMaxK];
 #pragma unroll
@@ -263,40 +268,57 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
                 rows[k] = (k < K) ? read_lane(myrow, k) : -1;
                 wts[k] = __builtin_bit_cast(float, read_lane(__builtin_bit_cast(int, myw), k));
             }
-            const int cl = active ? col0 : 0;
-            uint4 v[kMaxK];
+            int cl[kSub];
+#pragma unroll
+            for (int u = 0; u < kSub; ++u) {
+                const int c = col0 + u * kStepCols;
+                cl[u] = c < H ? c : 0;
+            }
+            uint4 v[kMaxK][kSub];
 #pragma unroll
             for (int k = 0; k < kMaxK; ++k) {
-                if constexpr (kMode == kReduce) {
-                    v[k] = make_uint4(0, 0, 0, 0);
-                    if (rows[k] >= 0) v[k] = load16<kStream>(y + (int64_t)rows[k] * H + cl);
-                } else {
-                    v[k] = load16<kStream>(y + (int64_t)(rows[k] >= 0 ? rows[k] : 0) * H + cl);
+#pragma unroll
+                for (int u = 0; u < kSub; ++u) {
+                    if constexpr (kMode == kReduce) {
+                        v[k][u] = make_uint4(0, 0, 0, 0);
+                        if (rows[k] >= 0) v[k][u] = load16<kStream>(y + (int64_t)rows[k] * H + cl[u]);
+                    } else {
+                        v[k][u] = load16<kStream>(y + (int64_t)(rows[k] >= 0 ? rows[k] : 0) * H + cl[u]);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);      // issue in k order, the fmaf order
             }
-            float acc[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+            for (int u = 0; u < kSub; ++u) {
+                float acc[8];
 #pragma unroll
-            for (int k = 0; k < kMaxK; ++k) {
-                if (rows[k] >= 0) {
-                    acc[0] = __builtin_fmaf(wts[k], bf16_lo(v[k].x), acc[0]);
-                    acc[1] = __builtin_fmaf(wts[k], bf16_hi(v[k].x), acc[1]);
-                    acc[2] = __builtin_fmaf(wts[k], bf16_lo(v[k].y), acc[2]);
-                    acc[3] = __builtin_fmaf(wts[k], bf16_hi(v[k].y), acc[3]);
-                    acc[4] = __builtin_fmaf(wts[k], bf16_lo(v[k].z), acc[4]);
-                    acc[5] = __builtin_fmaf(wts[k], bf16_hi(v[k].z), acc[5]);
-                    acc[6] = __builtin_fmaf(wts[k], bf16_lo(v[k].w), acc[6]);
-                    acc[7] = __builtin_fmaf(wts[k], bf16_hi(v[k].w), acc[7]);
+                for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+#pragma unroll
+                for (int k = 0; k < kMaxK; ++k) {
+                    if (rows[k] >= 0) {
+                        acc[0] = __builtin_fmaf(wts[k], bf16_lo(v[k][u].x), acc[0]);
+                        acc[1] = __builtin_fmaf(wts[k], bf16_hi(v[k][u].x), acc[1]);
+                        acc[2] = __builtin_fmaf(wts[k], bf16_lo(v[k][u].y), acc[2]);
+                        acc[3] = __builtin_fmaf(wts[k], bf16_hi(v[k][u].y), acc[3]);
+                        acc[4] = __builtin_fmaf(wts[k], bf16_lo(v[k][u].z), acc[4]);
+                        acc[5] = __builtin_fmaf(wts[k], bf16_hi(v[k][u].z), acc[5]);
+                        acc[6] = __builtin_fmaf(wts[k], bf16_lo(v[k][u].w), acc[6]);
+                        acc[7] = __builtin_fmaf(wts[k], bf16_hi(v[k][u].w), acc[7]);
+                    }
                 }
+                uint4 o;
+                o.x = pack2_bf16(acc[0], acc[1]);
+                o.y = pack2_bf16(acc[2], acc[3]);
+                o.z = pack2_bf16(acc[4], acc[5]);
+                o.w = pack2_bf16(acc[6], acc[7]);
+                // the output row is nontemporal at every size: no later access
+                // of this launch or the next one wants it in L2 (128 x 7168
+                // top-8, graphs of 50 steps on MI355X: step 6.97 -> 6.78 us
+                // warm, 9.94 -> 9.41 us over 16 rotating input sets; 4 and 4096
+                // tokens unchanged)
+                const int c = col0 + u * kStepCols;
+                if (c < H) store16<true>(out + (int64_t)t * H + c, o);
             }
-            uint4 o;
-            o.x = pack2_bf16(acc[0], acc[1]);
-            o.y = pack2_bf16(acc[2], acc[3]);
-            o.z = pack2_bf16(acc[4], acc[5]);
-            o.w = pack2_bf16(acc[6], acc[7]);
-            if (active) store16<kStream>(out + (int64_t)t * H + col0, o);
         } else {
             // level 1 with overlapping masks: for each copy in ascending p, the
             // entries of its mask in ascending k
@@ -331,10 +353,12 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
 
 constexpr int64_t kMaxGridBlocks = 1 << 20;
 
-// Streaming (nontemporal) expert-output reads and output writes once the
-// gathered rows exceed what the caches can usefully hold: measured on MI355X
-// at 4096 x 7168 top-8 right after a dispatch, the combine went 132 -> 96 us
-// because its once-read rows no longer evict the dispatch's fresh lines.
+// Streaming (nontemporal) expert-output reads (and partial-row writes) once
+// the gathered rows exceed what the caches can usefully hold: measured on
+// MI355X at 4096 x 7168 top-8 right after a dispatch, the combine went 132 ->
+// 96 us because its once-read rows no longer evict the dispatch's fresh lines.
+// Below that the reads stay cached: nontemporal reads of cache-resident rows
+// measured slower (128 x 7168 step 6.97 -> 7.42 us).
 // EP_FORCE_POLICY (build option for A/B runs): 1 = cached combine accesses,
 // 2 or more = streaming ones, whatever the size.
 bool combine_streams(int64_t gathered_rows, int H)
@@ -348,6 +372,14 @@ bool combine_streams(int64_t gathered_rows, int H)
 
 }  // namespace
 
+bool combine_launch_ok(int n_units, int H, MoveGeometry g)
+{
+    if (g.waves < 1 || g.waves > kMaxMoveWaves || g.max_blocks < 0) return false;
+    if (g.slice_steps != 1 && g.slice_steps != 2) return false;
+    const int64_t per_unit = (int64_t)(H + g.slice_steps * kStepCols - 1) / (g.slice_steps * kStepCols);
+    return (int64_t)n_units * per_unit + kMaxGridBlocks * kMaxMoveWaves < ((int64_t)1 << 31);
+}
+
 namespace {
 
 template <int kMode>
@@ -357,25 +389,32 @@ hipError_t launch_combine_mode(const uint16_t* y, const int32_t* row_of_pair,
                                int64_t gathered_rows, uint16_t* out, hipStream_t stream,
                                MoveGeometry g)
 {
-    const int steps = (H + kStepCols - 1) / kStepCols;
-    const int64_t items = (int64_t)n_units * steps;
+    if (!combine_launch_ok(n_units, H, g) || (kMode == kPartial && g.slice_steps != 1))
+        return hipErrorInvalidValue;                   // checked by the API first
+    const int per_unit = (H + g.slice_steps * kStepCols - 1) / (g.slice_steps * kStepCols);
+    const int64_t items = (int64_t)n_units * per_unit;
     if (items == 0) return hipSuccess;
-    if (g.waves < 1 || g.waves > kMaxMoveWaves || g.max_blocks < 0) return hipErrorInvalidValue;
-    if (items + kMaxGridBlocks * kMaxMoveWaves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     int64_t blocks = (items + g.waves - 1) / g.waves;
     if (g.max_blocks > 0 && blocks > g.max_blocks) blocks = g.max_blocks;
     if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
     const bool stream_policy = combine_streams(gathered_rows, H);
     const bool once = blocks * g.waves >= items;
-    using Kernel = decltype(&combine_kernel<8, true, kMode, true>);
-    const Kernel table[2][2][2] = {
-        {{combine_kernel<8, false, kMode, false>, combine_kernel<8, false, kMode, true>},
-         {combine_kernel<8, true, kMode, false>, combine_kernel<8, true, kMode, true>}},
-        {{combine_kernel<16, false, kMode, false>, combine_kernel<16, false, kMode, true>},
-         {combine_kernel<16, true, kMode, false>, combine_kernel<16, true, kMode, true>}}};
-    const Kernel k = table[K <= 8 ? 0 : 1][stream_policy ? 1 : 0][once ? 1 : 0];
+    constexpr int kS2 = kMode == kPartial ? 1 : 2;     // the partial mode has no 2-step slice
+    using Kernel = decltype(&combine_kernel<8, true, kMode, 1, true>);
+    // [K <= 8 ? 0 : 1][streaming][slice of 1 or 2 steps][one item per wave]
+    const Kernel table[2][2][2][2] = {
+        {{{combine_kernel<8, false, kMode, 1, false>, combine_kernel<8, false, kMode, 1, true>},
+          {combine_kernel<8, false, kMode, kS2, false>, combine_kernel<8, false, kMode, kS2, true>}},
+         {{combine_kernel<8, true, kMode, 1, false>, combine_kernel<8, true, kMode, 1, true>},
+          {combine_kernel<8, true, kMode, kS2, false>, combine_kernel<8, true, kMode, kS2, true>}}},
+        {{{combine_kernel<16, false, kMode, 1, false>, combine_kernel<16, false, kMode, 1, true>},
+          {combine_kernel<16, false, kMode, kS2, false>, combine_kernel<16, false, kMode, kS2, true>}},
+         {{combine_kernel<16, true, kMode, 1, false>, combine_kernel<16, true, kMode, 1, true>},
+          {combine_kernel<16, true, kMode, kS2, false>, combine_kernel<16, true, kMode, kS2, true>}}}};
+    const Kernel k = table[K <= 8 ? 0 : 1][stream_policy ? 1 : 0][g.slice_steps == 2 ? 1 : 0]
+                          [once ? 1 : 0];
     hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(g.waves * kWave), 0, stream, y, row_of_pair,
-                       topk_w, H, K, out, steps, (int)items, n_rows, tp_row, kmask, P, out_rows);
+                       topk_w, H, K, out, per_unit, (int)items, n_rows, tp_row, kmask, P, out_rows);
     return hipGetLastError();
 }
 
@@ -386,7 +425,7 @@ hipError_t launch_combine_mode(const uint16_t* y, const int32_t* row_of_pair,
 MoveGeometry dedup_geometry(int T, int H)
 {
     const int64_t items = (int64_t)T * ((H + kStepCols - 1) / kStepCols);
-    return MoveGeometry{items > 4 * kCUs ? 8 : 4, 0};
+    return MoveGeometry{items > 4 * kCUs ? 8 : 4, 0, 1};
 }
 
 }  // namespace

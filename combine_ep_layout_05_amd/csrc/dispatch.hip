@@ -45,80 +45,118 @@
 namespace ep {
 namespace {
 
-// Write one item to the receive rows of its token's entries: the fp8 bytes
-// q and the block scales (kPayload 0) or the bf16 vector v unchanged
-// (kPayload 1).  Lanes lane0 .. lane0+K-1 of `myrow` hold the rows of the
-// token's entries 0..K-1 (K <= kMaxRows); rows outside [0, n_rows) --
-// masked entries -- are skipped.  col_base is the item's first column.
+// Write one item to the receive rows of its token's entries.  An item is
+// kSub consecutive 512-column steps of one token (one wave, 8 columns per
+// lane and step); step s holds the fp8 bytes q[s] and the block scales
+// scale[s] (kPayload 0) or the bf16 vector v[s] unchanged (kPayload 1).
+// Lanes lane0 .. lane0+K-1 of `myrow` hold the rows of the token's entries
+// 0..K-1 (K <= kMaxRows); rows outside [0, n_rows) -- masked entries -- are
+// skipped.  col_base is the item's first column.
 //   - Payload: an unrolled loop over the entries.  A row's base address is
 //     formed in scalar registers and this lane's byte offset stays in one
 //     vector register, so a row costs one lane read, a few scalar
-//     instructions and one store (the scalar-base store form); a uniform
-//     test skips a masked row, and when the whole 512-column step lies
-//     inside the row the loop runs without a per-lane column mask.
-//   - fp8 scales: the item's 4 block scales (lanes 0, 16, 32, 48) go to each
-//     row as one 16-byte store made by the lane that holds the row, instead
-//     of four lanes storing 4 bytes into every row under a lane mask.
+//     instructions and one store per step (the scalar-base store form); a
+//     uniform test skips a masked row, and when the item lies inside the row
+//     the loop runs without per-lane column masks.
+//   - fp8 scales: the item's block scales (lanes 0, 16, 32, 48 of each step)
+//     go to each row as one 16-byte store per step, made by the lane that
+//     holds the row, instead of four lanes storing 4 bytes into every row
+//     under a lane mask.
 // The payload stores are nontemporal (the receive rows are read by the expert
 // computation, not by this launch again), in every dispatch kernel and at
-// every batch size.  Measured on MI355X against cached
-// stores, graphs of 50 steps, top-8, even with everything cache resident:
-// 128 x 7168 the fused launch 4.40 -> 4.30 us and the step with the combine
-// after it 7.31 -> 6.89 us (with 16 rotating input sets, nothing left in the
-// caches: 11.7 -> 10.1 us); 600 x 7168, unfused dispatch, step 32.5 -> 29.2
-// us.
-template <int kPayload, int kMaxRows>
-__device__ __forceinline__ void store_rows(uint4 v, uint2 q, float scale, int myrow, int lane0,
+// every batch size.  Measured on MI355X against cached stores, graphs of 50
+// steps, top-8, even with everything cache resident: 128 x 7168 the fused
+// launch 4.40 -> 4.30 us and the step with the combine after it 7.31 -> 6.89
+// us (with 16 rotating input sets, nothing left in the caches: 11.7 -> 10.1
+// us); 600 x 7168, unfused dispatch, step 32.5 -> 29.2 us.
+template <int kPayload, int kMaxRows, int kSub>
+__device__ __forceinline__ void store_rows(const uint4 (&v_in)[kSub], const uint2 (&q)[kSub],
+                                           const float (&scale)[kSub], int myrow, int lane0,
                                            int col_base, int lane, int H, int K, int n_rows,
                                            uint8_t* __restrict__ recv_x,
                                            float* __restrict__ recv_scales)
 {
     constexpr int kBytes = kPayload == 0 ? 1 : 2;
-    // The bf16 store data is the loaded x vector: wait for it once here.  A
-    // wait for a load is a wait for every earlier store too (one counter on
-    // this architecture), and the compiler would otherwise put one in front
-    // of every row's store, each row being a block of its own.
-    if constexpr (kPayload == 1) asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+    uint4 v[kSub];
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+        v[u] = v_in[u];
+        // The bf16 store data is the loaded x vector: wait for it once here.
+        // A wait for a load is a wait for every earlier store too (one
+        // counter on this architecture), and the compiler would otherwise
+        // put one in front of every row's store, each row being a block of
+        // its own.
+        if constexpr (kPayload == 1)
+            asm volatile("" : "+v"(v[u].x), "+v"(v[u].y), "+v"(v[u].z), "+v"(v[u].w));
+    }
     const uint32_t voff = (uint32_t)(col_base + lane * kColsPerLane) * kBytes;
-    auto row_loop = [&](bool lane_ok) {
+    auto row_loop = [&](bool full) {
+        bool lane_ok[kSub];
+#pragma unroll
+        for (int u = 0; u < kSub; ++u)
+            lane_ok[u] = full || col_base + u * kStepCols + lane * kColsPerLane < H;
 #pragma unroll
         for (int k = 0; k < kMaxRows; ++k) {
             if (k < K) {
                 const uint32_t r = (uint32_t)read_lane(myrow, lane0 + k);
                 if (r < (uint32_t)n_rows) {                    // uniform: a row, not masked
                     uint8_t* rowp = recv_x + (uint64_t)r * (uint32_t)(H * kBytes);
-                    if (lane_ok) {
-                        if constexpr (kPayload == 0) store8<true>(rowp + voff, q);
-                        else store16<true>(rowp + voff, v);
+#pragma unroll
+                    for (int u = 0; u < kSub; ++u) {
+                        const uint32_t o = voff + (uint32_t)(u * kStepCols * kBytes);
+                        if (lane_ok[u]) {
+                            if constexpr (kPayload == 0) store8<true>(rowp + o, q[u]);
+                            else store16<true>(rowp + o, v[u]);
+                        }
                     }
                 }
             }
         }
     };
-    if (col_base + kStepCols <= H) row_loop(true);              // uniform
-    else row_loop(col_base + lane * kColsPerLane < H);
+    if (col_base + kSub * kStepCols <= H) row_loop(true);       // uniform
+    else row_loop(false);
     if constexpr (kPayload == 0) {
-        const int sb = __builtin_bit_cast(int, scale);
-        const float s0 = __builtin_bit_cast(float, read_lane(sb, 0));
-        const float s1 = __builtin_bit_cast(float, read_lane(sb, kLanesPerScaleBlock));
-        const float s2 = __builtin_bit_cast(float, read_lane(sb, 2 * kLanesPerScaleBlock));
-        const float s3 = __builtin_bit_cast(float, read_lane(sb, 3 * kLanesPerScaleBlock));
+        constexpr int kBlk = kStepCols / kScaleBlock;            // 4 scales per step
+        float sc[kSub * kBlk];
+#pragma unroll
+        for (int u = 0; u < kSub; ++u)
+#pragma unroll
+            for (int b = 0; b < kBlk; ++b)
+                sc[u * kBlk + b] = __builtin_bit_cast(
+                    float, read_lane(__builtin_bit_cast(int, scale[u]), b * kLanesPerScaleBlock));
         const uint32_t nsc = (uint32_t)H / kScaleBlock;          // scales per row
         const uint32_t b0 = (uint32_t)col_base / kScaleBlock;    // the item's first block
-        const uint32_t nblk = nsc - b0 < 4u ? nsc - b0 : 4u;     // 4 unless the step is partial
+        const uint32_t nblk = nsc - b0 < (uint32_t)(kSub * kBlk) ? nsc - b0 : kSub * kBlk;
         const uint32_t k = (uint32_t)(lane - lane0);
         if (k < (uint32_t)K && (uint32_t)myrow < (uint32_t)n_rows) {
             float* sp = recv_scales + (uint64_t)(uint32_t)myrow * nsc + b0;
-            if (nblk == 4u && (nsc & 3u) == 0u) {               // 16-byte aligned: one store
-                *reinterpret_cast<float4*>(sp) = make_float4(s0, s1, s2, s3);
+            if (nblk == (uint32_t)(kSub * kBlk) && (nsc & 3u) == 0u) {   // 16-byte aligned
+#pragma unroll
+                for (int u = 0; u < kSub; ++u)
+                    *reinterpret_cast<float4*>(sp + u * kBlk) =
+                        make_float4(sc[u * kBlk], sc[u * kBlk + 1], sc[u * kBlk + 2],
+                                    sc[u * kBlk + 3]);
             } else {
-                sp[0] = s0;
-                if (nblk > 1u) sp[1] = s1;
-                if (nblk > 2u) sp[2] = s2;
-                if (nblk > 3u) sp[3] = s3;
+#pragma unroll
+                for (int b = 0; b < kSub * kBlk; ++b)
+                    if ((uint32_t)b < nblk) sp[b] = sc[b];
             }
         }
     }
+}
+
+// One 512-column step: the form the fused kernels use.
+template <int kPayload, int kMaxRows>
+__device__ __forceinline__ void store_rows(uint4 v, uint2 q, float scale, int myrow, int lane0,
+                                           int col_base, int lane, int H, int K, int n_rows,
+                                           uint8_t* __restrict__ recv_x,
+                                           float* __restrict__ recv_scales)
+{
+    const uint4 va[1] = {v};
+    const uint2 qa[1] = {q};
+    const float sa[1] = {scale};
+    store_rows<kPayload, kMaxRows, 1>(va, qa, sa, myrow, lane0, col_base, lane, H, K, n_rows,
+                                      recv_x, recv_scales);
 }
 
 // Quantise (fp8) one item; must be called by all 64 lanes of the wave (the
@@ -131,11 +169,14 @@ __device__ __forceinline__ uint2 prepare_item(uint4 v, float& scale)
     return make_uint2(0u, 0u);
 }
 
-template <int kPayload, int kMaxK, bool kOnce>
+// An item is kSub consecutive 512-column steps of one token (the slice of
+// the launch geometry: 512 or 1024 columns); items_per_token = ceil(steps /
+// kSub), the last item of a token possibly partial.
+template <int kPayload, int kMaxK, int kSub, bool kOnce>
 __global__ __launch_bounds__(kMaxMoveWaves * kWave) void dispatch_kernel(
     const uint16_t* __restrict__ x, int H, int K, const int32_t* __restrict__ row_of_pair,
     uint8_t* __restrict__ recv_x, float* __restrict__ recv_scales,
-    int steps_per_token, int n_items, int n_rows)
+    int items_per_token, int n_items, int n_rows)
 {
     const int lane = threadIdx.x % kWave;
     const int waves = blockDim.x / kWave;
@@ -144,51 +185,59 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void dispatch_kernel(
     if (item >= n_items) return;
 
     // load stage of one item: row ids (lanes < K) and this lane's 16 bytes of
-    // x, both loads without a branch around them (lanes past K read entry 0,
-    // columns past H read column 0; the values are dropped)
-    auto load_item = [&](int it, int& myrow, uint4& v, int& col0) {
-        const int t = it / steps_per_token;
-        col0 = (it - t * steps_per_token) * kStepCols + lane * kColsPerLane;
+    // x per step, all loads without a branch around them (lanes past K read
+    // entry 0, columns past H read column 0; the values are dropped)
+    auto load_item = [&](int it, int& myrow, uint4 (&v)[kSub], int& col_base) {
+        const int t = it / items_per_token;
+        col_base = (it - t * items_per_token) * (kSub * kStepCols);
         myrow = row_of_pair[(int64_t)t * K + (lane < K ? lane : 0)];
-        v = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + (col0 < H ? col0 : 0));
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) {
+            const int c = col_base + u * kStepCols + lane * kColsPerLane;
+            v[u] = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + (c < H ? c : 0));
+        }
+    };
+    auto quantise_and_store = [&](const uint4 (&v)[kSub], int myrow, int col_base) {
+        float scale[kSub];
+        uint2 q[kSub];
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) q[u] = prepare_item<kPayload>(v[u], scale[u]);
+        store_rows<kPayload, kMaxK, kSub>(v, q, scale, myrow, 0, col_base, lane, H, K, n_rows,
+                                          recv_x, recv_scales);
     };
 
-    int myrow, col0;
-    uint4 v;
-    load_item(item, myrow, v, col0);
+    int myrow, col_base;
+    uint4 v[kSub];
+    load_item(item, myrow, v, col_base);
     if constexpr (kOnce) {               // the grid covers every item: no prefetch loop
         // the row ids pinned where they are loaded, so the compiler does not
         // sink the load into the lanes < K (with a lazy argument load and a
         // wait of its own); x is waited for next anyway
         asm volatile("" : "+v"(myrow));
         if (lane >= K) myrow = -1;
-        float scale;
-        const uint2 q = prepare_item<kPayload>(v, scale);
-        store_rows<kPayload, kMaxK>(v, q, scale, myrow, 0, col0 - lane * kColsPerLane, lane,
-                                          H, K, n_rows, recv_x, recv_scales);
+        quantise_and_store(v, myrow, col_base);
         return;
     }
 
     if (lane >= K) myrow = -1;
     while (true) {
         const int next = item + stride;      // n_items + stride < 2^31 (checked by the launcher)
-        int nrow = -1, ncol0 = 0;
-        uint4 nv = make_uint4(0, 0, 0, 0);
+        int nrow = -1, ncol = 0;
+        uint4 nv[kSub];
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) nv[u] = make_uint4(0, 0, 0, 0);
         if (next < n_items) {
-            load_item(next, nrow, nv, ncol0);
+            load_item(next, nrow, nv, ncol);
             if (lane >= K) nrow = -1;
         }
 
-        float scale;
-        const uint2 q = prepare_item<kPayload>(v, scale);
-        store_rows<kPayload, kMaxK>(v, q, scale, myrow, 0, col0 - lane * kColsPerLane, lane,
-                                          H, K, n_rows, recv_x, recv_scales);
+        quantise_and_store(v, myrow, col_base);
 
         if (next >= n_items) break;
         item = next;
         myrow = nrow;
-        v = nv;
-        col0 = ncol0;
+        for (int u = 0; u < kSub; ++u) v[u] = nv[u];
+        col_base = ncol;
     }
 }
 
@@ -527,7 +576,7 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
 constexpr int kTinyPairs = 2 * kWave;
 
 template <int kPayload, int kOwn>
-__global__ __launch_bounds__(kMoveThreads) void layout_dispatch_tiny_kernel(
+__global__ __launch_bounds__(kMaxMoveWaves * kWave) void layout_dispatch_tiny_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, int n, int H, int K, int E,
     int P, int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset,
     int32_t* __restrict__ part_count, int32_t* __restrict__ part_offset,
@@ -938,29 +987,42 @@ constexpr int64_t kMaxGridBlocks = 1 << 20;
 
 }  // namespace
 
+bool dispatch_launch_ok(int T, int H, MoveGeometry g)
+{
+    if (g.waves < 1 || g.waves > kMaxMoveWaves || g.max_blocks < 0) return false;
+    if (g.slice_steps != 1 && g.slice_steps != 2) return false;
+    const int64_t per_token = (int64_t)(H + g.slice_steps * kStepCols - 1) / (g.slice_steps * kStepCols);
+    return (int64_t)T * per_token + kMaxGridBlocks * kMaxMoveWaves < ((int64_t)1 << 31);
+}
+
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, const int32_t* row_of_pair,
                            int payload, void* recv_x, float* recv_scales, hipStream_t stream,
                            MoveGeometry g)
 {
-    const int steps = (H + kStepCols - 1) / kStepCols;
-    const int64_t items = (int64_t)T * steps;
+    if (!dispatch_launch_ok(T, H, g)) return hipErrorInvalidValue;   // checked by the API first
+    const int per_token = (H + g.slice_steps * kStepCols - 1) / (g.slice_steps * kStepCols);
+    const int64_t items = (int64_t)T * per_token;
     if (items == 0) return hipSuccess;
-    if (g.waves < 1 || g.waves > kMaxMoveWaves || g.max_blocks < 0) return hipErrorInvalidValue;
-    if (items + kMaxGridBlocks * kMaxMoveWaves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     int64_t blocks = (items + g.waves - 1) / g.waves;
     if (g.max_blocks > 0 && blocks > g.max_blocks) blocks = g.max_blocks;
     if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
     const bool once = blocks * g.waves >= items;
-    using Kernel = decltype(&dispatch_kernel<0, 8, true>);
-    const Kernel table[2][2][2] = {
-        {{dispatch_kernel<0, 8, false>, dispatch_kernel<0, 8, true>},
-         {dispatch_kernel<0, 16, false>, dispatch_kernel<0, 16, true>}},
-        {{dispatch_kernel<1, 8, false>, dispatch_kernel<1, 8, true>},
-         {dispatch_kernel<1, 16, false>, dispatch_kernel<1, 16, true>}}};
-    const Kernel k = table[payload == 0 ? 0 : 1][K <= 8 ? 0 : 1][once ? 1 : 0];
+    using Kernel = decltype(&dispatch_kernel<0, 8, 1, true>);
+    // [payload][K <= 8 ? 0 : 1][slice of 1 or 2 steps][one item per wave]
+    const Kernel table[2][2][2][2] = {
+        {{{dispatch_kernel<0, 8, 1, false>, dispatch_kernel<0, 8, 1, true>},
+          {dispatch_kernel<0, 8, 2, false>, dispatch_kernel<0, 8, 2, true>}},
+         {{dispatch_kernel<0, 16, 1, false>, dispatch_kernel<0, 16, 1, true>},
+          {dispatch_kernel<0, 16, 2, false>, dispatch_kernel<0, 16, 2, true>}}},
+        {{{dispatch_kernel<1, 8, 1, false>, dispatch_kernel<1, 8, 1, true>},
+          {dispatch_kernel<1, 8, 2, false>, dispatch_kernel<1, 8, 2, true>}},
+         {{dispatch_kernel<1, 16, 1, false>, dispatch_kernel<1, 16, 1, true>},
+          {dispatch_kernel<1, 16, 2, false>, dispatch_kernel<1, 16, 2, true>}}}};
+    const Kernel k =
+        table[payload == 0 ? 0 : 1][K <= 8 ? 0 : 1][g.slice_steps == 2 ? 1 : 0][once ? 1 : 0];
     hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(g.waves * kWave), 0, stream, x, H, K,
-                       row_of_pair, (uint8_t*)recv_x, payload == 0 ? recv_scales : nullptr, steps,
-                       (int)items, T * K);
+                       row_of_pair, (uint8_t*)recv_x, payload == 0 ? recv_scales : nullptr,
+                       per_token, (int)items, T * K);
     return hipGetLastError();
 }
 
@@ -1013,6 +1075,8 @@ hipError_t launch_fused(int W, const int32_t* topk_idx, const uint16_t* x, int n
                         int32_t* src_pair, uint32_t* status, void* recv_x, float* recv_scales,
                         int steps, int items, const DedupOutputs& dd, hipStream_t stream)
 {
+    // n >= 1: the kernel clamps its id addresses to n - 1
+    if (n < 1 || (W != 4 && W != 8)) return hipErrorInvalidValue;
     const unsigned blocks = (unsigned)((items + W - 1) / W);
     const bool small = n <= kFusedMaxPairs / 2;
     auto k = W == 8 ? (small ? layout_dispatch_kernel<kPayload, kDedup, 8, kFusedMaxPairs / 2>
@@ -1026,8 +1090,32 @@ hipError_t launch_fused(int W, const int32_t* topk_idx, const uint16_t* x, int n
     return hipGetLastError();
 }
 
-// The counting kernel's instance for a payload, workgroup size (8, 7 or 6
-// waves) and own-entry bound (8 or 16); one extra workgroup, launch block 0.
+// The counting kernel's instance for a payload, workgroup size (8, 7, 6 or,
+// for plain entries, 4 waves) and own-entry bound (8 or 16); one extra
+// workgroup, launch block 0.  n >= 1: the kernel clamps its id addresses to
+// n - 1.
+template <int kPayload, bool kDedup>
+auto count_kernel(int W, bool own8)
+{
+    using Kernel = decltype(&layout_dispatch_count_kernel<kPayload, kDedup, 8, 8>);
+    const Kernel w8[2] = {layout_dispatch_count_kernel<kPayload, kDedup, 8, 8>,
+                          layout_dispatch_count_kernel<kPayload, kDedup, 8, 16>};
+    const Kernel w7[2] = {layout_dispatch_count_kernel<kPayload, kDedup, 7, 8>,
+                          layout_dispatch_count_kernel<kPayload, kDedup, 7, 16>};
+    const Kernel w6[2] = {layout_dispatch_count_kernel<kPayload, kDedup, 6, 8>,
+                          layout_dispatch_count_kernel<kPayload, kDedup, 6, 16>};
+    const int o = own8 ? 0 : 1;
+    if (W == 8) return w8[o];
+    if (W == 7) return w7[o];
+    if (W == 6) return w6[o];
+    if constexpr (!kDedup) {
+        const Kernel w4[2] = {layout_dispatch_count_kernel<kPayload, kDedup, 4, 8>,
+                              layout_dispatch_count_kernel<kPayload, kDedup, 4, 16>};
+        if (W == 4) return w4[o];
+    }
+    return Kernel(nullptr);
+}
+
 template <bool kDedup>
 hipError_t launch_count(int payload, int W, bool own8, const int32_t* topk_idx, const uint16_t* x,
                         int n, int H, int K, int E, int P, int32_t* expert_count,
@@ -1036,15 +1124,8 @@ hipError_t launch_count(int payload, int W, bool own8, const int32_t* topk_idx, 
                         float* recv_scales, int steps, int items, const DedupOutputs& dd,
                         hipStream_t stream)
 {
-    using Kernel = decltype(&layout_dispatch_count_kernel<0, kDedup, 8, 8>);
-    const Kernel table[2][3][2] = {
-        {{layout_dispatch_count_kernel<0, kDedup, 8, 8>, layout_dispatch_count_kernel<0, kDedup, 8, 16>},
-         {layout_dispatch_count_kernel<0, kDedup, 7, 8>, layout_dispatch_count_kernel<0, kDedup, 7, 16>},
-         {layout_dispatch_count_kernel<0, kDedup, 6, 8>, layout_dispatch_count_kernel<0, kDedup, 6, 16>}},
-        {{layout_dispatch_count_kernel<1, kDedup, 8, 8>, layout_dispatch_count_kernel<1, kDedup, 8, 16>},
-         {layout_dispatch_count_kernel<1, kDedup, 7, 8>, layout_dispatch_count_kernel<1, kDedup, 7, 16>},
-         {layout_dispatch_count_kernel<1, kDedup, 6, 8>, layout_dispatch_count_kernel<1, kDedup, 6, 16>}}};
-    const Kernel k = table[payload == 0 ? 0 : 1][8 - W][own8 ? 0 : 1];
+    const auto k = payload == 0 ? count_kernel<0, kDedup>(W, own8) : count_kernel<1, kDedup>(W, own8);
+    if (k == nullptr || n < 1) return hipErrorInvalidValue;
     const unsigned blocks = (unsigned)((items + W - 1) / W) + 1;
     hipLaunchKernelGGL(k, dim3(blocks), dim3(W * kWave), 0, stream, topk_idx, x, n, H, K, E, P,
                        expert_count, expert_offset, part_count, part_offset, row_of_pair, src_pair,
@@ -1055,50 +1136,89 @@ hipError_t launch_count(int payload, int W, bool own8, const int32_t* topk_idx, 
 
 }  // namespace
 
+bool plan_layout_dispatch(int T, int H, int K, int waves, FusedPlan* plan)
+{
+    const int steps = (H + kStepCols - 1) / kStepCols;
+    const int64_t items = (int64_t)T * steps;
+    const int64_t n = (int64_t)T * K;
+    if (T < 1 || n > kFusedMaxPairs || items > kMaxGridBlocks || waves < 0) return false;
+    FusedPlan pl{};
+    if (n <= kTinyPairs) {
+        // one wave per item, waves per workgroup free (1, 2, 4 or 8; 4 by default)
+        pl.kind = kFusedTiny;
+        pl.waves = waves ? waves : kMoveWaves;
+        if (pl.waves != 1 && pl.waves != 2 && pl.waves != 4 && pl.waves != 8) return false;
+        pl.blocks = (unsigned)((items + pl.waves - 1) / pl.waves) + 1;
+        *plan = pl;
+        return true;
+    }
+    if (n <= kCountMaxPairs) {
+        // by default workgroups of 8, 7 or 6 waves, the largest that divides
+        // the steps per token (a workgroup then holds part of one token, or
+        // whole tokens), else 8; 4 on request; own entries at most 16
+        int W = waves;
+        if (W == 0) {
+            W = 8;
+            for (int c = 8; c >= 6; --c)
+                if (steps % c == 0 || c % steps == 0) { W = c; break; }
+        }
+        if (W == 4 || W == 6 || W == 7 || W == 8) {
+            const int own = max_own_tokens_exact(W, steps, (int)items) * K;
+            if (own <= 16) {
+                pl.kind = kFusedCount;
+                pl.waves = W;
+                pl.own8 = own <= 8;
+                pl.blocks = (unsigned)((items + W - 1) / W) + 1;
+                *plan = pl;
+                return true;
+            }
+        }
+        if (waves != 0 && waves != 4 && waves != 8) return false;   // not a general-kernel size
+    }
+    // the general kernel: 4 or 8 waves, the workgroup's own entries within one wave
+    pl.kind = kFusedGeneral;
+    pl.waves = waves ? waves : fused_waves(items, steps, K);
+    if (pl.waves != 4 && pl.waves != 8) return false;
+    if (max_own_tokens(pl.waves, steps) * K > kWave) return false;
+    pl.blocks = (unsigned)((items + pl.waves - 1) / pl.waves);
+    *plan = pl;
+    return true;
+}
+
 hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
                                   int E, int P, int payload, int32_t* expert_count,
                                   int32_t* expert_offset, int32_t* part_count,
                                   int32_t* part_offset, int32_t* row_of_pair, int32_t* src_pair,
                                   uint32_t* status, void* recv_x, float* recv_scales,
-                                  hipStream_t stream)
+                                  hipStream_t stream, int waves)
 {
+    FusedPlan pl;
+    if (!plan_layout_dispatch(T, H, K, waves, &pl)) return hipErrorInvalidValue;  // checked first
     const int steps = (H + kStepCols - 1) / kStepCols;
-    const int64_t items = (int64_t)T * steps;
+    const int items = T * steps;
     const int n = T * K;
-    if (T == 0 || n > kFusedMaxPairs || items > kMaxGridBlocks) return hipErrorInvalidValue;
-    if (n <= kTinyPairs) {
-        const unsigned blocks = (unsigned)((items + kMoveWaves - 1) / kMoveWaves) + 1;
+    if (pl.kind == kFusedTiny) {
         auto k = payload == 0 ? (K <= 8 ? layout_dispatch_tiny_kernel<0, 8> : layout_dispatch_tiny_kernel<0, 16>)
                               : (K <= 8 ? layout_dispatch_tiny_kernel<1, 8> : layout_dispatch_tiny_kernel<1, 16>);
-        hipLaunchKernelGGL(k, dim3(blocks), dim3(kMoveThreads), 0, stream, topk_idx, x, n, H, K, E,
-                           P, expert_count, expert_offset, part_count, part_offset, row_of_pair,
-                           src_pair, status, (uint8_t*)recv_x, payload == 0 ? recv_scales : nullptr,
-                           steps, (int)items);
+        hipLaunchKernelGGL(k, dim3(pl.blocks), dim3(pl.waves * kWave), 0, stream, topk_idx, x, n, H,
+                           K, E, P, expert_count, expert_offset, part_count, part_offset,
+                           row_of_pair, src_pair, status, (uint8_t*)recv_x,
+                           payload == 0 ? recv_scales : nullptr, steps, items);
         return hipGetLastError();
     }
-    if (n <= kCountMaxPairs) {
-        // workgroups of 8, 7 or 6 waves, the largest that divides the steps
-        // per token (a workgroup then holds part of one token, or whole
-        // tokens), else 8; own entries at most 16
-        int W = 8;
-        for (int c = 8; c >= 6; --c)
-            if (steps % c == 0 || c % steps == 0) { W = c; break; }
-        const int own = max_own_tokens_exact(W, steps, (int)items) * K;
-        if (own <= 16)
-            return launch_count<false>(payload, W, own <= 8, topk_idx, x, n, H, K, E, P,
-                                       expert_count, expert_offset, part_count, part_offset,
-                                       row_of_pair, src_pair, status, recv_x, recv_scales, steps,
-                                       (int)items, DedupOutputs{}, stream);
-    }
-    const int W = fused_waves(items, steps, K);
+    if (pl.kind == kFusedCount)
+        return launch_count<false>(payload, pl.waves, pl.own8, topk_idx, x, n, H, K, E, P,
+                                   expert_count, expert_offset, part_count, part_offset,
+                                   row_of_pair, src_pair, status, recv_x, recv_scales, steps, items,
+                                   DedupOutputs{}, stream);
     const DedupOutputs none{};
     return payload == 0
-        ? launch_fused<0, false>(W, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
+        ? launch_fused<0, false>(pl.waves, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
                                  part_count, part_offset, row_of_pair, src_pair, status, recv_x,
-                                 recv_scales, steps, (int)items, none, stream)
-        : launch_fused<1, false>(W, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
+                                 recv_scales, steps, items, none, stream)
+        : launch_fused<1, false>(pl.waves, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
                                  part_count, part_offset, row_of_pair, src_pair, status, recv_x,
-                                 recv_scales, steps, (int)items, none, stream);
+                                 recv_scales, steps, items, none, stream);
 }
 
 hipError_t launch_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H,

@@ -42,15 +42,19 @@ constexpr int kLanesPerScaleBlock = kScaleBlock / kColsPerLane;   // 16 = one DP
 static_assert(kLanesPerScaleBlock == 16, "a scale block must be one 16-lane DPP row");
 
 // Launch geometry of the dispatch and combine kernels: waves per workgroup
-// (1, 2, 4 or 8; the kernels read it from blockDim) and a cap on the number
-// of workgroups (0: one wave per work item; otherwise the waves stride over
-// the items).  The default is 4 waves, uncapped.
+// (1, 2, 4 or 8; the kernels read it from blockDim), a cap on the number of
+// workgroups (0: one wave per work item; otherwise the waves stride over the
+// items) and the slice of a work item in 512-column steps (1 or 2: 512 or
+// 1024 columns of one token per wave).  The default is 4 waves, uncapped,
+// 512 columns.
 constexpr int kMaxMoveWaves = 8;
+constexpr int kMaxSliceSteps = 2;
 struct MoveGeometry {
     int waves;
     int max_blocks;
+    int slice_steps;
 };
-constexpr MoveGeometry kDefaultGeometry{kMoveWaves, 0};
+constexpr MoveGeometry kDefaultGeometry{kMoveWaves, 0, 1};
 static_assert(kMoveWaves * kMaxTopK <= kWave, "a workgroup's own entries fit in one wave");
 static_assert(kMaxExperts <= 1024, "fused slot ranks compare 10 id bits");
 

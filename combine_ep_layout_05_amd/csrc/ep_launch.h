@@ -19,6 +19,12 @@ hipError_t launch_layout(const int32_t* topk_idx, int T, int K, int E, int P,
                          int32_t* row_of_pair, int32_t* src_pair, uint32_t* status,
                          void* ws, hipStream_t stream);
 
+// Whether launch_dispatch / launch_combine accept a geometry for T tokens
+// (units) of hidden size H: the checks the launchers make, for the API to
+// make before it enqueues anything.
+bool dispatch_launch_ok(int T, int H, MoveGeometry g);
+bool combine_launch_ok(int n_units, int H, MoveGeometry g);
+
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K,
                            const int32_t* row_of_pair, int payload,
                            void* recv_x, float* recv_scales, hipStream_t stream,
@@ -26,12 +32,25 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K,
 
 bool fused_layout_dispatch_fits(int T, int H, int K);
 
+// Which fused layout+dispatch kernel a batch runs and how it is launched.
+enum FusedKind { kFusedTiny = 0, kFusedCount = 1, kFusedGeneral = 2 };
+struct FusedPlan {
+    int kind;          // FusedKind
+    int waves;         // waves per workgroup
+    bool own8;         // counting kernel: at most 8 own entries per workgroup
+    unsigned blocks;   // workgroups launched
+};
+// The plan for T >= 1 tokens with T*K <= kFusedMaxPairs and `waves` waves
+// per workgroup (0: the default for the batch); false when the batch does
+// not fit the fused kernels or that workgroup size is not one they take.
+bool plan_layout_dispatch(int T, int H, int K, int waves, FusedPlan* plan);
+
 hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
                                   int E, int P, int payload, int32_t* expert_count,
                                   int32_t* expert_offset, int32_t* part_count,
                                   int32_t* part_offset, int32_t* row_of_pair, int32_t* src_pair,
                                   uint32_t* status, void* recv_x, float* recv_scales,
-                                  hipStream_t stream);
+                                  hipStream_t stream, int waves = 0);
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of_pair,
                           const float* topk_w, int T, int H, int K,

@@ -1,10 +1,15 @@
-// ep_loop.cpp -- a native serving loop over the C ABI: ep_layout_dispatch +
-// ep_combine enqueued back to back on one stream, no synchronisation inside
-// the loop, the way a C++ serving process would drive the library.  Reports
-// the host time per step (what the enqueue costs) and the wall time per step
-// (whichever of host and GPU paces the loop).  At a few tokens the sources
-// found the host pacing the GPU (MoRI PR #614, view-cache paragraph); this
-// measures that quantity for this library without an interpreter in between.
+// ep_loop.cpp -- a native serving loop over the C ABI, the way a C++ serving
+// process would drive the library, in two forms:
+//   - direct: ep_layout_dispatch + ep_combine enqueued back to back on one
+//     stream, no synchronisation inside the loop;
+//   - graph1: the same two calls recorded once into a HIP graph
+//     (ep_graph_begin / ep_graph_end) and the graph replayed once per step.
+// For each it reports the host time per step (what the enqueue costs), the
+// wall time per step (whichever of host and GPU paces the loop) and, for the
+// graph, the device time per step between two events around all replays.  At
+// a few tokens the sources found the host pacing the GPU (MoRI PR #614,
+// view-cache paragraph); this measures that quantity for this library without
+// an interpreter in between.
 //
 //   ep_loop T H K E P [payload fp8|bf16] [steps]
 //
@@ -94,16 +99,54 @@ int main(int argc, char** argv)
             return 1;
         }
     CK(hipStreamSynchronize(s));
-    const auto t0 = std::chrono::steady_clock::now();
+    using clk = std::chrono::steady_clock;
+    auto us = [](clk::time_point a, clk::time_point b, int n) {
+        return std::chrono::duration<double, std::micro>(b - a).count() / n;
+    };
+    // direct launches
+    const auto t0 = clk::now();
     for (int i = 0; i < steps; ++i) step();
-    const auto t1 = std::chrono::steady_clock::now();
+    const auto t1 = clk::now();
     CK(hipStreamSynchronize(s));
-    const auto t2 = std::chrono::steady_clock::now();
-    const double host = std::chrono::duration<double, std::micro>(t1 - t0).count() / steps;
-    const double wall = std::chrono::duration<double, std::micro>(t2 - t0).count() / steps;
+    const auto t2 = clk::now();
+    // one-step graph, replayed once per step
+    void* g = nullptr;
+    if (int rc = ep_graph_begin(s)) {
+        std::fprintf(stderr, "ep_graph_begin: %s\n", ep_strerror(rc));
+        return 1;
+    }
+    const int rc_step = step();
+    if (int rc = ep_graph_end(s, &g)) {
+        std::fprintf(stderr, "ep_graph_end: %s\n", ep_strerror(rc));
+        return 1;
+    }
+    if (rc_step) {
+        std::fprintf(stderr, "captured step failed: %s\n", ep_strerror(rc_step));
+        return 1;
+    }
+    for (int i = 0; i < 200; ++i) ep_graph_launch(g, s);
+    CK(hipStreamSynchronize(s));
+    hipEvent_t e0, e1;
+    CK(hipEventCreate(&e0));
+    CK(hipEventCreate(&e1));
+    const auto g0 = clk::now();
+    CK(hipEventRecord(e0, s));
+    for (int i = 0; i < steps; ++i) ep_graph_launch(g, s);
+    CK(hipEventRecord(e1, s));
+    const auto g1 = clk::now();
+    CK(hipStreamSynchronize(s));
+    const auto g2 = clk::now();
+    float ms = 0.0f;
+    CK(hipEventElapsedTime(&ms, e0, e1));
+    ep_graph_destroy(g);
     std::printf("{\"T\": %d, \"H\": %d, \"K\": %d, \"E\": %d, \"P\": %d, \"steps\": %d, "
-                "\"host_us_per_step\": %.3f, \"wall_us_per_step\": %.3f}\n",
-                T, H, K, E, P, steps, host, wall);
+                "\"host_us_per_step\": %.3f, \"wall_us_per_step\": %.3f, "
+                "\"graph1_host_us_per_step\": %.3f, \"graph1_wall_us_per_step\": %.3f, "
+                "\"graph1_events_us_per_step\": %.3f}\n",
+                T, H, K, E, P, steps, us(t0, t1, steps), us(t0, t2, steps), us(g0, g1, steps),
+                us(g0, g2, steps), ms * 1000.0 / steps);
+    CK(hipEventDestroy(e0));
+    CK(hipEventDestroy(e1));
     CK(hipStreamDestroy(s));
     return 0;
 }

@@ -1,12 +1,18 @@
-"""Launch-geometry tuner for ep_dispatch and ep_combine on MI355X.
+"""Launch-geometry tuner for ep_layout_dispatch, ep_dispatch and ep_combine on MI355X.
 
-A geometry is (waves_per_block, max_blocks): 1, 2, 4 or 8 waves per
-workgroup, and either one wave per work item (max_blocks = 0) or a cap on the
-number of workgroups, whose waves then stride over the items.  Outputs do not
-depend on it; time does, and the best choice moves with token count and
-phase.  The selection rules follow what the MoRI EP tuner learned (MoRI PR
-#614 "perf(ep): InterNodeV1LL low-token latency on MI300X + CX7", tuner
-paragraphs):
+A geometry is (waves_per_block, max_blocks, slice_cols):
+  - dispatch / combine: 1, 2, 4 or 8 waves per workgroup; one wave per work
+    item (max_blocks = 0) or a cap on the number of workgroups, whose waves
+    then stride over the items; 512 or 1024 columns of one token per item;
+  - layout_dispatch: for batches that run fused (one launch, T*K <= 4096)
+    the fused kernel's waves per workgroup, the sizes that kernel takes
+    (found with ep_layout_dispatch_plan), max_blocks 0 and slice 0; for
+    larger batches the dispatch kernel's geometry as above.  (0, 0, 0) is
+    the library's own choice.
+Outputs do not depend on it; time does, and the best choice moves with token
+count and phase.  The selection rules follow what the MoRI EP tuner learned
+(MoRI PR #614 "perf(ep): InterNodeV1LL low-token latency on MI300X + CX7",
+tuner paragraphs):
 
   - score a candidate by its MEAN latency over the kept rounds; round 0 is
     dropped as warm-up.  The mean, unlike the median, is pulled up by a
@@ -19,13 +25,17 @@ paragraphs):
   - ties break on the full geometry tuple, so the pick does not depend on the
     order in which the sweep visits candidates;
   - a pick is adopted only after an interleaved A/B re-measurement against
-    the incumbent (the saved rule for the shape, else the library default)
-    confirms it, so a single noisy sample cannot win.
+    the incumbent (the saved rule for the shape, else the library default;
+    with --fresh always the library default) confirms it, so a single noisy
+    sample cannot win.
 
 Rules are kept in a JSON file (tuned_geometry.json beside this module by
-default), keyed by phase and shape; EpBuffers(..., geometry="tuned") uses
-them.  Run the sweep on the GPU with
+default), keyed by phase and exact shape; EpBuffers(..., geometry="tuned")
+uses them.  Run the sweep on the GPU with
     python -m combine_ep_layout_05_amd.tuning --preset bench --write
+(`--fresh` re-tunes every shape against the library default and writes only
+the rules adopted in that run, so rules that no longer win by the margin
+are dropped).
 """
 from __future__ import annotations
 
@@ -62,15 +72,41 @@ ROUNDS = _env_rounds()
 MARGIN = _env_margin()
 VERBOSE = (os.environ.get("EP_TUNING_VERBOSE") or "0") not in ("0", "")
 
-PHASES = ("dispatch", "combine")
-DEFAULT = (4, 0)                      # what ep_dispatch / ep_combine launch
+PHASES = ("layout_dispatch", "dispatch", "combine")
+LIBRARY = (0, 0, 0)                   # the library's own choice
+DEFAULT = {"layout_dispatch": LIBRARY, "dispatch": (4, 0, 512), "combine": (4, 0, 512)}
 WAVES = (1, 2, 4, 8)
 MAX_BLOCKS = (0, 256, 512, 1024, 2048)
+SLICES = (512, 1024)
+FUSED_WAVES = (1, 2, 4, 6, 7, 8)       # the workgroup sizes the fused kernels take, all told
 RULES_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tuned_geometry.json")
 
 
-def candidates():
-    return [(w, b) for w in WAVES for b in MAX_BLOCKS]
+def move_candidates():
+    """Geometries of the dispatch and combine kernels."""
+    return [(w, b, s) for w in WAVES for b in MAX_BLOCKS for s in SLICES]
+
+
+def candidates(phase, shape=None):
+    """Candidate geometries of a phase; layout_dispatch's depend on the shape
+    (dict with T, H, K, E, P, payload): the workgroup sizes its fused kernel
+    takes, or the dispatch kernel's geometries when the batch is not fused."""
+    if phase not in PHASES:
+        raise ValueError("phase must be one of %s" % (PHASES,))
+    if phase != "layout_dispatch":
+        return move_candidates()
+    from . import EpError, ep_layout_dispatch_plan
+    T, H, K, E, P, payload = (shape[k] for k in ("T", "H", "K", "E", "P", "payload"))
+    if ep_layout_dispatch_plan(T, H, K, E, P, payload)["kernel"] == "layout_then_dispatch":
+        return move_candidates()
+    out = []
+    for w in FUSED_WAVES:
+        try:
+            ep_layout_dispatch_plan(T, H, K, E, P, payload, (w, 0, 0))
+        except EpError:
+            continue
+        out.append((w, 0, 0))
+    return out
 
 
 # ---- selection (pure functions) ---------------------------------------------
@@ -87,7 +123,7 @@ def beats(new_us, old_us, margin):
     return new_us < old_us * (1.0 - margin)
 
 
-def pick(results, incumbent=DEFAULT, margin=None):
+def pick(results, incumbent, margin=None):
     """results: {geometry tuple: per-round latencies}.  The fastest mean wins,
     ties broken by the smaller geometry tuple; the incumbent (when it was
     measured) is kept unless the winner beats it by the margin."""
@@ -132,18 +168,27 @@ def save_rules(rules, path=None, arch="gfx950"):
     os.replace(tmp, path)
 
 
+def rule_geometry(rule):
+    """(waves, max_blocks, slice_cols) of a saved rule (slice 512 when absent)."""
+    return (int(rule["waves"]), int(rule["max_blocks"]), int(rule.get("slice_cols", 512)))
+
+
 def lookup(phase, T, H, K, payload, path=None):
     """Saved geometry for this exact shape, or None (library default)."""
     r = load_rules(path).get(rule_key(phase, T, H, K, payload))
-    return None if r is None else (int(r["waves"]), int(r["max_blocks"]))
+    return None if r is None else rule_geometry(r)
 
 
 # ---- measurement (GPU) ---------------------------------------------------------
 
+SPIN_CYCLES = 200000                  # GPU spin ahead of a timed graph (about 80 us)
+
+
 class ShapeBench:
     """Seeded synthetic inputs and persistent buffers for one shape; times
     one phase under a given geometry from HIP graphs of back-to-back
-    launches (device time per launch, host enqueue excluded)."""
+    launches (device time per launch: a GPU spin ahead of the first event
+    keeps the host's graph-launch time out of the timed region)."""
 
     def __init__(self, T, H, K, E, P, payload="fp8", seed=0, launches=20):
         import torch
@@ -166,9 +211,14 @@ class ShapeBench:
         self.graphs = {}
 
     def _enqueue(self, phase, geometry):
-        from . import ep_combine, ep_dispatch
+        from . import ep_combine, ep_dispatch, ep_layout_dispatch
         b = self.buf
-        if phase == "dispatch":
+        if phase == "layout_dispatch":
+            ep_layout_dispatch(self.idx, self.x, b.E, b.P, b.payload, b.expert_count,
+                               b.expert_offset, b.part_count, b.part_offset, b.row_of_pair,
+                               b.src_pair, b.status, b.ws, b.recv_x, b.recv_scales, self.stream,
+                               None if tuple(geometry) == LIBRARY else geometry)
+        elif phase == "dispatch":
             ep_dispatch(self.x, self.K, b.row_of_pair, b.payload, b.recv_x, b.recv_scales,
                         self.stream, geometry)
         else:
@@ -190,6 +240,8 @@ class ShapeBench:
         g = self.graph(phase, geometry)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            torch.cuda._sleep(SPIN_CYCLES)
         e0.record(self.stream)
         g.launch(self.stream)
         e1.record(self.stream)
@@ -213,28 +265,29 @@ class ShapeBench:
         self.graphs.clear()
 
 
-def tune(phase, shape, rules, rounds=None, margin=None, log=print):
+def tune(phase, shape, rules, rounds=None, margin=None, fresh=False, log=print):
     """Sweep one phase on one shape; returns (rule or None, report dict).
-    The incumbent is the saved rule for the shape, else the default."""
+    The incumbent is the saved rule for the shape, else (and always with
+    fresh) the library default."""
     rounds = ROUNDS if rounds is None else rounds
     margin = MARGIN if margin is None else margin
     T, H, K, E, P, payload = (shape[k] for k in ("T", "H", "K", "E", "P", "payload"))
     key = rule_key(phase, T, H, K, payload)
-    saved = rules.get(key)
-    incumbent = DEFAULT if saved is None else (int(saved["waves"]), int(saved["max_blocks"]))
+    saved = None if fresh else rules.get(key)
+    incumbent = DEFAULT[phase] if saved is None else rule_geometry(saved)
     sb = ShapeBench(T, H, K, E, P, payload, seed=shape.get("seed", 0))
     try:
-        cands = candidates()
+        cands = candidates(phase, shape)
         if incumbent not in cands:
             cands.append(incumbent)
         res = sb.sweep(phase, cands, rounds)
         if VERBOSE:
             for g in sorted(res, key=lambda g: score(res[g])):
-                log("  %s %s w=%d b=%d mean %.3f us rounds %s" % (
-                    phase, key, g[0], g[1], score(res[g]), ["%.2f" % v for v in res[g]]))
+                log("  %s %s %s mean %.3f us rounds %s" % (
+                    phase, key, g, score(res[g]), ["%.2f" % v for v in res[g]]))
         best = pick(res, incumbent, margin)
         report = {"key": key, "incumbent": list(incumbent), "sweep_pick": list(best),
-                  "sweep_mean_us": round(score(res[best]), 4),
+                  "candidates": len(cands), "sweep_mean_us": round(score(res[best]), 4),
                   "incumbent_sweep_mean_us": round(score(res[incumbent]), 4)}
         if best == incumbent:
             report["adopted"] = False
@@ -245,9 +298,10 @@ def tune(phase, shape, rules, rounds=None, margin=None, log=print):
                       adopted=bool(ok))
         if not ok:
             return None, report
-        rule = {"waves": best[0], "max_blocks": best[1], "avg_latency_us": round(score(new_s), 4),
-                "incumbent": list(incumbent), "incumbent_latency_us": round(score(old_s), 4),
-                "rounds": rounds, "margin": margin}
+        rule = {"waves": best[0], "max_blocks": best[1], "slice_cols": best[2],
+                "avg_latency_us": round(score(new_s), 4), "incumbent": list(incumbent),
+                "incumbent_latency_us": round(score(old_s), 4), "rounds": rounds,
+                "margin": margin}
         return rule, report
     finally:
         sb.close()
@@ -257,6 +311,7 @@ PRESETS = {
     "bench": [
         dict(name="ll_128x7168", T=128, H=7168, K=8, E=288, P=16, payload="fp8"),
         dict(name="sweep_4x6144", T=4, H=6144, K=8, E=256, P=16, payload="fp8"),
+        dict(name="sweep_8x6144", T=8, H=6144, K=8, E=256, P=16, payload="fp8"),
         dict(name="sweep_16x6144", T=16, H=6144, K=8, E=256, P=16, payload="fp8"),
         dict(name="bw_4096x7168", T=4096, H=7168, K=8, E=256, P=8, payload="fp8"),
         dict(name="masked_16384x4096_bf16", T=16384, H=4096, K=8, E=128, P=8, payload="bf16"),
@@ -267,25 +322,30 @@ PRESETS = {
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--preset", default="bench", choices=sorted(PRESETS))
-    ap.add_argument("--phases", default="dispatch,combine")
+    ap.add_argument("--phases", default=",".join(PHASES))
     ap.add_argument("--rules", default=None, help="rules file (default: the package's)")
     ap.add_argument("--write", action="store_true", help="save adopted rules")
+    ap.add_argument("--fresh", action="store_true",
+                    help="tune against the library default and write only this run's adopted "
+                         "rules (rules that no longer win by the margin are dropped)")
     args = ap.parse_args(argv)
     rules = load_rules(args.rules)
     phases = [p for p in args.phases.split(",") if p]
     for p in phases:
         if p not in PHASES:
             raise SystemExit("unknown phase %r" % p)
-    print("rounds %d (round 0 dropped), margin %g, %d candidates" % (
-        ROUNDS, MARGIN, len(candidates())), flush=True)
+    print("rounds %d (round 0 dropped), margin %g, %s" % (
+        ROUNDS, MARGIN, "fresh: incumbent = library default" if args.fresh else
+        "incumbent = saved rule, else library default"), flush=True)
+    new_rules = {} if args.fresh else dict(rules)
     for shape in PRESETS[args.preset]:
         for phase in phases:
-            rule, rep = tune(phase, shape, rules)
+            rule, rep = tune(phase, shape, rules, fresh=args.fresh)
             print(json.dumps(rep), flush=True)
             if rule is not None:
-                rules[rep["key"]] = rule
+                new_rules[rep["key"]] = rule
     if args.write:
-        save_rules(rules, args.rules)
+        save_rules(new_rules, args.rules)
         print("rules written to %s" % (args.rules or RULES_PATH), flush=True)
     return 0
 

@@ -30,11 +30,13 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work; none synchronises the host.  Buffers must stay
  *     alive until the stream has run the work.
- *   - Return 0 on success.  A negative code means a host-side check failed
- *     and NOTHING was enqueued: EP_EINVAL (bad argument), EP_ENOTSUP
- *     (unsupported payload), EP_EHIP (a HIP launch failed; see
- *     ep_last_hip_error()), EP_ESCRATCH (ep_layout_dispatch_noalloc only:
- *     the batch needs more scratch than the library holds).
+ *   - Return 0 on success.  EP_EINVAL (bad argument), EP_ENOTSUP
+ *     (unsupported payload) and EP_ESCRATCH (ep_layout_dispatch_noalloc
+ *     only: the batch needs more scratch than the library holds) mean a
+ *     host-side check failed and NOTHING was enqueued: every check, those of
+ *     the kernel launches included, runs before the first launch.  EP_EHIP
+ *     means HIP refused a launch (see ep_last_hip_error()); the launches of
+ *     the same call before it may have been enqueued.
  *   - Every call can be captured into a HIP graph: no call allocates,
  *     memsets or synchronises; counters the kernels need are cleared by
  *     the kernels themselves.
@@ -308,24 +310,76 @@ int ep_combine_reduce(const uint16_t* partial, const int32_t* tp_row, int T, int
  * Launch geometry (for tuning).  ep_dispatch and ep_combine launch 4 waves
  * (256 threads) per workgroup and one wave per work item, a work item being
  * one token's 512-column slice.  These variants take the geometry
- * explicitly: waves_per_block in {1, 2, 4, 8}, and max_blocks = 0 (one wave
- * per item) or a cap on the number of workgroups, whose waves then stride
- * over the items.  The outputs do not depend on the geometry (bit for bit);
- * only the time does.  The sources found that the best geometry moves with
- * token count and phase, and pick it by measurement (MoRI PR #614, tuner
- * paragraphs).
+ * explicitly:
+ *   waves_per_block  1, 2, 4 or 8;
+ *   max_blocks       0 (one wave per item) or a cap on the number of
+ *                    workgroups, whose waves then stride over the items;
+ *   slice_cols       0 or 512 (512 columns per item) or 1024 (two
+ *                    512-column halves of one token per wave, loaded
+ *                    together).
+ * The outputs do not depend on the geometry (bit for bit); only the time
+ * does.  The sources found that the best geometry moves with token count and
+ * phase, that items below 512 columns starve, and pick the geometry by
+ * measurement (MoRI PR #614, tuner and MultiWarpIter paragraphs).
  * Errors: those of ep_dispatch / ep_combine, and EP_EINVAL for another
- * waves_per_block or a negative max_blocks.
+ * waves_per_block, a negative max_blocks or another slice_cols.
  */
 #define EP_MAX_WAVES_PER_BLOCK 8
 
 int ep_dispatch_geom(const uint16_t* x, int T, int H, int K, const int32_t* row_of_pair,
                      int payload, void* recv_x, float* recv_scales, int waves_per_block,
-                     int max_blocks, void* stream);
+                     int max_blocks, int slice_cols, void* stream);
 
 int ep_combine_geom(const uint16_t* expert_out, const int32_t* row_of_pair, const float* topk_w,
                     int T, int H, int K, uint16_t* out, int waves_per_block, int max_blocks,
-                    void* stream);
+                    int slice_cols, void* stream);
+
+/*
+ * ep_layout_dispatch with an explicit launch geometry (0 = the library's
+ * choice for each of the three values).  Same results, bit for bit, as
+ * ep_layout_dispatch.
+ *   - A batch that runs fused (T*K <= 4096, one launch) takes only a
+ *     workgroup size: max_blocks must be 0 and slice_cols 0 or 512.  The
+ *     workgroup sizes the fused kernels take depend on the batch:
+ *       T*K <= 128 (EP_PLAN_FUSED_TINY): 1, 2, 4 or 8 waves (default 4);
+ *       T*K <= 1024 (EP_PLAN_FUSED_COUNT): 4, 6, 7 or 8 waves when a
+ *         workgroup's items then touch at most 16 entries (the default is
+ *         the largest of 8, 7, 6 that divides the 512-column steps per
+ *         token); 4 or 8 waves otherwise (EP_PLAN_FUSED_GENERAL);
+ *       T*K <= 4096 (EP_PLAN_FUSED_GENERAL): 4 or 8 waves when a
+ *         workgroup's items touch at most 64 entries.
+ *   - A larger batch runs the layout kernels and then the dispatch kernel,
+ *     which takes (waves_per_block, max_blocks, slice_cols) as
+ *     ep_dispatch_geom does.
+ * Errors: those of ep_layout_dispatch, and EP_EINVAL for a geometry the
+ * batch's kernels do not take (nothing is enqueued).
+ */
+int ep_layout_dispatch_geom(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
+                            int P, int payload, int32_t* expert_count, int32_t* expert_offset,
+                            int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
+                            int32_t* src_pair, uint32_t* status, void* ws, size_t ws_bytes,
+                            void* recv_x, float* recv_scales, int waves_per_block, int max_blocks,
+                            int slice_cols, void* stream);
+
+/*
+ * Host-only: how ep_layout_dispatch_geom would run a batch with the given
+ * geometry (0s = ep_layout_dispatch's own choice), written to plan[4]:
+ *   plan[0]  EP_PLAN_FUSED_TINY, EP_PLAN_FUSED_COUNT, EP_PLAN_FUSED_GENERAL
+ *            (one fused launch) or EP_PLAN_LAYOUT_THEN_DISPATCH;
+ *   plan[1]  waves per workgroup (of the fused kernel, or of the dispatch);
+ *   plan[2]  fused: workgroups launched; otherwise the dispatch's max_blocks;
+ *   plan[3]  columns per work item (512, or the dispatch's slice).
+ * Returns EP_EINVAL (plan untouched) for arguments or a geometry
+ * ep_layout_dispatch_geom would reject, EP_ENOTSUP for another payload.
+ * Pointers are not involved; nothing touches the GPU.
+ */
+#define EP_PLAN_FUSED_TINY 0
+#define EP_PLAN_FUSED_COUNT 1
+#define EP_PLAN_FUSED_GENERAL 2
+#define EP_PLAN_LAYOUT_THEN_DISPATCH 3
+
+int ep_layout_dispatch_plan(int T, int H, int K, int E, int P, int payload, int waves_per_block,
+                            int max_blocks, int slice_cols, int32_t* plan);
 
 /*
  * HIP graph capture for the small-token regime, where host enqueue paces the

@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
               "ep_graph_launch", "ep_graph_destroy", "ep_e4m3fn_encode", "ep_layout_dispatch",
               "ep_dedup_layout", "ep_dedup_layout_workspace_bytes", "ep_combine_partial",
               "ep_combine_reduce", "ep_dedup_layout_dispatch",
-              "ep_dedup_layout_dispatch_workspace_bytes", "ep_dispatch_geom", "ep_combine_geom"):
+              "ep_dedup_layout_dispatch_workspace_bytes", "ep_dispatch_geom", "ep_combine_geom",
+              "ep_layout_dispatch_geom", "ep_layout_dispatch_plan", "ep_layout_dispatch_noalloc"):
         assert n in names, n
 
 
@@ -133,15 +134,42 @@ def test_dedup_layout_dispatch_host_side_validation(lib):
 def test_geometry_host_side_validation(lib):
     P, I = ctypes.c_void_p, ctypes.c_int
     L = lib
-    L.ep_dispatch_geom.argtypes = [P, I, I, I, P, I, P, P, I, I, P]
-    L.ep_combine_geom.argtypes = [P, P, P, I, I, I, P, I, I, P]
+    L.ep_dispatch_geom.argtypes = [P, I, I, I, P, I, P, P, I, I, I, P]
+    L.ep_combine_geom.argtypes = [P, P, P, I, I, I, P, I, I, I, P]
     fake = P(0x10000)
-    for wv, mb in [(3, 0), (0, 0), (16, 0), (4, -1)]:
-        assert L.ep_dispatch_geom(fake, 4, 1024, 8, fake, 0, fake, fake, wv, mb, None) == -1
-        assert L.ep_combine_geom(fake, fake, fake, 4, 1024, 8, fake, wv, mb, None) == -1
+    for wv, mb, sc in [(3, 0, 0), (0, 0, 0), (16, 0, 0), (4, -1, 0), (4, 0, 256), (4, 0, 2048)]:
+        assert L.ep_dispatch_geom(fake, 4, 1024, 8, fake, 0, fake, fake, wv, mb, sc, None) == -1
+        assert L.ep_combine_geom(fake, fake, fake, 4, 1024, 8, fake, wv, mb, sc, None) == -1
     # valid geometry, empty batch: accepted, nothing launched
-    assert L.ep_dispatch_geom(None, 0, 1024, 8, None, 0, None, None, 8, 0, None) == 0
-    assert L.ep_combine_geom(None, None, None, 0, 1024, 8, None, 1, 256, None) == 0
+    assert L.ep_dispatch_geom(None, 0, 1024, 8, None, 0, None, None, 8, 0, 1024, None) == 0
+    assert L.ep_combine_geom(None, None, None, 0, 1024, 8, None, 1, 256, 512, None) == 0
+
+
+def test_layout_dispatch_geom_host_side_validation(lib):
+    """A fused batch takes only a workgroup size its kernel accepts; the plan
+    query agrees with what the call accepts (host only, nothing launched)."""
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L = lib
+    L.ep_layout_dispatch_geom.argtypes = [P, P, I, I, I, I, I, I] + [P] * 7 + [P, ctypes.c_size_t,
+                                                                              P, P, I, I, I, P]
+    L.ep_layout_dispatch_plan.argtypes = [I] * 9 + [P]
+    fake = P(0x10000)
+    outs = [fake] * 7
+    plan = (ctypes.c_int32 * 4)()
+    pp = ctypes.cast(plan, P)
+    for geom in [(4, 256, 0), (4, 0, 1024), (3, 0, 0), (16, 0, 0), (-1, 0, 0)]:
+        # 128 x 7168 top-8 runs fused: no cap, no 1024-column slice, 4/6/7/8 waves only
+        assert L.ep_layout_dispatch_plan(128, 7168, 8, 288, 16, 0, *geom, pp) == -1
+        assert L.ep_layout_dispatch_geom(fake, fake, 128, 7168, 8, 288, 16, 0, *outs, None, 0,
+                                         fake, fake, *geom, None) == -1
+    assert L.ep_layout_dispatch_plan(128, 7168, 8, 288, 16, 0, 0, 0, 0, pp) == 0
+    assert list(plan) == [1, 7, 257, 512]
+    assert L.ep_layout_dispatch_plan(4, 6144, 8, 256, 16, 0, 8, 0, 0, pp) == 0
+    assert list(plan) == [0, 8, 4 * 12 // 8 + 1, 512]
+    assert L.ep_layout_dispatch_plan(4096, 7168, 8, 256, 8, 0, 2, 256, 1024, pp) == 0
+    assert list(plan) == [3, 2, 256, 1024]
+    assert L.ep_layout_dispatch_plan(4, 6144, 8, 256, 16, 7, 0, 0, 0, pp) == -2
+    assert L.ep_layout_dispatch_plan(4, 6144, 8, 256, 16, 0, 0, 0, 0, None) == -1
 
 
 def test_noalloc_host_side_validation(lib):

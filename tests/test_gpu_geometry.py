@@ -1,14 +1,20 @@
 """GPU: every launch geometry the tuner may pick gives the same bytes.
 
-ep_dispatch_geom / ep_combine_geom over all (waves_per_block, max_blocks)
-candidates, plus a single one-wave workgroup striding over every item,
-compared bit for bit with the default launch (itself checked against the
-oracle), and once directly with the oracle.
+- ep_dispatch_geom / ep_combine_geom over all (waves_per_block, max_blocks,
+  slice_cols) candidates, plus single small workgroups striding over every
+  item, compared bit for bit with the default launch (itself checked
+  against the oracle);
+- ep_layout_dispatch_geom over every fused workgroup size the library
+  accepts for a batch (tiny, counting and general fused kernels) and over
+  dispatch geometries for a batch that runs unfused, each checked against
+  the oracle.
 """
+import sys
+
 import numpy as np
 import pytest
 
-from tests.pathrun import POISON_BYTE, compare, run_oracle, to_dev
+from tests.pathrun import POISON_BYTE, collect, compare, run_gpu, run_oracle, to_dev
 from workloads import WORKLOADS, generate
 
 pytestmark = pytest.mark.gpu
@@ -16,7 +22,11 @@ pytestmark = pytest.mark.gpu
 SHAPES = {
     "ll_128x7168": WORKLOADS["ll_128x7168"],
     "ragged_H640_T33": WORKLOADS["tiny_4x1024"].with_(name="geom_ragged", T=33, H=640),
+    "ragged_H1152_K16": WORKLOADS["tiny_4x1024"].with_(name="geom_ragged_k16", T=21, H=1152, K=16,
+                                                        E=64, P=8),
     "bf16_T300_H512": WORKLOADS["tiny_4x1024"].with_(name="geom_bf16", T=300, H=512, payload="bf16"),
+    "bf16_H1544": WORKLOADS["tiny_4x1024"].with_(name="geom_bf16_ragged", T=40, H=1544,
+                                                  payload="bf16"),
 }
 
 
@@ -37,7 +47,6 @@ def _run(wl, d, geometry):
     buf.dispatch(x)
     buf.combine(y, w)
     torch.cuda.synchronize()
-    from tests.pathrun import collect
     return collect(buf)
 
 
@@ -46,13 +55,64 @@ def test_all_geometries_bit_identical(shape):
     import combine_ep_layout_05_amd.tuning as tu
     wl = SHAPES[shape]
     d = generate(wl, seed=wl.seed + 31)
-    print("geometry parity %s T=%d H=%d %s" % (wl.name, wl.T, wl.H, wl.payload), flush=True)
+    print("geometry parity %s T=%d H=%d K=%d %s" % (wl.name, wl.T, wl.H, wl.K, wl.payload),
+          flush=True)
     base = _run(wl, d, None)
     assert compare(wl, base, run_oracle(wl, d), check_poison=True) == 0
-    for geom in tu.candidates() + [(1, 1), (8, 1), (2, 3)]:
+    extra = [(1, 1, 512), (8, 1, 512), (2, 3, 1024), (1, 1, 1024)]
+    for geom in tu.candidates("dispatch") + extra:
         got = _run(wl, d, geom)
         for k in base:
             assert np.array_equal(got[k], base[k]), (shape, geom, k)
+
+
+FUSED = {
+    # T*K <= 128: the barrier-free kernel, 1/2/4/8 waves
+    "tiny_4x6144": WORKLOADS["sweep_4x6144"],
+    "tiny_ragged_K5": WORKLOADS["tiny_4x1024"].with_(name="fg_tiny", T=25, H=640, K=5, E=40, P=8),
+    # 128 < T*K <= 1024: the counting kernel at 4, 6, 7, 8 waves (and general fallbacks)
+    "count_128x7168": WORKLOADS["ll_128x7168"],
+    "count_H2048": WORKLOADS["tiny_4x1024"].with_(name="fg_count", T=100, H=2048, E=288, P=16),
+    "count_bf16_H5632": WORKLOADS["tiny_4x1024"].with_(name="fg_count_bf16", T=90, H=5632,
+                                                       payload="bf16"),
+    # 1024 < T*K <= 4096: the general kernel at 4 and 8 waves
+    "general_300x7168": WORKLOADS["tiny_4x1024"].with_(name="fg_general", T=300, H=7168, E=288,
+                                                       P=16),
+}
+
+
+@pytest.mark.parametrize("shape", list(FUSED))
+def test_fused_workgroup_sizes_against_oracle(shape):
+    import combine_ep_layout_05_amd as ep
+    import combine_ep_layout_05_amd.tuning as tu
+    wl = FUSED[shape]
+    sh = dict(T=wl.T, H=wl.H, K=wl.K, E=wl.E, P=wl.P, payload=wl.payload)
+    cands = tu.candidates("layout_dispatch", sh)
+    assert cands, shape
+    d = generate(wl, seed=wl.seed + 41)
+    ref = run_oracle(wl, d)
+    for geom in cands:
+        plan = ep.ep_layout_dispatch_plan(wl.T, wl.H, wl.K, wl.E, wl.P, wl.payload, geom)
+        print("fused geometry %s %s -> %s" % (shape, geom, plan), flush=True)
+        sys.stdout.flush()
+        got = run_gpu(wl, d, fused=True, geometry={"layout_dispatch": geom})
+        assert compare(wl, got, ref) == 0, (shape, geom)
+
+
+def test_unfused_layout_dispatch_geometries_against_oracle():
+    """Above 4096 entries ep_layout_dispatch_geom passes its geometry to the
+    dispatch kernel (waves, cap, 1024-column slices)."""
+    import combine_ep_layout_05_amd as ep
+    wl = WORKLOADS["tiny_4x1024"].with_(name="unfused_geom", T=600, H=1664, E=96, P=8,
+                                        mask_frac=0.05)
+    d = generate(wl, seed=91)
+    ref = run_oracle(wl, d)
+    for geom in [(1, 0, 512), (8, 256, 1024), (2, 0, 1024), (4, 512, 512)]:
+        assert ep.ep_layout_dispatch_plan(wl.T, wl.H, wl.K, wl.E, wl.P, wl.payload,
+                                          geom)["kernel"] == "layout_then_dispatch"
+        print("unfused geometry %s" % (geom,), flush=True)
+        got = run_gpu(wl, d, fused=True, geometry={"layout_dispatch": geom, "combine": geom})
+        assert compare(wl, got, ref) == 0, geom
 
 
 def test_geometry_rejected_on_host():
@@ -60,6 +120,13 @@ def test_geometry_rejected_on_host():
     import combine_ep_layout_05_amd as ep
     buf = ep.EpBuffers(4, 1024, 8, 32, 8)
     x = torch.zeros(4, 1024, dtype=torch.bfloat16, device="cuda")
-    for bad in [(3, 0), (16, 0), (0, 0), (4, -1)]:
+    for bad in [(3, 0, 0), (16, 0, 0), (0, 0, 0), (4, -1, 0), (4, 0, 768), (4, 0, 2048)]:
         with pytest.raises(ep.EpError):
             ep.ep_dispatch(x, 8, buf.row_of_pair, "fp8", buf.recv_x, buf.recv_scales, None, bad)
+    idx = torch.zeros(4, 8, dtype=torch.int32, device="cuda")
+    for bad in [(4, 256, 0), (4, 0, 1024), (3, 0, 0)]:        # fused batch: workgroup size only
+        with pytest.raises(ep.EpError):
+            ep.ep_layout_dispatch(idx, x, 32, 8, "fp8", buf.expert_count, buf.expert_offset,
+                                  buf.part_count, buf.part_offset, buf.row_of_pair, buf.src_pair,
+                                  buf.status, buf.ws, buf.recv_x, buf.recv_scales, None, bad)
+    torch.cuda.synchronize()
