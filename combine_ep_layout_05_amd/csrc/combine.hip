@@ -99,8 +99,10 @@ __device__ __forceinline__ void partial_in_order(const uint16_t* __restrict__ y,
     // waits for one row at a time
     // The entries in that order through LDS (`ord`, this wave's kMaxTopK
     // slots): lane k writes its row, weight and partition to slot rank, lane
-    // j reads slot j back (one wave's LDS operations complete in order).
+    // j reads slot j back (one wave: wave_lds_sync between write and read,
+    // no workgroup barrier).
     if (valid) ord[rank] = make_int4(myrow, __builtin_bit_cast(int, myw), pk, 0);
+    wave_lds_sync();
     const int4 o = lane < nv ? ord[lane] : make_int4(0, 0, -1, 0);
     const int cl = active ? col0 : 0;
 #pragma unroll
@@ -221,8 +223,9 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
             // DPP row: the butterfly leaves the row's total in every lane).
             // The entry -> partition map is then transposed through LDS: each
             // couple lane writes its partition into the slot of every entry
-            // of its mask, and lane k reads slot k back -- one wave's LDS
-            // operations complete in program order, so no barrier is needed.
+            // of its mask, and lane k reads slot k back -- within one wave, so
+            // wave_lds_sync orders the hand-offs and no workgroup barrier is
+            // needed.
             const uint32_t kbits = (uint32_t)((1ull << K) - 1ull);
             uint32_t m = prow >= 0 ? (pmask & kbits) : 0u;
             int orv = (int)m, cnt = __builtin_popcount(m);
@@ -239,11 +242,13 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void combine_kernel(
             if (!overlap) {
                 int32_t* const slot = s_pk[threadIdx.x / kWave];
                 if (lane < kMaxTopK) slot[lane] = -1;
+                wave_lds_sync();
                 while (m) {                       // this couple's entries
                     const int k = __builtin_ctz(m);
                     m &= m - 1u;
                     slot[k] = lane;
                 }
+                wave_lds_sync();
                 const int pk = lane < K ? slot[lane] : -1;
                 partial_in_order<kMaxK, kStream>(y, out, H, col0, active, lane, myrow, myw, pk,
                                                  prow, s_ord[threadIdx.x / kWave]);

@@ -570,7 +570,8 @@ __global__ __launch_bounds__(kW * kWave) void layout_dispatch_kernel(
 // stores, where the general fused kernel spends three barriers and the LDS
 // histogram and scan.  One extra workgroup (launch block 0, dispatched first)
 // builds the per-expert histogram of the same ids in LDS within one wave (its
-// LDS operations complete in program order, so it needs no barrier either)
+// LDS operations complete in program order, so it needs no workgroup barrier,
+// only wave_lds_sync at each hand-off)
 // and writes the counts, offsets, partition sums and status.  Outputs are
 // those of the general kernel.
 constexpr int kTinyPairs = 2 * kWave;
@@ -603,8 +604,10 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void layout_dispatch_tiny_ke
             const int e = lane * kPerLane + j;
             if (e < E) cnt[e] = 0;
         }
+        wave_lds_sync();                          // counters cleared
         if (v0) atomicAdd(&cnt[id0], 1);
         if (v1) atomicAdd(&cnt[id1], 1);
+        wave_lds_sync();                          // histogram complete
         int c[kPerLane], sum = 0;
 #pragma unroll
         for (int j = 0; j < kPerLane; ++j) {
@@ -625,6 +628,7 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void layout_dispatch_tiny_ke
             }
             o += c[j];
         }
+        wave_lds_sync();                          // offsets written
         const int L = E / P;
         for (int p = lane; p < P; p += kWave) {
             const int lo = cnt[p * L];
@@ -716,23 +720,6 @@ __global__ __launch_bounds__(kMaxMoveWaves * kWave) void layout_dispatch_tiny_ke
 // before; the payload goes once to each of them.  Block 0 also writes the
 // per-partition token totals and offsets and the tp_src tail.
 constexpr int kCountMaxPairs = 1024;
-
-// Within each aligned group of K consecutive lanes (K = 1, 2, 4, 8 or 16,
-// so a group lies inside one 16-lane DPP row): the OR of v over the group's
-// lanes below this one (0 for the group's first lane).  Inclusive steps
-// row_shr 1, 2, 4, 8 taken only from sources inside the group, then one more
-// row_shr 1 for the exclusive value.
-__device__ __forceinline__ uint32_t group_excl_or(uint32_t v, int K, int lane)
-{
-    const int r = lane & (K - 1);            // position in the group
-    int x = (int)v;
-    if (K >= 2) { const int y = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false); x |= r >= 1 ? y : 0; }
-    if (K >= 4) { const int y = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false); x |= r >= 2 ? y : 0; }
-    if (K >= 8) { const int y = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false); x |= r >= 4 ? y : 0; }
-    if (K >= 16) { const int y = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false); x |= r >= 8 ? y : 0; }
-    const int y = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);        // row_shr:1
-    return r >= 1 ? (uint32_t)y : 0u;
-}
 
 template <int kPayload, bool kDedup, int kW, int kOwn>
 __global__ __launch_bounds__(kW * kWave) void layout_dispatch_count_kernel(

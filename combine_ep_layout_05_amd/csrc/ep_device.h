@@ -123,6 +123,37 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Within each aligned group of K consecutive lanes (K = 1, 2, 4, 8 or 16,
+// so a group lies inside one 16-lane DPP row): the OR of v over the group's
+// lanes below this one (0 for the group's first lane).  Inclusive steps
+// row_shr 1, 2, 4, 8 taken only from sources inside the group, then one more
+// row_shr 1 for the exclusive value.
+__device__ __forceinline__ uint32_t group_excl_or(uint32_t v, int K, int lane)
+{
+    const int r = lane & (K - 1);            // position in the group
+    int x = (int)v;
+    if (K >= 2) { const int y = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false); x |= r >= 1 ? y : 0; }
+    if (K >= 4) { const int y = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false); x |= r >= 2 ? y : 0; }
+    if (K >= 8) { const int y = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false); x |= r >= 4 ? y : 0; }
+    if (K >= 16) { const int y = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false); x |= r >= 8 ? y : 0; }
+    const int y = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);        // row_shr:1
+    return r >= 1 ? (uint32_t)y : 0u;
+}
+
+// Orders one wave's LDS accesses across a hand-off between its lanes: every
+// LDS write or atomic of this wave issued before it completes, and is visible
+// to the wave's LDS reads issued after it (a wave barrier between a release
+// and an acquire fence on the local address space).  For the places where the
+// lanes of one wave pass values through LDS with no workgroup barrier: the
+// hardware completes one wave's LDS operations in order, and this keeps the
+// compiler from reordering the non-atomic accesses around the hand-off.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // MI355X runs a launch's workgroups on its 8 XCDs round robin (workgroup b
 // on XCD b % 8), each XCD with its own L2.  xcd_block renumbers the grid so
 // that every XCD holds one contiguous range of logical blocks: kernels that

@@ -380,7 +380,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
 // ---------------------------------------------------------------------------
 // Tiny batches (n <= kTinyLayoutPairs = 128 entries): one wave does it all.
 // A wave's LDS operations complete in program order, so the single-workgroup
-// kernel's barriers are not needed: match-any groups add their sizes to the
+// kernel's barriers are not needed (wave_lds_sync orders each hand-off
+// between lanes): match-any groups add their sizes to the
 // LDS histogram, a DPP wave scan over the experts (kMaxExperts / 64 per lane)
 // turns it into offsets that stay in LDS as per-expert cursors, and each
 // round's rows are cursor + in-wave rank, the group leaders then moving the
@@ -412,8 +413,10 @@ __global__ __launch_bounds__(kWave) void layout_tiny_kernel(
     const uint64_t peers0 = match_peers(e0, v0, nbits);
     const uint64_t peers1 = (n > kWave) ? match_peers(e1, v1, nbits) : 0ull;
     const int rank0 = lanes_below(peers0), rank1 = lanes_below(peers1);
+    wave_lds_sync();                              // counters cleared
     if (v0 && rank0 == 0) atomicAdd(&cur[e0], (int)__popcll(peers0));
     if (v1 && rank1 == 0) atomicAdd(&cur[e1], (int)__popcll(peers1));
+    wave_lds_sync();                              // histogram complete
 
     int c[kPerLane], sum = 0;
 #pragma unroll
@@ -435,6 +438,7 @@ __global__ __launch_bounds__(kWave) void layout_tiny_kernel(
         }
         o += c[j];
     }
+    wave_lds_sync();                              // offsets written
     if (part_count) {
         const int L = E / P;
         for (int p = lane; p < P; p += kWave) {
@@ -454,7 +458,9 @@ __global__ __launch_bounds__(kWave) void layout_tiny_kernel(
     // rows: round 0, then its group leaders move the cursors past their
     // groups (after every lane of the wave has read them), then round 1
     const int row0 = v0 ? cur[e0] + rank0 : -1;
+    wave_lds_sync();                              // every lane has read its cursor
     if (v0 && rank0 == 0) cur[e0] = row0 + (int)__popcll(peers0);
+    wave_lds_sync();                              // cursors moved past round 0
     const int row1 = v1 ? cur[e1] + rank1 : -1;
     if (lane < n) {
         row_of_pair[lane] = row0;
@@ -640,6 +646,121 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
         src_pair[r] = -1;
 }
 
+// ---------------------------------------------------------------------------
+// Dedup layout by counting, for T*K <= kSmallMaxPairs entries with K and P
+// powers of two.  Couple (t, p) is present when token t has a valid expert in
+// partition p; its row is the partition's offset plus the number of earlier
+// tokens present in p.  Every workgroup loads all T*K ids (coalesced, one per
+// thread and round); a token's K entries are K aligned lanes of one wave, so
+// an entry knows from a DPP prefix OR over its group whether a lower entry of
+// its token is in the same partition, and the entry that is first counts the
+// token for that partition, in LDS: in all, and before the workgroup's
+// tokens (e / L by an exact multiply-shift, as in the fused kernels).  One
+// barrier later wave 0 takes the workgroup's couples, one per lane in couple
+// order -- 64 / P tokens, lane u*P + p for couple (t_lo + u, p) -- derives
+// each couple's top-k mask from its token's ids, ranks it among the
+// workgroup's earlier tokens with one ballot and writes tp_row, kmask and
+// tp_src with consecutive lanes on consecutive couples.  Launch block 0
+// writes the per-partition totals and offsets, status and the tp_src tail.
+// Spreading the work this way keeps every global access coalesced and each
+// workgroup's share small: one workgroup doing all of it (a thread per
+// token, its P couples' writes strided by P) took 6-8 us at 128 x top-8 / 16
+// partitions on one CU's memory pipeline.
+template <int kIds, int kMaxK>
+__global__ __launch_bounds__(kLayoutThreads) void dedup_layout_count_kernel(
+    const int32_t* __restrict__ idx, int T, int K, int E, int P, int32_t* __restrict__ tp_row,
+    int32_t* __restrict__ part_tokens, int32_t* __restrict__ part_token_offset,
+    int32_t* __restrict__ tp_src, uint32_t* __restrict__ kmask, uint32_t* __restrict__ status)
+{
+    static_assert(kIds * kLayoutThreads <= kSmallMaxPairs, "the launcher's bound");
+    __shared__ int32_t cnt[2][kMaxTopK];        // tokens present per partition: all, before t_lo
+    __shared__ uint32_t sbad;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int n = T * K;
+    const int kshift = __builtin_ctz((unsigned)K);          // K is a power of two
+    const int tpw = kWave / P;                              // tokens per workgroup (P a power of two)
+    const int t_lo = blockIdx.x == 0 ? T : (int)(blockIdx.x - 1) * tpw;
+    // e / L for e < 1024 and L <= 1024: (e * magic) >> 20 with magic =
+    // floor(2^20 / L) + 1, exact since e * (L - 2^20 mod L) < 2^20
+    const uint32_t magic = (1u << 20) / (uint32_t)(E / P) + 1u;
+
+    int id[kIds];                                           // loads first, addresses clamped
+#pragma unroll
+    for (int j = 0; j < kIds; ++j) {
+        const int p = j * kLayoutThreads + tid;
+        id[j] = idx[p < n ? p : n - 1];
+    }
+    // wave 0 of a couple workgroup: couple (t_lo + u, pc) on lane u * P + pc;
+    // its token's ids loaded now, with the others (uniform branch)
+    const int u = lane / P;                                 // P a power of two: a shift
+    const int pc = lane - u * P;
+    const int t = t_lo + u;
+    const bool own = t < T;                                 // lanes of tokens past T: nothing
+    int ids[kMaxK];
+    if (blockIdx.x != 0 && tid < kWave) {
+        const int64_t row = (int64_t)(own ? t : T - 1) * K;
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) ids[k] = idx[row + (k < K ? k : K - 1)];
+    }
+    if (tid < 2 * kMaxTopK) cnt[tid / kMaxTopK][tid % kMaxTopK] = 0;
+    if (tid == 0) sbad = 0u;
+    lds_barrier();                                          // (1) counters cleared
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < kIds; ++j) {
+        const int p = j * kLayoutThreads + tid;
+        const int e = p < n ? id[j] : -1;
+        bad |= e >= E;
+        const bool valid = e >= 0 && e < E;
+        const uint32_t pp = valid ? ((uint32_t)e * magic) >> 20 : 0u;
+        const uint32_t bit = valid ? 1u << pp : 0u;
+        const uint32_t lower = group_excl_or(bit, K, lane);   // every lane: DPP sources
+        if (valid && !(lower & bit)) {                      // the token's first entry in pp
+            atomicAdd(&cnt[0][pp], 1);
+            if ((p >> kshift) < t_lo) atomicAdd(&cnt[1][pp], 1);
+        }
+    }
+    if (__ballot(bad) != 0ull && lane == 0) sbad = 1u;
+    lds_barrier();                                          // (2) counts complete
+
+    const int tot = lane < P ? cnt[0][lane] : 0;
+    const int incl = wave_inclusive_scan(tot);              // partition offsets
+    const int M = read_lane(incl, P - 1);
+    if (blockIdx.x == 0) {
+        if (tid < P) {
+            part_tokens[tid] = tot;
+            part_token_offset[tid] = incl - tot;
+        }
+        if (tid == 0) {
+            part_token_offset[P] = M;
+            *status = sbad ? 1u : 0u;
+        }
+        for (int r = M + tid; r < T * P; r += kLayoutThreads) tp_src[r] = -1;
+        return;
+    }
+    if (tid >= kWave) return;                               // wave 0 takes the couples
+    uint32_t m = 0u;                                        // top-k mask of the couple
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        const bool valid = k < K && ids[k] >= 0 && ids[k] < E;
+        const uint32_t pp = valid ? ((uint32_t)ids[k] * magic) >> 20 : 32u;
+        m |= (pp == (uint32_t)pc ? 1u : 0u) << k;
+    }
+    if (!own) m = 0u;
+    // earlier tokens of this workgroup present in pc: the lanes u' * P + pc, u' < u
+    const uint64_t same = (~0ull / ((1ull << P) - 1ull)) << pc;
+    const uint64_t b = __ballot(m != 0u) & same & ((1ull << lane) - 1ull);
+    const int before = __shfl(incl - tot, pc) + cnt[1][pc] + __builtin_popcountll(b);
+    if (own) {
+        const int j = t * P + pc;
+        const int r = m ? before : -1;
+        tp_row[j] = r;
+        kmask[j] = m;
+        if (r >= 0) tp_src[r] = j;
+    }
+}
+
 int64_t num_chunks(int64_t n) { return (n + kChunkPairs - 1) / kChunkPairs; }
 
 }  // namespace
@@ -729,6 +850,16 @@ hipError_t launch_dedup_layout(const int32_t* idx, int T, int K, int E, int P, i
                                int32_t* part_tokens, int32_t* part_token_offset, int32_t* tp_src,
                                uint32_t* kmask, uint32_t* status, void* ws, hipStream_t stream)
 {
+    const bool pow2 = (K & (K - 1)) == 0 && (P & (P - 1)) == 0;
+    if (T >= 1 && pow2 && (int64_t)T * K <= kSmallMaxPairs) {
+        const unsigned blocks = (unsigned)((T + kWave / P - 1) / (kWave / P)) + 1;
+        const bool one = (int64_t)T * K <= kLayoutThreads;
+        hipLaunchKernelGGL(K <= 8 ? (one ? dedup_layout_count_kernel<1, 8> : dedup_layout_count_kernel<2, 8>)
+                                  : (one ? dedup_layout_count_kernel<1, 16> : dedup_layout_count_kernel<2, 16>),
+                           dim3(blocks), dim3(kLayoutThreads), 0, stream, idx, T, K, E, P, tp_row,
+                           part_tokens, part_token_offset, tp_src, kmask, status);
+        return hipGetLastError();
+    }
     // ids 0..P-1 with one partition per id: the per-"expert" counts and scan
     // are the per-partition token counts and offsets.
     const DedupEntries src{idx, kmask, K, E, E / P, P};

@@ -48,9 +48,12 @@ DEDUP_EDGE = {
     "K1": dict(K=1),
     "K16_P16": dict(K=16, E=64, P=16),
     "H640": dict(H=640, T=33),
-    "single_wg_limit_2048": dict(T=256, H=256, P=8),     # T*P = 2048: one layout workgroup
-    "chunked_4096": dict(T=512, H=256, P=8),
-    "chunked_4104": dict(T=513, H=256, P=8),             # T*P = 4104: chunked layout
+    "T256_P8": dict(T=256, H=256, P=8),                  # ep_dedup_layout: one thread per token
+    "T512_P8": dict(T=512, H=256, P=8),
+    "T513_P8": dict(T=513, H=256, P=8),
+    "token_kernel_limit_1024": dict(T=1024, H=128, E=64, P=16),   # 16 waves, every partition
+    "over_token_kernel_1025": dict(T=1025, H=128, P=8),  # T*P = 8200: chunked couples
+    "single_wg_P1_T2000": dict(T=2000, H=128, E=32, P=1),  # T*P = 2000: single-workgroup couples
     "many_chunks_scan_pass": dict(T=40000, H=128, E=64, P=8),   # > 256 chunks of couples
     "bf16": dict(payload="bf16", T=50, H=512),
 }
