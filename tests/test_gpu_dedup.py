@@ -146,11 +146,29 @@ def test_dedup_masked_duplicate_and_bad_ids(T):
     assert int(got["kmask"][3 * wl.P + 7 // (wl.E // wl.P)]) == 0x3F
 
 
-def test_dedup_empty_batch():
+@pytest.mark.parametrize("fused", [False, True])
+def test_dedup_empty_batch(fused):
+    """T = 0 through ep_dedup_layout, and through ep_dedup_layout_dispatch
+    (the plain layout's outputs included): zero counts and offsets, clean
+    status."""
     import torch
     import combine_ep_layout_05_amd as ep
+    print("dedup case T=0 fused=%s" % fused, flush=True)
     db = ep.EpDedupBuffers(0, 1024, 8, 32, 8)
-    db.layout(torch.empty((0, 8), dtype=torch.int32, device="cuda"))
+    idx = torch.empty((0, 8), dtype=torch.int32, device="cuda")
+    for t in (db.part_tokens, db.part_token_offset, db.status):
+        t.fill_(-7)
+    if fused:
+        # the per-expert layout goes to `buf`, the status (one for the call) to db
+        buf = ep.EpBuffers(0, 1024, 8, 32, 8)
+        for t in (buf.expert_count, buf.expert_offset, buf.part_count, buf.part_offset):
+            t.fill_(-7)
+        db.layout_dispatch(idx, torch.empty((0, 1024), dtype=torch.bfloat16, device="cuda"), buf)
+        torch.cuda.synchronize()
+        for t in (buf.expert_count, buf.expert_offset, buf.part_count, buf.part_offset):
+            assert np.all(t.cpu().numpy() == 0)
+    else:
+        db.layout(idx)
     torch.cuda.synchronize()
     assert np.all(db.part_tokens.cpu().numpy() == 0)
     assert np.all(db.part_token_offset.cpu().numpy() == 0)

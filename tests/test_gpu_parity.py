@@ -205,10 +205,15 @@ def test_all_masked_batch():
     assert int(got["expert_offset"][-1]) == 0 and np.all(got["out"] == 0)
 
 
-def test_empty_batch():
+@pytest.mark.parametrize("fused", [False, True])
+def test_empty_batch(fused):
+    """T = 0 through ep_layout + ep_dispatch + ep_combine, and through
+    ep_layout_dispatch (which takes the same guarded one-wave layout kernel
+    and enqueues no dispatch): zero counts and offsets, clean status."""
     wl = WORKLOADS["tiny_4x1024"].with_(name="edge_T0", T=0)
     d = generate(wl, seed=1)
-    got = run_gpu(wl, d)
+    print("case edge_T0 fused=%s" % fused, flush=True)
+    got = run_gpu(wl, d, fused=fused)
     assert np.all(got["expert_count"] == 0) and np.all(got["expert_offset"] == 0)
     assert np.all(got["part_offset"] == 0) and int(got["status"][0]) == 0
 
