@@ -447,9 +447,24 @@ def large_leg(name, graph_steps, min_steps=100, min_ms=50.0):
     return out
 
 
+def native_ceilings(mib=1024):
+    """The package's ep_ceilings probe (hand-written 16-byte-per-lane read,
+    write and copy kernels over buffers far larger than the caches), run as a
+    child process before this process touches the GPU."""
+    exe = os.path.join(ROOT, "combine_ep_layout_05_amd", "ep_ceilings")
+    if not os.path.exists(exe):
+        return {"error": "ep_ceilings not built"}
+    r = subprocess.run([exe, str(mib)], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        return {"error": (r.stderr or r.stdout)[-300:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def ceilings(mib=1024, samples=10):
-    """Plain HBM copy, write and read rates of this GPU (torch's copy, fill and
-    sum kernels over buffers far larger than the caches)."""
+    """HBM read, write and copy rates of this GPU: the native probe's kernels
+    (the ceilings), then torch's copy, fill and sum kernels over the same
+    sizes for comparison."""
+    native = native_ceilings(mib)
     import torch
     n = mib << 20
     a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -474,7 +489,8 @@ def ceilings(mib=1024, samples=10):
             v.append(nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
         res[name] = {"GBps_median": round(float(np.median(v)), 1), "GBps_max": round(max(v), 1),
                      "bytes": nbytes}
-    return {"ceilings": res, "buffer_MiB": mib}
+    return {"ceilings": native.get("ceilings_native", native), "torch_kernels": res,
+            "buffer_MiB": mib}
 
 
 def main():

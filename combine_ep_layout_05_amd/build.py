@@ -24,6 +24,7 @@ FLAGS = [
 
 
 LOOP = os.path.join(HERE, "ep_loop")     # native serving-loop timer over the C ABI
+CEILINGS = os.path.join(HERE, "ep_ceilings")   # native HBM read/write/copy rate probe
 
 
 def sources():
@@ -55,6 +56,18 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     if r.returncode != 0:
         raise RuntimeError("hipcc failed on ep_loop.cpp:\n" + r.stdout + r.stderr)
     os.replace(tmp, LOOP)
+    # the ceilings probe: its own kernels, same code-generation flags, no library
+    tmp = CEILINGS + ".tmp%d" % os.getpid()
+    cmd = ["hipcc", "-x", "hip", *[f for f in FLAGS if f not in ("-fPIC", "-shared")
+                                   and not f.startswith("-Wl,-soname")],
+           os.path.join(CSRC, "ep_ceilings.cpp"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+        raise RuntimeError("hipcc failed on ep_ceilings.cpp:\n" + msg)
+    os.replace(tmp, CEILINGS)
     return LIB
 
 
