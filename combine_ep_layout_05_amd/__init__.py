@@ -59,6 +59,9 @@ _SIGS = {
     "ep_dedup_layout_dispatch_workspace_bytes": ([_I, _I, _I, _I], _SZ),
     "ep_dedup_layout_dispatch": ([_P, _P, _I, _I, _I, _I, _I, _I] + [_P] * 12 + [_P, _SZ, _P, _P, _P],
                                  _I),
+    "ep_dedup_layout_dispatch_geom": ([_P, _P, _I, _I, _I, _I, _I, _I] + [_P] * 12
+                                      + [_P, _SZ, _P, _P, _I, _I, _I, _P], _I),
+    "ep_dedup_layout_dispatch_plan": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, _P], _I),
     "ep_combine_reduce": ([_P, _P, _I, _I, _I, _P, _P], _I),
     "ep_strerror": ([_I], ctypes.c_char_p),
     "ep_last_hip_error": ([], _I),
@@ -235,18 +238,28 @@ def ep_layout_dispatch(topk_idx, x, E, P, payload, expert_count, expert_offset, 
                _lib.ep_layout_dispatch_geom(*args, *_geometry(geometry), _stream(stream)))
 
 
-def ep_layout_dispatch_plan(T, H, K, E, P, payload, geometry=None):
-    """How ep_layout_dispatch(_geom) would run this batch (host only):
-    {"kernel": ..., "waves": ..., "blocks" or "max_blocks": ..., "slice_cols": ...}."""
+def _plan(name, T, H, K, E, P, payload, geometry):
     payload = PAYLOADS.get(payload, payload)
     plan = (ctypes.c_int32 * 4)()
     wv, mb, sc = _geometry(geometry) if geometry is not None else (0, 0, 0)
-    _check("ep_layout_dispatch_plan", _lib.ep_layout_dispatch_plan(
-        T, H, K, E, P, payload, wv, mb, sc, ctypes.cast(plan, ctypes.c_void_p)))
+    _check(name, getattr(_lib, name)(T, H, K, E, P, payload, wv, mb, sc,
+                                     ctypes.cast(plan, ctypes.c_void_p)))
     kind = PLAN_KINDS[plan[0]]
     d = {"kernel": kind, "waves": int(plan[1]), "slice_cols": int(plan[3])}
     d["max_blocks" if kind == "layout_then_dispatch" else "blocks"] = int(plan[2])
     return d
+
+
+def ep_dedup_layout_dispatch_plan(T, H, K, E, P, payload, geometry=None):
+    """How ep_dedup_layout_dispatch(_geom) would run this batch (host only),
+    in the form ep_layout_dispatch_plan returns."""
+    return _plan("ep_dedup_layout_dispatch_plan", T, H, K, E, P, payload, geometry)
+
+
+def ep_layout_dispatch_plan(T, H, K, E, P, payload, geometry=None):
+    """How ep_layout_dispatch(_geom) would run this batch (host only):
+    {"kernel": ..., "waves": ..., "blocks" or "max_blocks": ..., "slice_cols": ...}."""
+    return _plan("ep_layout_dispatch_plan", T, H, K, E, P, payload, geometry)
 
 
 def ep_layout_dispatch_noalloc(topk_idx, x, E, P, payload, expert_count, expert_offset,
@@ -337,8 +350,10 @@ def ep_dedup_layout_dispatch_workspace_bytes(T: int, K: int, E: int, P: int) -> 
 def ep_dedup_layout_dispatch(topk_idx, x, E, P, payload, expert_count, expert_offset, part_count,
                              part_offset, row_of_pair, src_pair, tp_row, part_tokens,
                              part_token_offset, tp_src, kmask, status, ws, recv_x,
-                             recv_scales=None, stream=None):
-    """Per-expert layout + dedup layout + dedup dispatch (one launch for small batches)."""
+                             recv_scales=None, stream=None, geometry=None):
+    """Per-expert layout + dedup layout + dedup dispatch (one launch for small
+    batches).  geometry: None (the library's choice) or (waves_per_block,
+    max_blocks[, slice_cols]) as ep_dedup_layout_dispatch_geom takes it."""
     _dt(topk_idx, torch.int32)
     _dt(x, *_BF16)
     payload = PAYLOADS.get(payload, payload)
@@ -350,11 +365,15 @@ def ep_dedup_layout_dispatch(topk_idx, x, E, P, payload, expert_count, expert_of
                     src_pair, status)
     _dedup_outputs(T, P, tp_row, part_tokens, part_token_offset, tp_src, kmask, status)
     _receive(payload, T * P, H, recv_x, recv_scales)
-    _check("ep_dedup_layout_dispatch", _lib.ep_dedup_layout_dispatch(
-        _ptr(topk_idx), _ptr(x), T, H, K, E, P, payload, _ptr(expert_count), _ptr(expert_offset),
-        _ptr(part_count), _ptr(part_offset), _ptr(row_of_pair), _ptr(src_pair), _ptr(tp_row),
-        _ptr(part_tokens), _ptr(part_token_offset), _ptr(tp_src), _ptr(kmask), _ptr(status),
-        _ptr(ws), _ws_bytes(ws), _ptr(recv_x), _ptr(recv_scales), _stream(stream)))
+    args = (_ptr(topk_idx), _ptr(x), T, H, K, E, P, payload, _ptr(expert_count),
+            _ptr(expert_offset), _ptr(part_count), _ptr(part_offset), _ptr(row_of_pair),
+            _ptr(src_pair), _ptr(tp_row), _ptr(part_tokens), _ptr(part_token_offset), _ptr(tp_src),
+            _ptr(kmask), _ptr(status), _ptr(ws), _ws_bytes(ws), _ptr(recv_x), _ptr(recv_scales))
+    if geometry is None:
+        _check("ep_dedup_layout_dispatch", _lib.ep_dedup_layout_dispatch(*args, _stream(stream)))
+    else:
+        _check("ep_dedup_layout_dispatch_geom",
+               _lib.ep_dedup_layout_dispatch_geom(*args, *_geometry(geometry), _stream(stream)))
 
 
 def ep_combine_partial(expert_out, row_of_pair, topk_w, tp_row, kmask, P, partial, stream=None):
@@ -522,14 +541,21 @@ class EpDedupBuffers:
                         self.part_token_offset, self.tp_src, self.kmask, self.status, self.ws,
                         stream)
 
-    def layout_dispatch(self, topk_idx, x, plain, stream=None):
+    def layout_dispatch(self, topk_idx, x, plain, stream=None, geometry=None):
         """ep_dedup_layout_dispatch: the per-expert layout into `plain` (an
-        EpBuffers of the same shape), the dedup layout and dispatch here."""
+        EpBuffers of the same shape), the dedup layout and dispatch here.
+        geometry: None or a (waves_per_block, max_blocks[, slice_cols]) tuple
+        (ep_dedup_layout_dispatch_geom)."""
         ep_dedup_layout_dispatch(topk_idx, x, self.E, self.P, self.payload, plain.expert_count,
                                  plain.expert_offset, plain.part_count, plain.part_offset,
                                  plain.row_of_pair, plain.src_pair, self.tp_row, self.part_tokens,
                                  self.part_token_offset, self.tp_src, self.kmask, self.status,
-                                 self.ws, self.recv_x, self.recv_scales, stream)
+                                 self.ws, self.recv_x, self.recv_scales, stream, geometry)
+
+    def plan(self, geometry=None):
+        """How layout_dispatch runs this shape (ep_dedup_layout_dispatch_plan)."""
+        return ep_dedup_layout_dispatch_plan(self.T, self.H, self.K, self.E, self.P, self.payload,
+                                             geometry)
 
     def dispatch(self, x, stream=None):
         """One copy of each token per partition it reaches (ep_dispatch, K = P, tp_row)."""

@@ -379,13 +379,16 @@ size_t ep_dedup_layout_dispatch_workspace_bytes(int T, int K, int E, int P)
     return a > b ? a : b;
 }
 
-int ep_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
-                             int P, int payload, int32_t* expert_count, int32_t* expert_offset,
-                             int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
-                             int32_t* src_pair, int32_t* tp_row, int32_t* part_tokens,
-                             int32_t* part_token_offset, int32_t* tp_src, uint32_t* kmask,
-                             uint32_t* status, void* ws, size_t ws_bytes, void* recv_x,
-                             float* recv_scales, void* stream)
+namespace {
+
+// Argument checks of ep_dedup_layout_dispatch(_geom) that involve neither the
+// workspace nor the geometry.
+int dedup_layout_dispatch_args(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
+                               int E, int P, int payload, int32_t* expert_count,
+                               int32_t* expert_offset, int32_t* part_count, int32_t* part_offset,
+                               int32_t* row_of_pair, int32_t* src_pair, int32_t* tp_row,
+                               int32_t* part_tokens, int32_t* part_token_offset, int32_t* tp_src,
+                               uint32_t* kmask, uint32_t* status, void* recv_x, float* recv_scales)
 {
     if (payload != EP_PAYLOAD_FP8_E4M3FN && payload != EP_PAYLOAD_BF16) return EP_ENOTSUP;
     if (!routing_ok(T, K) || !dedup_ok(T, P) || E < 1 || E > EP_MAX_EXPERTS || E % P != 0 || H <= 0)
@@ -403,15 +406,49 @@ int ep_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, 
             return EP_EINVAL;
         if (payload == EP_PAYLOAD_FP8_E4M3FN && !ptr_ok(recv_scales, 4)) return EP_EINVAL;
     }
+    return EP_OK;
+}
+
+// Which path a dedup batch takes and its geometry: the fused kernels (a
+// workgroup size only) or the two layouts then the dispatch to the couple
+// rows (K = P entries per token over tp_row) with the dispatch geometry.
+bool dedup_layout_dispatch_route(int T, int H, int K, int P, int waves_per_block, int max_blocks,
+                                 int slice_cols, bool* fused, ep::FusedPlan* plan,
+                                 ep::MoveGeometry* g)
+{
+    *fused = T > 0 && ep::fused_layout_dispatch_fits(T, H, K);
+    if (*fused) {
+        if (max_blocks != 0 || (slice_cols != 0 && slice_cols != ep::kStepCols)) return false;
+        return ep::plan_dedup_layout_dispatch(T, H, K, P, waves_per_block, plan);
+    }
+    if (!move_geometry(waves_per_block, max_blocks, slice_cols, g)) return false;
+    return T == 0 || ep::dispatch_launch_ok(T, H, *g);
+}
+
+int dedup_layout_dispatch_checked(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
+                                  int E, int P, int payload, int32_t* expert_count,
+                                  int32_t* expert_offset, int32_t* part_count,
+                                  int32_t* part_offset, int32_t* row_of_pair, int32_t* src_pair,
+                                  int32_t* tp_row, int32_t* part_tokens,
+                                  int32_t* part_token_offset, int32_t* tp_src, uint32_t* kmask,
+                                  uint32_t* status, void* ws, size_t ws_bytes, void* recv_x,
+                                  float* recv_scales, int waves_per_block, int max_blocks,
+                                  int slice_cols, void* stream)
+{
     const size_t need = ep_dedup_layout_dispatch_workspace_bytes(T, K, E, P);
     if (need > 0 && (ws_bytes < need || !ptr_ok(ws, 16))) return EP_EINVAL;
-    if (!ep::dispatch_launch_ok(T, H, ep::kDefaultGeometry)) return EP_EINVAL;
+    bool fused = false;
+    ep::FusedPlan plan{};
+    ep::MoveGeometry g = ep::kDefaultGeometry;
+    if (!dedup_layout_dispatch_route(T, H, K, P, waves_per_block, max_blocks, slice_cols, &fused,
+                                     &plan, &g))
+        return EP_EINVAL;
     hipStream_t s = (hipStream_t)stream;
-    if (T > 0 && ep::fused_layout_dispatch_fits(T, H, K))
+    if (fused)
         return from_hip(ep::launch_dedup_layout_dispatch(
             topk_idx, x, T, H, K, E, P, payload, expert_count, expert_offset, part_count,
             part_offset, row_of_pair, src_pair, tp_row, part_tokens, part_token_offset, tp_src,
-            kmask, status, recv_x, recv_scales, s));
+            kmask, status, recv_x, recv_scales, s, plan.waves));
     // larger batches: the two layouts one after the other on the stream (they
     // share the workspace), then the dispatch to the dedup rows
     int rc = from_hip(ep::launch_layout(topk_idx, T, K, E, P, expert_count, expert_offset,
@@ -421,7 +458,81 @@ int ep_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, 
     rc = from_hip(ep::launch_dedup_layout(topk_idx, T, K, E, P, tp_row, part_tokens,
                                           part_token_offset, tp_src, kmask, status, ws, s));
     if (rc != EP_OK || T == 0) return rc;
-    return from_hip(ep::launch_dispatch(x, T, H, P, tp_row, payload, recv_x, recv_scales, s));
+    return from_hip(ep::launch_dispatch(x, T, H, P, tp_row, payload, recv_x, recv_scales, s, g));
+}
+
+}  // namespace
+
+int ep_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K, int E,
+                             int P, int payload, int32_t* expert_count, int32_t* expert_offset,
+                             int32_t* part_count, int32_t* part_offset, int32_t* row_of_pair,
+                             int32_t* src_pair, int32_t* tp_row, int32_t* part_tokens,
+                             int32_t* part_token_offset, int32_t* tp_src, uint32_t* kmask,
+                             uint32_t* status, void* ws, size_t ws_bytes, void* recv_x,
+                             float* recv_scales, void* stream)
+{
+    const int rc = dedup_layout_dispatch_args(topk_idx, x, T, H, K, E, P, payload, expert_count,
+                                              expert_offset, part_count, part_offset, row_of_pair,
+                                              src_pair, tp_row, part_tokens, part_token_offset,
+                                              tp_src, kmask, status, recv_x, recv_scales);
+    if (rc != EP_OK) return rc;
+    return dedup_layout_dispatch_checked(topk_idx, x, T, H, K, E, P, payload, expert_count,
+                                         expert_offset, part_count, part_offset, row_of_pair,
+                                         src_pair, tp_row, part_tokens, part_token_offset, tp_src,
+                                         kmask, status, ws, ws_bytes, recv_x, recv_scales, 0, 0, 0,
+                                         stream);
+}
+
+int ep_dedup_layout_dispatch_geom(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
+                                  int E, int P, int payload, int32_t* expert_count,
+                                  int32_t* expert_offset, int32_t* part_count,
+                                  int32_t* part_offset, int32_t* row_of_pair, int32_t* src_pair,
+                                  int32_t* tp_row, int32_t* part_tokens,
+                                  int32_t* part_token_offset, int32_t* tp_src, uint32_t* kmask,
+                                  uint32_t* status, void* ws, size_t ws_bytes, void* recv_x,
+                                  float* recv_scales, int waves_per_block, int max_blocks,
+                                  int slice_cols, void* stream)
+{
+    const int rc = dedup_layout_dispatch_args(topk_idx, x, T, H, K, E, P, payload, expert_count,
+                                              expert_offset, part_count, part_offset, row_of_pair,
+                                              src_pair, tp_row, part_tokens, part_token_offset,
+                                              tp_src, kmask, status, recv_x, recv_scales);
+    if (rc != EP_OK) return rc;
+    return dedup_layout_dispatch_checked(topk_idx, x, T, H, K, E, P, payload, expert_count,
+                                         expert_offset, part_count, part_offset, row_of_pair,
+                                         src_pair, tp_row, part_tokens, part_token_offset, tp_src,
+                                         kmask, status, ws, ws_bytes, recv_x, recv_scales,
+                                         waves_per_block, max_blocks, slice_cols, stream);
+}
+
+int ep_dedup_layout_dispatch_plan(int T, int H, int K, int E, int P, int payload,
+                                  int waves_per_block, int max_blocks, int slice_cols,
+                                  int32_t* plan)
+{
+    if (plan == nullptr) return EP_EINVAL;
+    if (payload != EP_PAYLOAD_FP8_E4M3FN && payload != EP_PAYLOAD_BF16) return EP_ENOTSUP;
+    if (!routing_ok(T, K) || !dedup_ok(T, P) || E < 1 || E > EP_MAX_EXPERTS || E % P != 0 || H <= 0)
+        return EP_EINVAL;
+    if (payload == EP_PAYLOAD_FP8_E4M3FN && H % ep::kScaleBlock != 0) return EP_EINVAL;
+    if (payload == EP_PAYLOAD_BF16 && H % ep::kColsPerLane != 0) return EP_EINVAL;
+    bool fused = false;
+    ep::FusedPlan fp{};
+    ep::MoveGeometry g = ep::kDefaultGeometry;
+    if (!dedup_layout_dispatch_route(T, H, K, P, waves_per_block, max_blocks, slice_cols, &fused,
+                                     &fp, &g))
+        return EP_EINVAL;
+    if (fused) {
+        plan[0] = fp.kind;
+        plan[1] = fp.waves;
+        plan[2] = (int32_t)fp.blocks;
+        plan[3] = ep::kStepCols;
+    } else {
+        plan[0] = EP_PLAN_LAYOUT_THEN_DISPATCH;
+        plan[1] = g.waves;
+        plan[2] = g.max_blocks;
+        plan[3] = g.slice_steps * ep::kStepCols;
+    }
+    return EP_OK;
 }
 
 int ep_combine_partial(const uint16_t* expert_out, const int32_t* row_of_pair,

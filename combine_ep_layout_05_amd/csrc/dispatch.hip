@@ -1208,6 +1208,45 @@ hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, in
                                  recv_scales, steps, items, none, stream);
 }
 
+bool plan_dedup_layout_dispatch(int T, int H, int K, int P, int waves, FusedPlan* plan)
+{
+    const int steps = (H + kStepCols - 1) / kStepCols;
+    const int64_t items = (int64_t)T * steps;
+    const int64_t n = (int64_t)T * K;
+    if (T < 1 || n > kFusedMaxPairs || P > kMaxTopK || items > kMaxGridBlocks || waves < 0)
+        return false;
+    FusedPlan pl{};
+    if (n <= kCountMaxPairs && (K & (K - 1)) == 0) {
+        // the counting kernel: every workgroup inside one token (8, 7 or 6
+        // waves dividing the steps per token, the largest by default), a
+        // token's K entries on K aligned lanes (K a power of two, so K
+        // divides 64)
+        int W = 0;
+        if (waves == 0) {
+            for (int c = 8; c >= 6; --c)
+                if (steps % c == 0) { W = c; break; }
+        } else if (waves >= 6 && waves <= 8 && steps % waves == 0) {
+            W = waves;
+        }
+        if (W != 0) {
+            pl.kind = kFusedCount;
+            pl.waves = W;
+            pl.own8 = K <= 8;
+            pl.blocks = (unsigned)((items + W - 1) / W) + 1;
+            *plan = pl;
+            return true;
+        }
+    }
+    // the general kernel: 4 or 8 waves, the workgroup's own entries within one wave
+    pl.kind = kFusedGeneral;
+    pl.waves = waves ? waves : fused_waves(items, steps, K);
+    if (pl.waves != 4 && pl.waves != 8) return false;
+    if (max_own_tokens(pl.waves, steps) * K > kWave) return false;
+    pl.blocks = (unsigned)((items + pl.waves - 1) / pl.waves);
+    *plan = pl;
+    return true;
+}
+
 hipError_t launch_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H,
                                         int K, int E, int P, int payload, int32_t* expert_count,
                                         int32_t* expert_offset, int32_t* part_count,
@@ -1215,33 +1254,26 @@ hipError_t launch_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t*
                                         int32_t* src_pair, int32_t* tp_row, int32_t* part_tokens,
                                         int32_t* part_token_offset, int32_t* tp_src,
                                         uint32_t* kmask, uint32_t* status, void* recv_x,
-                                        float* recv_scales, hipStream_t stream)
+                                        float* recv_scales, hipStream_t stream, int waves)
 {
+    FusedPlan pl;
+    if (!plan_dedup_layout_dispatch(T, H, K, P, waves, &pl)) return hipErrorInvalidValue;
     const int steps = (H + kStepCols - 1) / kStepCols;
-    const int64_t items = (int64_t)T * steps;
+    const int items = T * steps;
     const int n = T * K;
-    if (T == 0 || n > kFusedMaxPairs || P > kMaxTopK || items > kMaxGridBlocks)
-        return hipErrorInvalidValue;
     const DedupOutputs dd{tp_row, part_tokens, part_token_offset, tp_src, kmask};
-    if (n <= kCountMaxPairs && (K & (K - 1)) == 0) {
-        // the counting kernel: every workgroup inside one token (8, 7 or 6
-        // waves dividing the steps per token), a token's K entries on K
-        // aligned lanes (K a power of two, so K divides 64)
-        for (int W = 8; W >= 6; --W)
-            if (steps % W == 0)
-                return launch_count<true>(payload, W, K <= 8, topk_idx, x, n, H, K, E, P,
-                                          expert_count, expert_offset, part_count, part_offset,
-                                          row_of_pair, src_pair, status, recv_x, recv_scales,
-                                          steps, (int)items, dd, stream);
-    }
-    const int W = fused_waves(items, steps, K);
+    if (pl.kind == kFusedCount)
+        return launch_count<true>(payload, pl.waves, pl.own8, topk_idx, x, n, H, K, E, P,
+                                  expert_count, expert_offset, part_count, part_offset,
+                                  row_of_pair, src_pair, status, recv_x, recv_scales, steps, items,
+                                  dd, stream);
     return payload == 0
-        ? launch_fused<0, true>(W, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
+        ? launch_fused<0, true>(pl.waves, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
                                 part_count, part_offset, row_of_pair, src_pair, status, recv_x,
-                                recv_scales, steps, (int)items, dd, stream)
-        : launch_fused<1, true>(W, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
+                                recv_scales, steps, items, dd, stream)
+        : launch_fused<1, true>(pl.waves, topk_idx, x, n, H, K, E, P, expert_count, expert_offset,
                                 part_count, part_offset, row_of_pair, src_pair, status, recv_x,
-                                recv_scales, steps, (int)items, dd, stream);
+                                recv_scales, steps, items, dd, stream);
 }
 
 hipError_t launch_e4m3fn_encode(const float* in, int64_t n, uint8_t* out, hipStream_t stream)

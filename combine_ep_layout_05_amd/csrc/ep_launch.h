@@ -72,6 +72,12 @@ hipError_t launch_combine_partial(const uint16_t* y, const int32_t* row_of_pair,
 hipError_t launch_combine_reduce(const uint16_t* partial, const int32_t* tp_row, int T, int H,
                                  int P, uint16_t* out, hipStream_t stream);
 
+// The same for the per-destination (dedup) fused kernels: the counting one
+// (K a power of two, T*K <= 1024, 8, 7 or 6 waves dividing the 512-column
+// steps per token, so that every workgroup lies inside one token) or the
+// general one (4 or 8 waves); P <= kMaxTopK.
+bool plan_dedup_layout_dispatch(int T, int H, int K, int P, int waves, FusedPlan* plan);
+
 hipError_t launch_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, int T, int H,
                                         int K, int E, int P, int payload, int32_t* expert_count,
                                         int32_t* expert_offset, int32_t* part_count,
@@ -79,7 +85,7 @@ hipError_t launch_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t*
                                         int32_t* src_pair, int32_t* tp_row, int32_t* part_tokens,
                                         int32_t* part_token_offset, int32_t* tp_src,
                                         uint32_t* kmask, uint32_t* status, void* recv_x,
-                                        float* recv_scales, hipStream_t stream);
+                                        float* recv_scales, hipStream_t stream, int waves = 0);
 
 hipError_t launch_e4m3fn_encode(const float* in, int64_t n, uint8_t* out,
                                 hipStream_t stream);

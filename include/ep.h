@@ -382,6 +382,45 @@ int ep_layout_dispatch_plan(int T, int H, int K, int E, int P, int payload, int 
                             int max_blocks, int slice_cols, int32_t* plan);
 
 /*
+ * ep_dedup_layout_dispatch with an explicit launch geometry (0 = the
+ * library's choice for each value); same results, bit for bit.  Same
+ * arguments as ep_dedup_layout_dispatch, then the geometry, then the stream.
+ *   - A batch that runs fused (T*K <= 4096) takes only a workgroup size
+ *     (max_blocks 0, slice_cols 0 or 512):
+ *       K a power of two and T*K <= 1024 (EP_PLAN_FUSED_COUNT): 6, 7 or 8
+ *         waves that divide the 512-column steps per token, so that every
+ *         workgroup lies inside one token (default: the largest); when
+ *         none does, or another size is asked for, the general kernel;
+ *       otherwise (EP_PLAN_FUSED_GENERAL): 4 or 8 waves when a workgroup's
+ *         items touch at most 64 entries.
+ *   - A larger batch runs the two layouts and then the dispatch to the
+ *     couple rows (P entries per token over tp_row), which takes
+ *     (waves_per_block, max_blocks, slice_cols) as ep_dispatch_geom does.
+ * Errors: those of ep_dedup_layout_dispatch, and EP_EINVAL for a geometry
+ * the batch's kernels do not take (nothing is enqueued).
+ */
+int ep_dedup_layout_dispatch_geom(const int32_t* topk_idx, const uint16_t* x, int T, int H, int K,
+                                  int E, int P, int payload, int32_t* expert_count,
+                                  int32_t* expert_offset, int32_t* part_count,
+                                  int32_t* part_offset, int32_t* row_of_pair, int32_t* src_pair,
+                                  int32_t* tp_row, int32_t* part_tokens,
+                                  int32_t* part_token_offset, int32_t* tp_src, uint32_t* kmask,
+                                  uint32_t* status, void* ws, size_t ws_bytes, void* recv_x,
+                                  float* recv_scales, int waves_per_block, int max_blocks,
+                                  int slice_cols, void* stream);
+
+/*
+ * Host-only: how ep_dedup_layout_dispatch_geom would run a batch, written to
+ * plan[4] as by ep_layout_dispatch_plan (plan[0] EP_PLAN_FUSED_COUNT,
+ * EP_PLAN_FUSED_GENERAL or EP_PLAN_LAYOUT_THEN_DISPATCH).  EP_EINVAL (plan
+ * untouched) for arguments or a geometry ep_dedup_layout_dispatch_geom would
+ * reject, EP_ENOTSUP for another payload.  Nothing touches the GPU.
+ */
+int ep_dedup_layout_dispatch_plan(int T, int H, int K, int E, int P, int payload,
+                                  int waves_per_block, int max_blocks, int slice_cols,
+                                  int32_t* plan);
+
+/*
  * HIP graph capture for the small-token regime, where host enqueue paces the
  * GPU (MoRI PR #614, view-cache paragraph: at 4 tokens most of a round's
  * wall time was host work, and stable buffers are what make the op

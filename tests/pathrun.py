@@ -108,12 +108,12 @@ PLAIN_LAYOUT_KEYS = ("expert_count", "expert_offset", "part_count", "part_offset
                      "src_pair")
 
 
-def run_gpu_dedup(wl, d, stream=None, fused=False):
+def run_gpu_dedup(wl, d, stream=None, fused=False, geometry=None):
     """Per-destination path on the GPU: ep_layout (expert rows for the expert
     outputs), ep_dedup_layout, ep_dispatch with K = P over tp_row,
     ep_combine_partial and ep_combine_reduce; fused=True runs
-    ep_dedup_layout_dispatch in place of the first three.  Buffers start
-    poisoned."""
+    ep_dedup_layout_dispatch in place of the first three (with `geometry`,
+    ep_dedup_layout_dispatch_geom).  Buffers start poisoned."""
     ep = gpu_lib()
     buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
     db = ep.EpDedupBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
@@ -129,7 +129,7 @@ def run_gpu_dedup(wl, d, stream=None, fused=False):
     y = to_dev(d["y"].view(np.int16), torch.bfloat16)
     w = to_dev(d["w"])
     if fused:
-        db.layout_dispatch(idx, x, buf, stream)
+        db.layout_dispatch(idx, x, buf, stream, geometry)
     else:
         buf.layout(idx, stream)
         db.layout(idx, stream)

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
               "ep_dedup_layout", "ep_dedup_layout_workspace_bytes", "ep_combine_partial",
               "ep_combine_reduce", "ep_dedup_layout_dispatch",
               "ep_dedup_layout_dispatch_workspace_bytes", "ep_dispatch_geom", "ep_combine_geom",
-              "ep_layout_dispatch_geom", "ep_layout_dispatch_plan", "ep_layout_dispatch_noalloc"):
+              "ep_layout_dispatch_geom", "ep_layout_dispatch_plan", "ep_layout_dispatch_noalloc",
+              "ep_dedup_layout_dispatch_geom", "ep_dedup_layout_dispatch_plan"):
         assert n in names, n
 
 
@@ -170,6 +171,59 @@ def test_layout_dispatch_geom_host_side_validation(lib):
     assert list(plan) == [3, 2, 256, 1024]
     assert L.ep_layout_dispatch_plan(4, 6144, 8, 256, 16, 7, 0, 0, 0, pp) == -2
     assert L.ep_layout_dispatch_plan(4, 6144, 8, 256, 16, 0, 0, 0, 0, None) == -1
+
+
+def test_dedup_layout_dispatch_geom_host_side_validation(lib):
+    """ep_dedup_layout_dispatch_geom / _plan: the counting kernel takes 6, 7 or
+    8 waves that divide the 512-column steps per token, the general kernel 4
+    or 8, a fused batch no cap and no 1024-column slice; a large batch takes
+    the dispatch geometry.  Rejections happen on the host (fake pointers are
+    never dereferenced)."""
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L = lib
+    L.ep_dedup_layout_dispatch_geom.argtypes = ([P, P, I, I, I, I, I, I] + [P] * 12
+                                                + [P, ctypes.c_size_t, P, P, I, I, I, P])
+    L.ep_dedup_layout_dispatch_plan.argtypes = [I] * 9 + [P]
+    fake = P(0x10000)
+    outs = [fake] * 12
+    plan = (ctypes.c_int32 * 4)()
+    pp = ctypes.cast(plan, P)
+    # 128 x 7168 top-8 (14 steps per token): the counting kernel with 7 waves by default
+    assert L.ep_dedup_layout_dispatch_plan(128, 7168, 8, 288, 16, 0, 0, 0, 0, pp) == 0
+    assert list(plan) == [1, 7, 128 * 14 // 7 + 1, 512]
+    # 8 waves do not divide 14 steps: the general kernel; 4 waves too
+    assert L.ep_dedup_layout_dispatch_plan(128, 7168, 8, 288, 16, 0, 8, 0, 0, pp) == 0
+    assert list(plan) == [2, 8, 128 * 14 // 8, 512]
+    assert L.ep_dedup_layout_dispatch_plan(128, 7168, 8, 288, 16, 0, 4, 0, 0, pp) == 0
+    assert list(plan) == [2, 4, 128 * 14 // 4, 512]
+    # 24 steps per token (hidden 12288): 8 by default, 6 on request; 7 is no size it takes
+    assert L.ep_dedup_layout_dispatch_plan(64, 12288, 8, 256, 8, 0, 0, 0, 0, pp) == 0
+    assert list(plan) == [1, 8, 64 * 24 // 8 + 1, 512]
+    assert L.ep_dedup_layout_dispatch_plan(64, 12288, 8, 256, 8, 0, 6, 0, 0, pp) == 0
+    assert list(plan) == [1, 6, 64 * 24 // 6 + 1, 512]
+    for geom in [(7, 0, 0), (6, 0, 0), (2, 0, 0)]:
+        bad = 12288 if geom[0] == 7 else 7168
+        assert L.ep_dedup_layout_dispatch_plan(64, bad, 8, 256, 8, 0, *geom, pp) == -1
+        assert L.ep_dedup_layout_dispatch_geom(fake, fake, 64, bad, 8, 256, 8, 0, *outs, None, 0,
+                                               fake, fake, *geom, None) == -1
+    # a fused batch takes no cap and no 1024-column slice
+    for geom in [(4, 256, 0), (4, 0, 1024)]:
+        assert L.ep_dedup_layout_dispatch_plan(128, 7168, 8, 288, 16, 0, *geom, pp) == -1
+        assert L.ep_dedup_layout_dispatch_geom(fake, fake, 128, 7168, 8, 288, 16, 0, *outs, None,
+                                               0, fake, fake, *geom, None) == -1
+    # 640 tokens (5120 entries): the layouts, then the dispatch with its geometry
+    assert L.ep_dedup_layout_dispatch_plan(640, 7168, 8, 256, 8, 0, 2, 256, 1024, pp) == 0
+    assert list(plan) == [3, 2, 256, 1024]
+    assert L.ep_dedup_layout_dispatch_plan(640, 7168, 8, 256, 8, 0, 0, 0, 0, pp) == 0
+    assert list(plan) == [3, 4, 0, 512]
+    for geom in [(3, 0, 0), (4, -1, 0), (4, 0, 768)]:
+        assert L.ep_dedup_layout_dispatch_plan(640, 7168, 8, 256, 8, 0, *geom, pp) == -1
+    # other arguments: checked as ep_dedup_layout_dispatch checks them
+    assert L.ep_dedup_layout_dispatch_plan(4, 1024, 8, 64, 32, 0, 0, 0, 0, pp) == -1
+    assert L.ep_dedup_layout_dispatch_plan(4, 1024, 8, 32, 8, 5, 0, 0, 0, pp) == -2
+    assert L.ep_dedup_layout_dispatch_plan(4, 1024, 8, 32, 8, 0, 0, 0, 0, None) == -1
+    assert L.ep_dedup_layout_dispatch_geom(fake, P(0x10004), 4, 1024, 8, 32, 8, 0, *outs, None, 0,
+                                           fake, fake, 0, 0, 0, None) == -1
 
 
 def test_noalloc_host_side_validation(lib):

@@ -15,11 +15,11 @@ from workloads import WORKLOADS, generate
 pytestmark = pytest.mark.gpu
 
 
-def _case(wl, seed=None, d=None, fused=False):
-    print("dedup case %s T=%d H=%d E=%d P=%d K=%d %s seed=%s fused=%s" % (
-        wl.name, wl.T, wl.H, wl.E, wl.P, wl.K, wl.payload, seed, fused), flush=True)
+def _case(wl, seed=None, d=None, fused=False, geometry=None):
+    print("dedup case %s T=%d H=%d E=%d P=%d K=%d %s seed=%s fused=%s geometry=%s" % (
+        wl.name, wl.T, wl.H, wl.E, wl.P, wl.K, wl.payload, seed, fused, geometry), flush=True)
     d = generate(wl, seed=seed) if d is None else d
-    got = run_gpu_dedup(wl, d, fused=fused)
+    got = run_gpu_dedup(wl, d, fused=fused, geometry=geometry)
     ref = run_oracle_dedup(wl, d)
     ndiff = compare_dedup(wl, got, ref)
     assert ndiff == 0, "%s: %d partial/output values differ by 1 ulp" % (wl.name, ndiff)
@@ -245,3 +245,34 @@ def test_dedup_masked_entries_never_use_row0(fused):
     y[0, :] = 0x7F80                                    # bf16 +inf
     d["y"] = y
     _case(wl, d=d, fused=fused)
+
+
+# ep_dedup_layout_dispatch_geom: every workgroup size the fused dedup kernels
+# take, and dispatch geometries of the unfused path, against the oracle.
+# (shape, geometry, kernel the plan must report)
+DEDUP_GEOMETRY = {
+    "count_w8_24steps": (dict(T=64, H=12288, E=256, P=8), (8, 0, 0), "fused_count"),
+    "count_w6_24steps": (dict(T=64, H=12288, E=256, P=8), (6, 0, 0), "fused_count"),
+    "general_w4_24steps": (dict(T=64, H=12288, E=256, P=8), (4, 0, 0), "fused_general"),
+    "count_w7_14steps": (dict(T=128, H=7168, E=288, P=16), (7, 0, 0), "fused_count"),
+    "general_w8_14steps": (dict(T=128, H=7168, E=288, P=16), (8, 0, 0), "fused_general"),
+    "general_w4_14steps": (dict(T=128, H=7168, E=288, P=16), (4, 0, 0), "fused_general"),
+    "general_w8_2048": (dict(T=256, H=1536, E=64, P=8), (8, 0, 0), "fused_general"),
+    "general_w4_2048_bf16": (dict(T=256, H=1536, E=64, P=8, payload="bf16"), (4, 0, 0),
+                             "fused_general"),
+    "unfused_w1": (dict(T=640, H=1536, E=64, P=8), (1, 0, 512), "layout_then_dispatch"),
+    "unfused_w2_cap_slice1024": (dict(T=640, H=1536, E=64, P=8), (2, 256, 1024),
+                                 "layout_then_dispatch"),
+    "unfused_w8_cap64_slice1024_bf16": (dict(T=640, H=1536, E=64, P=8, payload="bf16"),
+                                        (8, 64, 1024), "layout_then_dispatch"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DEDUP_GEOMETRY))
+def test_dedup_layout_dispatch_geometry(case):
+    import combine_ep_layout_05_amd as ep
+    shape, geometry, kernel = DEDUP_GEOMETRY[case]
+    wl = WORKLOADS["ll_128x7168"].with_(name="dedup_geom_" + case, **shape)
+    plan = ep.ep_dedup_layout_dispatch_plan(wl.T, wl.H, wl.K, wl.E, wl.P, wl.payload, geometry)
+    assert plan["kernel"] == kernel and plan["waves"] == geometry[0], plan
+    _case(wl, 60 + len(case), fused=True, geometry=geometry)
