@@ -325,13 +325,24 @@ def recorded_traffic(phase, workload):
 
 
 def cpu_model():
+    """The host CPU's model name with its family / model / stepping numbers
+    (a virtualised host may report a bare brand name)."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.lower().startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" not in line:
+                if info:
+                    break                    # the first processor's block is enough
+                continue
+            k, v = (t.strip() for t in line.split(":", 1))
+            info.setdefault(k.lower(), v)
     except OSError:
         pass
-    return platform.processor() or "unknown"
+    name = info.get("model name") or platform.processor() or "unknown"
+    ids = [("family", info.get("cpu family")), ("model", info.get("model")),
+           ("stepping", info.get("stepping"))]
+    ids = ", ".join("%s %s" % (k, v) for k, v in ids if v)
+    return "%s (%s)" % (name, ids) if ids else name
 
 
 def cpu_baseline(wl, d, N, seconds):
