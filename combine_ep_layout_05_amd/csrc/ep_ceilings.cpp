@@ -21,6 +21,14 @@
 //   write_nt   the same, nontemporal
 //   copy       load + store (bytes counted: read + written)
 //   copy_nt    load + nontemporal store
+//   gather, gather_nt  the combine's access pattern at 4096 tokens x hidden
+//              7168 x top-8: one wave per (token, 512-column step) loads its
+//              16 bytes per lane from 8 rows of 14336 bytes spread over the
+//              32768 rows (a fixed odd-multiplier permutation) and stores 16
+//              bytes of the token's output row; bytes counted: 8 rows read +
+//              1 row written per token, as the combine's algorithmic bytes.
+//              Timed with 1, 2 and 4 waves per workgroup (cached or
+//              nontemporal loads; the store is nontemporal).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -189,6 +197,37 @@ void tiles_by_shape(int shape, int op, hipStream_t s, uint4* a, uint4* b, uint32
     }
 }
 
+// The combine-shaped gather (see the header): rows of kRow16 16-byte pieces,
+// kGatherK source rows per token, one wave per (token, 64-piece step).
+constexpr int kRow16 = 7168 * 2 / 16;      // 896 pieces per row
+constexpr int kGatherK = 8;
+constexpr int kGatherT = 4096;
+constexpr int kSteps = kRow16 / 64;        // 14
+constexpr uint32_t kGatherRows = (uint32_t)kGatherT * kGatherK;   // 32768, a power of two
+
+template <bool kNt>
+__global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ src,
+                                                     uint4* __restrict__ dst)
+{
+    const int lane = threadIdx.x % 64;
+    const int item = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;   // grid covers items exactly
+    const int t = item / kSteps;
+    const int step = item - t * kSteps;
+    uint4 v[kGatherK];
+#pragma unroll
+    for (int k = 0; k < kGatherK; ++k) {
+        // an odd multiplier permutes [0, 2^15): every row is read exactly once
+        const uint32_t row = ((uint32_t)(t * kGatherK + k) * 2654435761u) & (kGatherRows - 1u);
+        v[k] = ld<kNt>(src + (int64_t)row * kRow16 + step * 64 + lane);
+    }
+    uint4 acc = v[0];
+#pragma unroll
+    for (int k = 1; k < kGatherK; ++k) {
+        acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
+    }
+    st<true>(dst + (int64_t)t * kRow16 + step * 64 + lane, acc);
+}
+
 }  // namespace
 
 int main(int argc, char** argv)
@@ -208,6 +247,11 @@ int main(int argc, char** argv)
         return 2;
     }
     const size_t bytes = (size_t)n16 * 16;
+    if ((int64_t)kGatherRows * kRow16 > n16) {
+        fprintf(stderr, "ep_ceilings: the gather needs buffers of at least %lld MiB\n",
+                (long long)(((int64_t)kGatherRows * kRow16 * 16) >> 20) + 1);
+        return 2;
+    }
     uint4 *a = nullptr, *b = nullptr;
     uint32_t* sink = nullptr;
     CK(hipMalloc(&a, bytes));
@@ -301,6 +345,44 @@ int main(int argc, char** argv)
         out += per_grid + "}}";
         first = false;
         fprintf(stderr, "%s done\n", k.name);
+    }
+    // the combine-shaped gather: 1, 2 and 4 waves per workgroup
+    const int items = kGatherT * kSteps;
+    const double gather_bytes = (double)(kGatherRows + kGatherT) * kRow16 * 16;
+    for (int nt = 0; nt < 2; ++nt) {
+        double best_med = 0.0;
+        int best_w = 0;
+        std::string per_form;
+        for (int w : {1, 2, 4}) {
+            auto launch = [&]() {
+                if (nt) hipLaunchKernelGGL(gather_kernel<true>, dim3(items / w), dim3(64 * w), 0, s, a, b);
+                else hipLaunchKernelGGL(gather_kernel<false>, dim3(items / w), dim3(64 * w), 0, s, a, b);
+            };
+            launch();   // warm-up
+            CK(hipGetLastError());
+            std::vector<double> gbps;
+            for (int i = 0; i < samples; ++i) {
+                CK(hipEventRecord(e0, s));
+                for (int r = 0; r < reps; ++r) launch();
+                CK(hipEventRecord(e1, s));
+                CK(hipEventSynchronize(e1));
+                float ms = 0.0f;
+                CK(hipEventElapsedTime(&ms, e0, e1));
+                gbps.push_back(gather_bytes * reps / (ms * 1e-3) / 1e9);
+            }
+            std::sort(gbps.begin(), gbps.end());
+            const double med = gbps[gbps.size() / 2];
+            char buf[96];
+            snprintf(buf, sizeof buf, "%s\"%d waves\": %.1f", per_form.empty() ? "" : ", ", w, med);
+            per_form += buf;
+            if (med > best_med) { best_med = med; best_w = w; }
+        }
+        char buf[256];
+        snprintf(buf, sizeof buf, ", \"%s\": {\"GBps\": %.1f, \"form\": \"%d waves\", \"by_form\": {",
+                 nt ? "gather_nt" : "gather", best_med, best_w);
+        out += buf;
+        out += per_form + "}}";
+        fprintf(stderr, "%s done\n", nt ? "gather_nt" : "gather");
     }
     char tail[160];
     snprintf(tail, sizeof tail,
