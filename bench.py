@@ -235,7 +235,8 @@ class DedupPath(Path):
 
     def __init__(self, wl, seed=None):
         super().__init__(wl, seed)
-        self.db = self.ep.EpDedupBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+        self.db = self.ep.EpDedupBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload,
+                                         geometry="tuned" if GEOMETRY else None)
         self.enqueue("dedup_layout")
         self.torch.cuda.synchronize()
         self.M = int(self.db.part_token_offset[wl.P].item())
@@ -293,6 +294,7 @@ def dedup_report(wl):
     out = {"workload": wl.name, "E": wl.E, "P": wl.P, "pairs_N": p.N, "copies_M": p.M,
            "us_per_step_graph": round(us, 3),
            "step": "ep_dedup_layout_dispatch + ep_combine_partial + ep_combine_reduce",
+           "launches": {"dedup_layout_dispatch": p.db.plan()},
            "us_per_step_graph_separate_calls": round(us_sep, 3),
            "phases_us": {k: round(v, 3) for k, v in ph.items()},
            "phase_GBps": {k: round(b[k] / (ph[k] * 1e-6) / 1e9, 1)

@@ -514,9 +514,17 @@ class EpDedupBuffers:
     shape: the dedup layout, the dedup receive rows (one per present (token,
     partition) couple), the partial rows and the output."""
 
-    def __init__(self, T, H, K, E, P, payload="fp8", device="cuda"):
+    def __init__(self, T, H, K, E, P, payload="fp8", device="cuda", geometry=None):
+        """geometry: None (the library's choice), "tuned" (the saved rule of
+        the dedup_layout_dispatch phase for this shape, if any) or a
+        (waves_per_block, max_blocks[, slice_cols]) tuple, used by
+        layout_dispatch when it is given none."""
         self.T, self.H, self.K, self.E, self.P = T, H, K, E, P
         self.payload = payload
+        if geometry == "tuned":
+            from . import tuning
+            geometry = tuning.lookup("dedup_layout_dispatch", T, H, K, payload)
+        self.geometry = None if geometry is None else _geometry(geometry)
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         self.tp_row = torch.empty(T * P, **i32)
@@ -544,8 +552,10 @@ class EpDedupBuffers:
     def layout_dispatch(self, topk_idx, x, plain, stream=None, geometry=None):
         """ep_dedup_layout_dispatch: the per-expert layout into `plain` (an
         EpBuffers of the same shape), the dedup layout and dispatch here.
-        geometry: None or a (waves_per_block, max_blocks[, slice_cols]) tuple
-        (ep_dedup_layout_dispatch_geom)."""
+        geometry: None (the buffers' own, see __init__) or a (waves_per_block,
+        max_blocks[, slice_cols]) tuple (ep_dedup_layout_dispatch_geom)."""
+        if geometry is None:
+            geometry = self.geometry
         ep_dedup_layout_dispatch(topk_idx, x, self.E, self.P, self.payload, plain.expert_count,
                                  plain.expert_offset, plain.part_count, plain.part_offset,
                                  plain.row_of_pair, plain.src_pair, self.tp_row, self.part_tokens,
@@ -553,9 +563,10 @@ class EpDedupBuffers:
                                  self.ws, self.recv_x, self.recv_scales, stream, geometry)
 
     def plan(self, geometry=None):
-        """How layout_dispatch runs this shape (ep_dedup_layout_dispatch_plan)."""
+        """How layout_dispatch runs this shape (ep_dedup_layout_dispatch_plan),
+        with the buffers' own geometry unless one is given."""
         return ep_dedup_layout_dispatch_plan(self.T, self.H, self.K, self.E, self.P, self.payload,
-                                             geometry)
+                                             self.geometry if geometry is None else geometry)
 
     def dispatch(self, x, stream=None):
         """One copy of each token per partition it reaches (ep_dispatch, K = P, tp_row)."""

@@ -8,7 +8,9 @@ A geometry is (waves_per_block, max_blocks, slice_cols):
     the fused kernel's waves per workgroup, the sizes that kernel takes
     (found with ep_layout_dispatch_plan), max_blocks 0 and slice 0; for
     larger batches the dispatch kernel's geometry as above.  (0, 0, 0) is
-    the library's own choice.
+    the library's own choice;
+  - dedup_layout_dispatch: the same for ep_dedup_layout_dispatch (sizes from
+    ep_dedup_layout_dispatch_plan).
 Outputs do not depend on it; time does, and the best choice moves with token
 count and phase.  The selection rules follow what the MoRI EP tuner learned
 (MoRI PR #614 "perf(ep): InterNodeV1LL low-token latency on MI300X + CX7",
@@ -31,7 +33,7 @@ tuner paragraphs):
 
 Rules are kept in a JSON file (tuned_geometry.json beside this module by
 default), keyed by phase and exact shape; EpBuffers(..., geometry="tuned")
-uses them.  Run the sweep on the GPU with
+and EpDedupBuffers(..., geometry="tuned") use them.  Run the sweep on the GPU with
     python -m combine_ep_layout_05_amd.tuning --preset bench --write
 (`--fresh` re-tunes every shape against the library default and writes only
 the rules adopted in that run, so rules that no longer win by the margin
@@ -72,9 +74,11 @@ ROUNDS = _env_rounds()
 MARGIN = _env_margin()
 VERBOSE = (os.environ.get("EP_TUNING_VERBOSE") or "0") not in ("0", "")
 
-PHASES = ("layout_dispatch", "dispatch", "combine")
+PHASES = ("layout_dispatch", "dispatch", "combine", "dedup_layout_dispatch")
+FUSED_PHASES = ("layout_dispatch", "dedup_layout_dispatch")   # fused for small batches
 LIBRARY = (0, 0, 0)                   # the library's own choice
-DEFAULT = {"layout_dispatch": LIBRARY, "dispatch": (4, 0, 512), "combine": (4, 0, 512)}
+DEFAULT = {"layout_dispatch": LIBRARY, "dispatch": (4, 0, 512), "combine": (4, 0, 512),
+           "dedup_layout_dispatch": LIBRARY}
 WAVES = (1, 2, 4, 8)
 MAX_BLOCKS = (0, 256, 512, 1024, 2048)
 SLICES = (512, 1024)
@@ -88,21 +92,23 @@ def move_candidates():
 
 
 def candidates(phase, shape=None):
-    """Candidate geometries of a phase; layout_dispatch's depend on the shape
-    (dict with T, H, K, E, P, payload): the workgroup sizes its fused kernel
-    takes, or the dispatch kernel's geometries when the batch is not fused."""
+    """Candidate geometries of a phase; those of the fused phases depend on
+    the shape (dict with T, H, K, E, P, payload): the workgroup sizes its
+    fused kernel takes, or the dispatch kernel's geometries when the batch is
+    not fused."""
     if phase not in PHASES:
         raise ValueError("phase must be one of %s" % (PHASES,))
-    if phase != "layout_dispatch":
+    if phase not in FUSED_PHASES:
         return move_candidates()
-    from . import EpError, ep_layout_dispatch_plan
+    from . import EpError, ep_dedup_layout_dispatch_plan, ep_layout_dispatch_plan
+    plan = ep_layout_dispatch_plan if phase == "layout_dispatch" else ep_dedup_layout_dispatch_plan
     T, H, K, E, P, payload = (shape[k] for k in ("T", "H", "K", "E", "P", "payload"))
-    if ep_layout_dispatch_plan(T, H, K, E, P, payload)["kernel"] == "layout_then_dispatch":
+    if plan(T, H, K, E, P, payload)["kernel"] == "layout_then_dispatch":
         return move_candidates()
     out = []
     for w in FUSED_WAVES:
         try:
-            ep_layout_dispatch_plan(T, H, K, E, P, payload, (w, 0, 0))
+            plan(T, H, K, E, P, payload, (w, 0, 0))
         except EpError:
             continue
         out.append((w, 0, 0))
@@ -194,7 +200,8 @@ class ShapeBench:
         import torch
         from . import EpBuffers
         self.torch = torch
-        self.T, self.H, self.K, self.payload = T, H, K, payload
+        self.T, self.H, self.K, self.E, self.P, self.payload = T, H, K, E, P, payload
+        self.dbuf = None                  # per-destination buffers, made on first use
         self.launches = launches
         g = torch.Generator().manual_seed(seed)
         idx = torch.rand(T, E, generator=g).argsort(dim=1)[:, :K].to(torch.int32)
@@ -211,9 +218,14 @@ class ShapeBench:
         self.graphs = {}
 
     def _enqueue(self, phase, geometry):
-        from . import ep_combine, ep_dispatch, ep_layout_dispatch
+        from . import EpDedupBuffers, ep_combine, ep_dispatch, ep_layout_dispatch
         b = self.buf
-        if phase == "layout_dispatch":
+        if phase == "dedup_layout_dispatch":
+            if self.dbuf is None:
+                self.dbuf = EpDedupBuffers(self.T, self.H, self.K, self.E, self.P, self.payload)
+            self.dbuf.layout_dispatch(self.idx, self.x, b, self.stream,
+                                      None if tuple(geometry) == LIBRARY else geometry)
+        elif phase == "layout_dispatch":
             ep_layout_dispatch(self.idx, self.x, b.E, b.P, b.payload, b.expert_count,
                                b.expert_offset, b.part_count, b.part_offset, b.row_of_pair,
                                b.src_pair, b.status, b.ws, b.recv_x, b.recv_scales, self.stream,

@@ -86,30 +86,44 @@ def test_rules_round_trip_and_lookup(tmp_path):
     assert tu.lookup("combine", 128, 7168, 8, "fp8", path) == (8, 256, 512)
 
 
-def test_candidates_cover_every_knob_and_only_accepted_fused_sizes():
-    """dispatch / combine: every waves x cap x slice combination; layout_dispatch
-    on a fused batch: exactly the workgroup sizes the library's plan accepts
-    for that batch (checked through the host-only ep_layout_dispatch_plan)."""
+@pytest.mark.parametrize("phase", ["layout_dispatch", "dedup_layout_dispatch"])
+def test_candidates_cover_every_knob_and_only_accepted_fused_sizes(phase):
+    """dispatch / combine: every waves x cap x slice combination; the fused
+    phases on a fused batch: exactly the workgroup sizes the library's plan
+    accepts for that batch (checked through the host-only plan queries)."""
     tu = _tuning()
     import combine_ep_layout_05_amd as ep
     mc = tu.candidates("combine")
     assert len(mc) == len(set(mc)) == 4 * 5 * 2 and (4, 0, 512) in mc and (8, 2048, 1024) in mc
+    plan_of = ep.ep_layout_dispatch_plan if phase == "layout_dispatch" else \
+        ep.ep_dedup_layout_dispatch_plan
     for sh in tu.PRESETS["bench"]:
-        c = tu.candidates("layout_dispatch", sh)
-        plan = ep.ep_layout_dispatch_plan(sh["T"], sh["H"], sh["K"], sh["E"], sh["P"], sh["payload"])
+        c = tu.candidates(phase, sh)
+        plan = plan_of(sh["T"], sh["H"], sh["K"], sh["E"], sh["P"], sh["payload"])
         if plan["kernel"] == "layout_then_dispatch":
             assert c == tu.move_candidates()
             continue
         assert c and all(g[1:] == (0, 0) for g in c)
         for w in (1, 2, 3, 4, 5, 6, 7, 8, 16):
             try:
-                ep.ep_layout_dispatch_plan(sh["T"], sh["H"], sh["K"], sh["E"], sh["P"],
-                                           sh["payload"], (w, 0, 0))
+                plan_of(sh["T"], sh["H"], sh["K"], sh["E"], sh["P"], sh["payload"], (w, 0, 0))
                 ok = True
             except ep.EpError:
                 ok = False
             assert ok == ((w, 0, 0) in c), (sh["name"], w)
         assert (plan["waves"], 0, 0) in c       # the library's own choice is among them
+
+
+def test_dedup_candidates_at_the_bench_shapes():
+    """The dedup phase's fused sizes: at hidden 7168 (14 steps per token) the
+    counting kernel only takes 7 waves, the general kernel 4 or 8; at 4 tokens
+    x 6144 (12 steps, 32 entries) the counting kernel takes 6, the general
+    kernel 4 or 8."""
+    tu = _tuning()
+    ll = next(sh for sh in tu.PRESETS["bench"] if sh["name"] == "ll_128x7168")
+    assert tu.candidates("dedup_layout_dispatch", ll) == [(4, 0, 0), (7, 0, 0), (8, 0, 0)]
+    s4 = next(sh for sh in tu.PRESETS["bench"] if sh["name"] == "sweep_4x6144")
+    assert tu.candidates("dedup_layout_dispatch", s4) == [(4, 0, 0), (6, 0, 0), (8, 0, 0)]
 
 
 def test_plan_reports_the_kernel_each_batch_runs():
@@ -133,7 +147,7 @@ def test_shipped_rules_are_valid_geometries():
         phase = key.split(":")[0]
         assert phase in tu.PHASES
         g = tu.rule_geometry(r)
-        if phase == "layout_dispatch":
+        if phase in tu.FUSED_PHASES:
             f = dict(kv.split("=") for kv in key.split(":")[1:4])
             shape = next(sh for sh in tu.PRESETS["bench"]
                          if (sh["T"], sh["H"], sh["K"]) == (int(f["T"]), int(f["H"]), int(f["K"])))
