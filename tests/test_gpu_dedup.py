@@ -265,6 +265,9 @@ DEDUP_GEOMETRY = {
                                  "layout_then_dispatch"),
     "unfused_w8_cap64_slice1024_bf16": (dict(T=640, H=1536, E=64, P=8, payload="bf16"),
                                         (8, 64, 1024), "layout_then_dispatch"),
+    # the shipped rule's geometry for 16384 x 4096 bf16, on a smaller batch
+    "unfused_w1_cap1024_bf16": (dict(T=640, H=4096, E=128, P=8, payload="bf16"), (1, 1024, 512),
+                                "layout_then_dispatch"),
 }
 
 
