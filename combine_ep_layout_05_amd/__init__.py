@@ -421,6 +421,19 @@ class EpGraph:
     def launch(self, stream=None):
         _check("ep_graph_launch", _lib.ep_graph_launch(self._h, _stream(stream)))
 
+    def bind(self, stream=None):
+        """A zero-argument callable that replays the graph on `stream` (torch's
+        current stream when None, looked up now): the handle and the stream
+        are marshalled once, as a serving loop that replays one graph per
+        step would do.  Each call still checks the return code."""
+        f, h, s = _lib.ep_graph_launch, self._h, _stream(stream)
+
+        def replay():
+            rc = f(h, s)
+            if rc != 0:
+                _check("ep_graph_launch", rc)
+        return replay
+
     def destroy(self):
         if self._h:
             _check("ep_graph_destroy", _lib.ep_graph_destroy(self._h))

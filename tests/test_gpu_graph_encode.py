@@ -49,13 +49,17 @@ def test_graph_replay_matches_eager(name, fused):
             buf.dispatch(x, s)
         buf.combine(y, w, s)
         g = ep.ep_graph_end(s)
+    replay = g.bind(s)                   # the bound form: odd replays
     for rep in range(4):
         buf.recv_x.view(torch.uint8).fill_(0)
         buf.out.zero_()
         buf.row_of_pair.fill_(-5)
         junk = torch.randn(1 << 20, device="cuda").sum()     # unrelated eager work
         torch.cuda.synchronize()
-        g.launch(s)
+        if rep % 2 == 0:
+            g.launch(s)
+        else:
+            replay()
         s.synchronize()
         got = collect(buf)
         for k in ref:
