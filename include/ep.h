@@ -119,7 +119,11 @@ int ep_layout(const int32_t* topk_idx, int T, int K, int E, int P,
 
 /*
  * Dispatch: scatter each token's hidden vector into the receive rows of its
- * valid pairs.
+ * valid pairs, fp8 with its per-128-column scales travelling with the row
+ * (DeepEP PR #693 "Pipeline direct NVLink dispatch with triple-buffered
+ * prefetch", Summary: a token's hidden data, scale factors and routing are
+ * sent together; MoRI PR #614 "perf(ep): InterNodeV1LL low-token latency on
+ * MI300X + CX7" dispatches fp8 and combines bf16), or bf16 as is.
  *
  *   x            bf16 bits [T, H], 16-byte aligned.
  *   row_of_pair  int32 [T*K] from ep_layout.
@@ -189,7 +193,10 @@ int ep_layout_dispatch_noalloc(const int32_t* topk_idx, const uint16_t* x, int T
                                void* recv_x, float* recv_scales, void* stream);
 
 /*
- * Combine: out[t, c] = bf16_rne(acc), acc = 0.0f, then for k = 0..K-1 with
+ * Combine (MoRI PR #614 "perf(ep): InterNodeV1LL low-token latency on MI300X
+ * + CX7": the expert outputs are gathered back to their tokens and reduced,
+ * read in place from the receive rows -- zero-copy combine paragraph):
+ * out[t, c] = bf16_rne(acc), acc = 0.0f, then for k = 0..K-1 with
  * r = row_of_pair[t*K+k] >= 0: acc = fmaf(topk_w[t*K+k], y[r, c], acc)
  * (fp32, fixed k order; masked entries are skipped, weights used as given).
  * A token with every entry masked gives +0.  bf16 rounding is to nearest
