@@ -326,6 +326,9 @@ def recorded_traffic(phase, workload):
     readings (profiles/traffic.txt), or None when there is no reading for this
     kernel and workload or the kernel's sources changed since it was taken."""
     from combine_ep_layout_05_amd import build as B
+    # the source family each phase's kernels are built from
+    family = {"dedup_layout_dispatch": "layout_dispatch", "combine_partial": "combine",
+              "combine_reduce": "combine", "dedup_layout": "layout"}.get(phase, phase)
     path = os.path.join(ROOT, "profiles", "traffic.txt")
     if not os.path.exists(path):
         return None
@@ -335,7 +338,7 @@ def recorded_traffic(phase, workload):
         f = line.split()
         kv = dict(x.split("=", 1) for x in f[2:])
         if f[0] == phase and f[1] == workload:
-            if kv.get("source_digest") != B.source_digest(phase):
+            if kv.get("source_digest") != B.source_digest(family):
                 return None
             return int(float(kv["traffic_bytes"]))
     return None
