@@ -31,15 +31,20 @@ def test_algorithmic_bytes_of_the_five_configurations():
 
 
 def test_recorded_traffic_follows_the_source_digest(tmp_path, monkeypatch):
-    """Every committed reading resolves for the current sources; a reading
-    whose digest no longer matches, an unknown pair and a missing file give
-    None."""
+    """A committed reading is returned exactly when its digest matches the
+    current sources of its kernel family (else None, and the bench reports
+    no traffic); an unknown pair and a missing file give None."""
+    from combine_ep_layout_05_amd import build as B
+    family = {"dedup_layout_dispatch": "layout_dispatch", "combine_partial": "combine",
+              "combine_reduce": "combine", "dedup_layout": "layout"}
     path = os.path.join(ROOT, "profiles", "traffic.txt")
     lines = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
     assert len(lines) >= 13
     for f in lines:
         kv = dict(x.split("=", 1) for x in f[2:])
-        assert bench.recorded_traffic(f[0], f[1]) == int(float(kv["traffic_bytes"])), f[:2]
+        current = kv["source_digest"] == B.source_digest(family.get(f[0], f[0]))
+        want = int(float(kv["traffic_bytes"])) if current else None
+        assert bench.recorded_traffic(f[0], f[1]) == want, f[:2]
     assert bench.recorded_traffic("combine", "no_such_workload") is None
     (tmp_path / "profiles").mkdir()
     (tmp_path / "profiles" / "traffic.txt").write_text(
