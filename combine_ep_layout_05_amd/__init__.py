@@ -469,7 +469,8 @@ class EpBuffers:
         self.payload = payload
         if geometry == "tuned":
             from . import tuning
-            geometry = {ph: tuning.lookup(ph, T, H, K, payload) for ph in tuning.PHASES}
+            geometry = {ph: tuning.lookup(ph, T, H, K, payload)
+                        for ph in ("layout_dispatch", "dispatch", "combine")}
         self.geometry = {k: _geometry(v) for k, v in (geometry or {}).items() if v is not None}
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
