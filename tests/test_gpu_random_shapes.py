@@ -1,7 +1,13 @@
-"""GPU parity on seeded random shapes: T, H, E, P, K and payload drawn within
-the API's limits (both layout regimes, both dispatch launches, partial
-512-column steps), for the plain path (separate calls and the fused call) and
-the per-destination path, each against the oracle."""
+"""GPU parity on seeded random shapes: T, H, E, P, K, payload and masking drawn
+within the API's limits (every layout regime, both dispatch launches, partial
+512-column steps), for the plain path (separate calls, the fused call, and the
+fused call with a random geometry its plan accepts) and the per-destination
+path (the same three), each against the oracle.
+
+64 shapes by default; EP_RANDOM_SHAPES and EP_RANDOM_SEED draw more (or other)
+shapes, e.g. EP_RANDOM_SHAPES=3000 for a long sweep."""
+import os
+
 import numpy as np
 import pytest
 
@@ -11,39 +17,48 @@ from workloads import WORKLOADS, generate
 
 pytestmark = pytest.mark.gpu
 
+COUNT = int(os.environ.get("EP_RANDOM_SHAPES") or "64")
+SEED = int(os.environ.get("EP_RANDOM_SEED") or "2024")
 
-def _shapes(n, seed=2024):
+
+def _shapes(n, seed):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
-        K = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16]))
-        P = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        K = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 12, 16]))
+        P = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
         L = int(rng.integers(1, 65))
-        E = min(P * L, 1024 // P * P)
-        E = max(E, P)
-        if K > E:
-            K = E
+        E = max(min(P * L, 1024 // P * P), P)
+        K = min(K, E)
         payload = "bf16" if rng.random() < 0.3 else "fp8"
-        H = int(rng.integers(1, 41)) * (8 if payload == "bf16" else 128)
-        T = int(rng.choice([1, 2, 5, 17, 64, 129, 300, 700]))
-        out.append(dict(name="rand%02d" % i, T=T, H=H, E=E, P=P, K=K, payload=payload,
-                        mask_frac=float(rng.choice([0.0, 0.05]))))
+        H = int(rng.integers(1, 57)) * (8 if payload == "bf16" else 128)
+        T = int(rng.choice([1, 2, 3, 4, 7, 16, 33, 64, 100, 128, 129, 200, 256, 300, 511, 700]))
+        out.append(dict(name="rand%04d" % i, T=T, H=H, E=E, P=P, K=K, payload=payload,
+                        mask_frac=float(rng.choice([0.0, 0.05, 0.3])),
+                        pick=int(rng.integers(1 << 30)), dpick=int(rng.integers(1 << 30))))
     return out
 
 
-SHAPES = _shapes(64)
+SHAPES = _shapes(COUNT, SEED)
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[s["name"] for s in SHAPES])
 def test_random_shape_parity(shape):
-    wl = WORKLOADS["tiny_4x1024"].with_(**shape)
-    print("random shape", shape, flush=True)
-    d = generate(wl, seed=500 + int(shape["name"][4:]))
+    from combine_ep_layout_05_amd import tuning
+    sh = {k: v for k, v in shape.items() if k not in ("pick", "dpick")}
+    wl = WORKLOADS["tiny_4x1024"].with_(**sh)
+    dims = dict(T=wl.T, H=wl.H, K=wl.K, E=wl.E, P=wl.P, payload=wl.payload)
+    cands = tuning.candidates("layout_dispatch", dims)
+    geom = cands[shape["pick"] % len(cands)]
+    dcands = tuning.candidates("dedup_layout_dispatch", dims)
+    dgeom = dcands[shape["dpick"] % len(dcands)]
+    print("random shape", sh, "geometry", geom, "dedup geometry", dgeom, flush=True)
+    d = generate(wl, seed=500 + int(shape["name"][4:]) + SEED)
     ref = run_oracle(wl, d)
-    for fused in (False, True):
-        got = run_gpu(wl, d, fused=fused)
-        assert compare(wl, got, ref) == 0, (shape, fused)
+    for fused, g in ((False, None), (True, None), (True, {"layout_dispatch": geom})):
+        got = run_gpu(wl, d, fused=fused, geometry=g)
+        assert compare(wl, got, ref) == 0, (shape, fused, g)
     dref = run_oracle_dedup(wl, d)
-    for fused in (False, True):
-        got = run_gpu_dedup(wl, d, fused=fused)
-        assert compare_dedup(wl, got, dref) == 0, (shape, fused)
+    for fused, g in ((False, None), (True, None), (True, dgeom)):
+        got = run_gpu_dedup(wl, d, fused=fused, geometry=g)
+        assert compare_dedup(wl, got, dref) == 0, (shape, fused, g)
