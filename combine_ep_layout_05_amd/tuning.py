@@ -11,6 +11,15 @@ A geometry is (waves_per_block, max_blocks, slice_cols):
     the library's own choice;
   - dedup_layout_dispatch: the same for ep_dedup_layout_dispatch (sizes from
     ep_dedup_layout_dispatch_plan).
+Candidates of the calls a step is made of are timed inside that step, in
+the context they run in: a layout_dispatch or combine candidate in the plain
+step (ep_layout_dispatch, then ep_combine reading the row map it has just
+written; the other call with its saved rule, else the library's choice), a
+dedup_layout_dispatch candidate in the per-destination step (then
+ep_combine_partial and ep_combine_reduce).  Their scores are step times.
+(Timed alone, on a row map written long before, the best combine geometry at
+128 x 7168 was slower in the step than the library default.)  A dispatch
+candidate, for bare ep_dispatch calls, is timed alone.
 Outputs do not depend on it; time does, and the best choice moves with token
 count and phase.  The selection rules follow what the MoRI EP tuner learned
 (MoRI PR #614 "perf(ep): InterNodeV1LL low-token latency on MI300X + CX7",
@@ -35,9 +44,9 @@ Rules are kept in a JSON file (tuned_geometry.json beside this module by
 default), keyed by phase and exact shape; EpBuffers(..., geometry="tuned")
 and EpDedupBuffers(..., geometry="tuned") use them.  Run the sweep on the GPU with
     python -m combine_ep_layout_05_amd.tuning --preset bench --write
-(`--fresh` re-tunes every shape against the library default and writes only
-the rules adopted in that run, so rules that no longer win by the margin
-are dropped).
+(`--fresh` re-tunes every shape of the given phases against the library
+default and replaces those phases' rules by the ones adopted in that run, so
+rules that no longer win by the margin are dropped).
 """
 from __future__ import annotations
 
@@ -220,21 +229,28 @@ class ShapeBench:
     def _enqueue(self, phase, geometry):
         from . import EpDedupBuffers, ep_combine, ep_dispatch, ep_layout_dispatch
         b = self.buf
-        if phase == "dedup_layout_dispatch":
-            if self.dbuf is None:
-                self.dbuf = EpDedupBuffers(self.T, self.H, self.K, self.E, self.P, self.payload)
-            self.dbuf.layout_dispatch(self.idx, self.x, b, self.stream,
-                                      None if tuple(geometry) == LIBRARY else geometry)
-        elif phase == "layout_dispatch":
+        saved = lambda ph: lookup(ph, self.T, self.H, self.K, self.payload)
+        if phase in ("layout_dispatch", "combine"):
+            # the plain step: layout+dispatch writes the row map the combine reads
+            ld = geometry if phase == "layout_dispatch" else saved("layout_dispatch")
             ep_layout_dispatch(self.idx, self.x, b.E, b.P, b.payload, b.expert_count,
                                b.expert_offset, b.part_count, b.part_offset, b.row_of_pair,
                                b.src_pair, b.status, b.ws, b.recv_x, b.recv_scales, self.stream,
+                               None if ld is None or tuple(ld) == LIBRARY else ld)
+            cb = geometry if phase == "combine" else saved("combine")
+            ep_combine(self.y, b.row_of_pair, self.w, b.out, self.stream, cb)
+        elif phase == "dedup_layout_dispatch":
+            # the per-destination step
+            if self.dbuf is None:
+                self.dbuf = EpDedupBuffers(self.T, self.H, self.K, self.E, self.P, self.payload)
+            db = self.dbuf
+            db.layout_dispatch(self.idx, self.x, b, self.stream,
                                None if tuple(geometry) == LIBRARY else geometry)
-        elif phase == "dispatch":
+            db.combine_partial(self.y, b.row_of_pair, self.w, self.stream)
+            db.combine_reduce(self.stream)
+        else:
             ep_dispatch(self.x, self.K, b.row_of_pair, b.payload, b.recv_x, b.recv_scales,
                         self.stream, geometry)
-        else:
-            ep_combine(self.y, b.row_of_pair, self.w, b.out, self.stream, geometry)
 
     def graph(self, phase, geometry):
         from . import ep_graph_begin, ep_graph_end
@@ -338,8 +354,9 @@ def main(argv=None):
     ap.add_argument("--rules", default=None, help="rules file (default: the package's)")
     ap.add_argument("--write", action="store_true", help="save adopted rules")
     ap.add_argument("--fresh", action="store_true",
-                    help="tune against the library default and write only this run's adopted "
-                         "rules (rules that no longer win by the margin are dropped)")
+                    help="tune the given phases against the library default and replace their "
+                         "saved rules by this run's adopted ones (rules that no longer win by "
+                         "the margin are dropped); other phases' rules are kept")
     args = ap.parse_args(argv)
     rules = load_rules(args.rules)
     phases = [p for p in args.phases.split(",") if p]
@@ -349,7 +366,9 @@ def main(argv=None):
     print("rounds %d (round 0 dropped), margin %g, %s" % (
         ROUNDS, MARGIN, "fresh: incumbent = library default" if args.fresh else
         "incumbent = saved rule, else library default"), flush=True)
-    new_rules = {} if args.fresh else dict(rules)
+    # --fresh: drop the saved rules of the phases being tuned, keep the others
+    new_rules = {k: v for k, v in rules.items()
+                 if not (args.fresh and k.split(":")[0] in phases)}
     for shape in PRESETS[args.preset]:
         for phase in phases:
             rule, rep = tune(phase, shape, rules, fresh=args.fresh)
