@@ -647,6 +647,15 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Workgroup size of the dedup counting kernel: 8 waves, every id loaded in two
+// (four) rounds, measured faster than 16 waves in one (two) and than 4 waves
+// (graphs of 50 launches on MI355X, top-8, hidden 7168: 128 tokens with 16
+// partitions 3.24 -> 3.14 us, with E = 32, P = 8 3.10 -> 2.98 us; 4 to 256
+// tokens 1-3 % faster; 4 waves 4-16 % slower): its two barriers wait on half as
+// many waves.
+constexpr int kDedupCountThreads = 512;
+
+// ---------------------------------------------------------------------------
 // Dedup layout by counting, for T*K <= kSmallMaxPairs entries with K and P
 // powers of two.  Couple (t, p) is present when token t has a valid expert in
 // partition p; its row is the partition's offset plus the number of earlier
@@ -667,12 +676,12 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
 // token, its P couples' writes strided by P) took 6-8 us at 128 x top-8 / 16
 // partitions on one CU's memory pipeline.
 template <int kIds, int kMaxK>
-__global__ __launch_bounds__(kLayoutThreads) void dedup_layout_count_kernel(
+__global__ __launch_bounds__(kDedupCountThreads) void dedup_layout_count_kernel(
     const int32_t* __restrict__ idx, int T, int K, int E, int P, int32_t* __restrict__ tp_row,
     int32_t* __restrict__ part_tokens, int32_t* __restrict__ part_token_offset,
     int32_t* __restrict__ tp_src, uint32_t* __restrict__ kmask, uint32_t* __restrict__ status)
 {
-    static_assert(kIds * kLayoutThreads <= kSmallMaxPairs, "the launcher's bound");
+    static_assert(kIds * kDedupCountThreads <= kSmallMaxPairs, "the launcher's bound");
     __shared__ int32_t cnt[2][kMaxTopK];        // tokens present per partition: all, before t_lo
     __shared__ uint32_t sbad;
     const int tid = threadIdx.x;
@@ -688,7 +697,7 @@ __global__ __launch_bounds__(kLayoutThreads) void dedup_layout_count_kernel(
     int id[kIds];                                           // loads first, addresses clamped
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
-        const int p = j * kLayoutThreads + tid;
+        const int p = j * kDedupCountThreads + tid;
         id[j] = idx[p < n ? p : n - 1];
     }
     // wave 0 of a couple workgroup: couple (t_lo + u, pc) on lane u * P + pc;
@@ -709,7 +718,7 @@ __global__ __launch_bounds__(kLayoutThreads) void dedup_layout_count_kernel(
     bool bad = false;
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
-        const int p = j * kLayoutThreads + tid;
+        const int p = j * kDedupCountThreads + tid;
         const int e = p < n ? id[j] : -1;
         bad |= e >= E;
         const bool valid = e >= 0 && e < E;
@@ -736,7 +745,7 @@ __global__ __launch_bounds__(kLayoutThreads) void dedup_layout_count_kernel(
             part_token_offset[P] = M;
             *status = sbad ? 1u : 0u;
         }
-        for (int r = M + tid; r < T * P; r += kLayoutThreads) tp_src[r] = -1;
+        for (int r = M + tid; r < T * P; r += kDedupCountThreads) tp_src[r] = -1;
         return;
     }
     if (tid >= kWave) return;                               // wave 0 takes the couples
@@ -853,10 +862,12 @@ hipError_t launch_dedup_layout(const int32_t* idx, int T, int K, int E, int P, i
     const bool pow2 = (K & (K - 1)) == 0 && (P & (P - 1)) == 0;
     if (T >= 1 && pow2 && (int64_t)T * K <= kSmallMaxPairs) {
         const unsigned blocks = (unsigned)((T + kWave / P - 1) / (kWave / P)) + 1;
-        const bool one = (int64_t)T * K <= kLayoutThreads;
-        hipLaunchKernelGGL(K <= 8 ? (one ? dedup_layout_count_kernel<1, 8> : dedup_layout_count_kernel<2, 8>)
-                                  : (one ? dedup_layout_count_kernel<1, 16> : dedup_layout_count_kernel<2, 16>),
-                           dim3(blocks), dim3(kLayoutThreads), 0, stream, idx, T, K, E, P, tp_row,
+        // ids per thread: 2 up to 1024 entries, 4 up to kSmallMaxPairs
+        constexpr int kR = kSmallMaxPairs / kDedupCountThreads;
+        const bool half = (int64_t)T * K <= kSmallMaxPairs / 2;
+        hipLaunchKernelGGL(K <= 8 ? (half ? dedup_layout_count_kernel<kR / 2, 8> : dedup_layout_count_kernel<kR, 8>)
+                                  : (half ? dedup_layout_count_kernel<kR / 2, 16> : dedup_layout_count_kernel<kR, 16>),
+                           dim3(blocks), dim3(kDedupCountThreads), 0, stream, idx, T, K, E, P, tp_row,
                            part_tokens, part_token_offset, tp_src, kmask, status);
         return hipGetLastError();
     }
