@@ -305,8 +305,9 @@ int ep_combine_partial(const uint16_t* expert_out, const int32_t* row_of_pair,
  * Combine level 2, at the token's home: out[t, c] = bf16_rne(acc), acc = 0.0f,
  * then for p = 0..P-1 in order with r = tp_row[t*P+p] >= 0:
  * acc = acc + partial[r, c] (fp32).  A token with no present couple gives +0.
- *   partial bf16 [T*P, H] from ep_combine_partial; tp_row int32 [T*P];
- *   out bf16 [T, H]; 16-B aligned rows.
+ *   partial bf16 [T*P, H] from ep_combine_partial, all T*P rows readable
+ *               (row 0 is read, unused, in place of absent couples);
+ *   tp_row int32 [T*P]; out bf16 [T, H]; 16-B aligned rows.
  * Errors: EP_EINVAL for T < 0, P outside 1..16, T*P >= 2^31, H <= 0 or
  * H % 8 != 0, NULL or misaligned pointers when T > 0.
  */

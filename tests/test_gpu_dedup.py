@@ -42,6 +42,18 @@ def test_dedup_few_partitions_many_shared():
     assert np.count_nonzero([bin(int(v)).count("1") > 1 for v in km]) > wl.T
 
 
+def test_dedup_reduce_both_copy_regimes():
+    """ep_combine_reduce compacts the present copies of a token with at most 8
+    of them and loops over the partitions above that: top-16 over 16
+    partitions of 4 experts, 30 % of entries masked, gives tokens of both
+    kinds (6 to 12 copies) in one launch."""
+    wl = WORKLOADS["ll_128x7168"].with_(name="dedup_k16_p16_copies", T=96, H=1536, K=16, E=64,
+                                        P=16, mask_frac=0.3)
+    got, ref, _ = _case(wl, 33)
+    copies = (np.asarray(ref["tp_row"]).reshape(wl.T, wl.P) >= 0).sum(axis=1)
+    assert (copies > 8).any() and (copies <= 8).any()
+
+
 DEDUP_EDGE = {
     "T1": dict(T=1),
     "P1": dict(P=1, E=32),
