@@ -11,6 +11,12 @@ A geometry is (waves_per_block, max_blocks, slice_cols):
     the library's own choice;
   - dedup_layout_dispatch: the same for ep_dedup_layout_dispatch (sizes from
     ep_dedup_layout_dispatch_plan).
+The inputs are those of the bench's synthetic workload of each shape (its
+routing, masked entries and outlier rows; a preset entry names it), when the
+repository's `workloads` package is importable, else uniform routing with
+nothing masked: the best geometry moves with the input, e.g. at 16384 x 4096
+bf16 one capped-grid dispatch won by 2.8 % on unmasked inputs and lost by 2 %
+with the workload's 10 % of entries masked.
 Candidates of the calls a step is made of are timed inside that step, in
 the context they run in: a layout_dispatch or combine candidate in the plain
 step (ep_layout_dispatch, then ep_combine reading the row map it has just
@@ -199,27 +205,56 @@ def lookup(phase, T, H, K, payload, path=None):
 SPIN_CYCLES = 200000                  # GPU spin ahead of a timed graph (about 80 us)
 
 
+def workload_inputs(name, T, H, K, E, P, payload):
+    """The seeded inputs of the named synthetic workload (the repository's
+    `workloads` package, beside this one), or None when no name is given or
+    that package is not importable.  The workload must have this shape."""
+    if not name:
+        return None
+    try:
+        from workloads import WORKLOADS, generate
+    except ImportError:
+        return None
+    wl = WORKLOADS[name]
+    if (wl.T, wl.H, wl.K, wl.E, wl.P, wl.payload) != (T, H, K, E, P, payload):
+        raise ValueError("workload %s is not the shape T=%d H=%d K=%d E=%d P=%d %s"
+                         % (name, T, H, K, E, P, payload))
+    return generate(wl)
+
+
 class ShapeBench:
     """Seeded synthetic inputs and persistent buffers for one shape; times
     one phase under a given geometry from HIP graphs of back-to-back
     launches (device time per launch: a GPU spin ahead of the first event
     keeps the host's graph-launch time out of the timed region)."""
 
-    def __init__(self, T, H, K, E, P, payload="fp8", seed=0, launches=20):
+    def __init__(self, T, H, K, E, P, payload="fp8", seed=0, launches=20, workload=None):
         import torch
         from . import EpBuffers
         self.torch = torch
         self.T, self.H, self.K, self.E, self.P, self.payload = T, H, K, E, P, payload
         self.dbuf = None                  # per-destination buffers, made on first use
         self.launches = launches
-        g = torch.Generator().manual_seed(seed)
-        idx = torch.rand(T, E, generator=g).argsort(dim=1)[:, :K].to(torch.int32)
-        w = torch.softmax(torch.randn(T, K, generator=g), dim=1)
         dev = "cuda"
-        self.idx = idx.contiguous().to(dev)
-        self.w = w.contiguous().to(dev)
-        self.x = torch.randn(T, H, generator=g).to(torch.bfloat16).to(dev)
-        self.y = torch.randn(T * K, H, generator=g).to(torch.bfloat16).to(dev)
+        d = workload_inputs(workload, T, H, K, E, P, payload)
+        if d is not None:
+            # the named workload's own inputs: its routing, masked entries and
+            # outlier rows, as the bench times them
+            import numpy as np
+
+            def up(a, bf16=False):
+                t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if bf16 else a))
+                return (t.view(torch.bfloat16) if bf16 else t).to(dev)
+            self.idx, self.w = up(d["idx"]), up(d["w"])
+            self.x, self.y = up(d["x"], True), up(d["y"], True)
+        else:
+            g = torch.Generator().manual_seed(seed)
+            idx = torch.rand(T, E, generator=g).argsort(dim=1)[:, :K].to(torch.int32)
+            w = torch.softmax(torch.randn(T, K, generator=g), dim=1)
+            self.idx = idx.contiguous().to(dev)
+            self.w = w.contiguous().to(dev)
+            self.x = torch.randn(T, H, generator=g).to(torch.bfloat16).to(dev)
+            self.y = torch.randn(T * K, H, generator=g).to(torch.bfloat16).to(dev)
         self.buf = EpBuffers(T, H, K, E, P, payload=payload)
         self.stream = torch.cuda.Stream()
         self.buf.layout(self.idx, self.stream)
@@ -303,7 +338,8 @@ def tune(phase, shape, rules, rounds=None, margin=None, fresh=False, log=print):
     key = rule_key(phase, T, H, K, payload)
     saved = None if fresh else rules.get(key)
     incumbent = DEFAULT[phase] if saved is None else rule_geometry(saved)
-    sb = ShapeBench(T, H, K, E, P, payload, seed=shape.get("seed", 0))
+    sb = ShapeBench(T, H, K, E, P, payload, seed=shape.get("seed", 0),
+                    workload=shape.get("workload"))
     try:
         cands = candidates(phase, shape)
         if incumbent not in cands:
@@ -337,12 +373,18 @@ def tune(phase, shape, rules, rounds=None, margin=None, fresh=False, log=print):
 
 PRESETS = {
     "bench": [
-        dict(name="ll_128x7168", T=128, H=7168, K=8, E=288, P=16, payload="fp8"),
-        dict(name="sweep_4x6144", T=4, H=6144, K=8, E=256, P=16, payload="fp8"),
-        dict(name="sweep_8x6144", T=8, H=6144, K=8, E=256, P=16, payload="fp8"),
-        dict(name="sweep_16x6144", T=16, H=6144, K=8, E=256, P=16, payload="fp8"),
-        dict(name="bw_4096x7168", T=4096, H=7168, K=8, E=256, P=8, payload="fp8"),
-        dict(name="masked_16384x4096_bf16", T=16384, H=4096, K=8, E=128, P=8, payload="bf16"),
+        dict(name="ll_128x7168", T=128, H=7168, K=8, E=288, P=16, payload="fp8",
+             workload="ll_128x7168"),
+        dict(name="sweep_4x6144", T=4, H=6144, K=8, E=256, P=16, payload="fp8",
+             workload="sweep_4x6144"),
+        dict(name="sweep_8x6144", T=8, H=6144, K=8, E=256, P=16, payload="fp8",
+             workload="sweep_8x6144"),
+        dict(name="sweep_16x6144", T=16, H=6144, K=8, E=256, P=16, payload="fp8",
+             workload="sweep_16x6144"),
+        dict(name="bw_4096x7168", T=4096, H=7168, K=8, E=256, P=8, payload="fp8",
+             workload="bw_4096x7168_zipf"),
+        dict(name="masked_16384x4096_bf16", T=16384, H=4096, K=8, E=128, P=8, payload="bf16",
+             workload="masked_16384x4096_bf16"),
     ],
 }
 

@@ -172,3 +172,25 @@ def test_env_knobs_validated_at_import():
     assert r.returncode == 0 and r.stdout.split() == ["10", "0.0"]
     r = _import_with({"EP_TUNING_MARGIN": "1.5"})
     assert r.returncode != 0 and "[0, 1)" in r.stderr
+
+
+def test_presets_time_the_bench_workloads():
+    """Every preset shape names the bench workload whose inputs it is timed
+    on, with that workload's exact shape."""
+    from workloads import WORKLOADS
+    tu = _tuning()
+    for sh in tu.PRESETS["bench"]:
+        wl = WORKLOADS[sh["workload"]]
+        assert (wl.T, wl.H, wl.K, wl.E, wl.P, wl.payload) == \
+            (sh["T"], sh["H"], sh["K"], sh["E"], sh["P"], sh["payload"]), sh["name"]
+
+
+def test_workload_inputs():
+    import numpy as np
+    tu = _tuning()
+    assert tu.workload_inputs(None, 4, 1024, 8, 32, 8, "fp8") is None
+    d = tu.workload_inputs("tiny_4x1024", 4, 1024, 8, 32, 8, "fp8")
+    assert d["idx"].shape == (4, 8) and d["x"].shape == (4, 1024) and d["y"].shape == (32, 1024)
+    assert d["idx"].dtype == np.int32 and d["x"].dtype == np.uint16
+    with pytest.raises(ValueError):
+        tu.workload_inputs("tiny_4x1024", 4, 1024, 8, 64, 8, "fp8")
