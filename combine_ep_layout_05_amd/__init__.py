@@ -53,6 +53,7 @@ _SIGS = {
     "ep_e4m3fn_encode": ([_P, _I64, _P, _P], _I),
     "ep_dispatch_geom": ([_P, _I, _I, _I, _P, _I, _P, _P, _I, _I, _I, _P], _I),
     "ep_combine_geom": ([_P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _P], _I),
+    "ep_combine_plan": ([_I, _I, _I, _I, _I, _I, _P], _I),
     "ep_dedup_layout_workspace_bytes": ([_I, _I, _I, _I], _SZ),
     "ep_dedup_layout": ([_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "ep_combine_partial": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
@@ -260,6 +261,18 @@ def ep_layout_dispatch_plan(T, H, K, E, P, payload, geometry=None):
     """How ep_layout_dispatch(_geom) would run this batch (host only):
     {"kernel": ..., "waves": ..., "blocks" or "max_blocks": ..., "slice_cols": ...}."""
     return _plan("ep_layout_dispatch_plan", T, H, K, E, P, payload, geometry)
+
+
+def ep_combine_plan(T, H, K, geometry=None):
+    """The geometry ep_combine (geometry None) or ep_combine_geom would launch
+    a combine of T tokens x top-k K at hidden size H with (host only):
+    {"waves": ..., "max_blocks": ..., "slice_cols": ..., "streaming": bool}."""
+    plan = (ctypes.c_int32 * 4)()
+    wv, mb, sc = _geometry(geometry) if geometry is not None else (0, 0, 0)
+    _check("ep_combine_plan", _lib.ep_combine_plan(T, H, K, wv, mb, sc,
+                                                   ctypes.cast(plan, ctypes.c_void_p)))
+    return {"waves": int(plan[0]), "max_blocks": int(plan[1]), "slice_cols": int(plan[2]),
+            "streaming": bool(plan[3])}
 
 
 def ep_layout_dispatch_noalloc(topk_idx, x, E, P, payload, expert_count, expert_offset,
@@ -507,10 +520,12 @@ class EpBuffers:
         d = {"layout_dispatch": ep_layout_dispatch_plan(self.T, self.H, self.K, self.E, self.P,
                                                         self.payload,
                                                         self.geometry.get("layout_dispatch"))}
-        for ph in ("dispatch", "combine"):
-            g = self.geometry.get(ph)
-            d[ph] = "library default (4 waves, uncapped, 512 columns)" if g is None else \
-                {"waves": g[0], "max_blocks": g[1], "slice_cols": g[2] or 512}
+        g = self.geometry.get("dispatch")
+        d["dispatch"] = "library default (4 waves, uncapped, 512 columns)" if g is None else \
+            {"waves": g[0], "max_blocks": g[1], "slice_cols": g[2] or 512}
+        g = self.geometry.get("combine")
+        c = ep_combine_plan(self.T, self.H, self.K, g)
+        d["combine"] = dict(c, source="library default" if g is None else "given")
         return d
 
     def dispatch(self, x, stream=None):

@@ -342,9 +342,29 @@ int ep_combine(const uint16_t* expert_out, const int32_t* row_of_pair, const flo
     if (T == 0) return EP_OK;
     if (!ptr_ok(expert_out, 16) || !ptr_ok(row_of_pair, 4) || !ptr_ok(topk_w, 4) || !ptr_ok(out, 16))
         return EP_EINVAL;
-    if (!ep::combine_launch_ok(T, H, ep::kDefaultGeometry)) return EP_EINVAL;
+    const ep::MoveGeometry g = ep::combine_default_geometry(T, H, K);
+    if (!ep::combine_launch_ok(T, H, g)) return EP_EINVAL;
     return from_hip(ep::launch_combine(expert_out, row_of_pair, topk_w, T, H, K, out,
-                                       (hipStream_t)stream));
+                                       (hipStream_t)stream, g));
+}
+
+int ep_combine_plan(int T, int H, int K, int waves_per_block, int max_blocks, int slice_cols,
+                    int32_t* plan)
+{
+    if (plan == nullptr) return EP_EINVAL;
+    if (!routing_ok(T, K) || H <= 0 || H % ep::kColsPerLane != 0) return EP_EINVAL;
+    ep::MoveGeometry g = ep::combine_default_geometry(T, H, K);
+    if (waves_per_block != 0) {
+        if (!move_geometry(waves_per_block, max_blocks, slice_cols, &g)) return EP_EINVAL;
+    } else if (max_blocks != 0 || slice_cols != 0) {
+        return EP_EINVAL;
+    }
+    if (T > 0 && !ep::combine_launch_ok(T, H, g)) return EP_EINVAL;
+    plan[0] = g.waves;
+    plan[1] = g.max_blocks;
+    plan[2] = g.slice_steps * ep::kStepCols;
+    plan[3] = ep::combine_streaming(T, H, K) ? 1 : 0;
+    return EP_OK;
 }
 
 size_t ep_dedup_layout_workspace_bytes(int T, int K, int E, int P)

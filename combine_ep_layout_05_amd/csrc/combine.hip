@@ -427,6 +427,23 @@ bool combine_streams(int64_t gathered_rows, int H)
 
 }  // namespace
 
+bool combine_streaming(int T, int H, int K)
+{
+    return combine_streams((int64_t)T * K, H);
+}
+
+// The streaming regime's combine in 2-wave workgroups, the cached one in
+// kDefaultGeometry's 4: measured on MI355X with the step's own inputs
+// (graphs of 20 steps, interleaved), 4096 x 7168 top-8 Zipf routing: step
+// 146.0 -> 143.4 us (combine alone 90.8 -> 88.2 us), 16384 x 4096 bf16 with
+// 10 % of entries masked: step 381.9 -> 373.7 us (189.5 -> 182.9 us); 1 and 8
+// waves in between, 4 the slowest of the four in both.  At 4 to 128 tokens
+// no geometry beat 4 waves by 2 % in the step.
+MoveGeometry combine_default_geometry(int T, int H, int K)
+{
+    return combine_streaming(T, H, K) ? MoveGeometry{2, 0, 1} : kDefaultGeometry;
+}
+
 bool combine_launch_ok(int n_units, int H, MoveGeometry g)
 {
     if (g.waves < 1 || g.waves > kMaxMoveWaves || g.max_blocks < 0) return false;

@@ -52,6 +52,13 @@ hipError_t launch_layout_dispatch(const int32_t* topk_idx, const uint16_t* x, in
                                   uint32_t* status, void* recv_x, float* recv_scales,
                                   hipStream_t stream, int waves = 0);
 
+// Whether the combine of T tokens x top-k K at hidden size H streams (its
+// gathered rows reach kStreamMinBytes: nontemporal accesses, launch-order
+// blocks), and the geometry ep_combine launches it with: 2 waves per
+// workgroup when it streams, else kDefaultGeometry; uncapped, 512 columns.
+bool combine_streaming(int T, int H, int K);
+MoveGeometry combine_default_geometry(int T, int H, int K);
+
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of_pair,
                           const float* topk_w, int T, int H, int K,
                           uint16_t* out, hipStream_t stream,

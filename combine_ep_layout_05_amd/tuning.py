@@ -92,7 +92,9 @@ VERBOSE = (os.environ.get("EP_TUNING_VERBOSE") or "0") not in ("0", "")
 PHASES = ("layout_dispatch", "dispatch", "combine", "dedup_layout_dispatch")
 FUSED_PHASES = ("layout_dispatch", "dedup_layout_dispatch")   # fused for small batches
 LIBRARY = (0, 0, 0)                   # the library's own choice
-DEFAULT = {"layout_dispatch": LIBRARY, "dispatch": (4, 0, 512), "combine": (4, 0, 512),
+# the incumbent of a fresh sweep: the library's own choice (the combine's
+# depends on the batch: 2 waves per workgroup when it streams, else 4)
+DEFAULT = {"layout_dispatch": LIBRARY, "dispatch": (4, 0, 512), "combine": LIBRARY,
            "dedup_layout_dispatch": LIBRARY}
 WAVES = (1, 2, 4, 8)
 MAX_BLOCKS = (0, 256, 512, 1024, 2048)
@@ -273,7 +275,8 @@ class ShapeBench:
                                b.src_pair, b.status, b.ws, b.recv_x, b.recv_scales, self.stream,
                                None if ld is None or tuple(ld) == LIBRARY else ld)
             cb = geometry if phase == "combine" else saved("combine")
-            ep_combine(self.y, b.row_of_pair, self.w, b.out, self.stream, cb)
+            ep_combine(self.y, b.row_of_pair, self.w, b.out, self.stream,
+                       None if cb is None or tuple(cb) == LIBRARY else cb)
         elif phase == "dedup_layout_dispatch":
             # the per-destination step
             if self.dbuf is None:

@@ -343,6 +343,25 @@ int ep_combine_geom(const uint16_t* expert_out, const int32_t* row_of_pair, cons
                     int slice_cols, void* stream);
 
 /*
+ * Host-only: the geometry an ep_combine of T tokens x top-k K at hidden size
+ * H runs with, written to plan[4]:
+ *   plan[0]  waves per workgroup, plan[1] max_blocks, plan[2] columns per
+ *            work item, as ep_combine_geom takes them;
+ *   plan[3]  1 when the combine streams (the gathered rows T*K*H*2 bytes
+ *            reach 64 MiB: nontemporal loads and stores), else 0.
+ * With waves_per_block = 0 (then max_blocks and slice_cols 0 too) it is
+ * ep_combine's own choice: 2 waves per workgroup when the combine streams,
+ * 4 otherwise, uncapped, 512 columns (the geometry found fastest by
+ * measurement, as the sources pick theirs: MoRI PR #614 "perf(ep):
+ * InterNodeV1LL low-token latency on MI300X + CX7", tuner paragraphs);
+ * otherwise the geometry given, as ep_combine_geom would launch it.
+ * Returns EP_EINVAL (plan untouched) for arguments or a geometry
+ * ep_combine / ep_combine_geom would reject.  Nothing touches the GPU.
+ */
+int ep_combine_plan(int T, int H, int K, int waves_per_block, int max_blocks, int slice_cols,
+                    int32_t* plan);
+
+/*
  * ep_layout_dispatch with an explicit launch geometry (0 = the library's
  * choice for each of the three values).  Same results, bit for bit, as
  * ep_layout_dispatch.

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
               "ep_combine_reduce", "ep_dedup_layout_dispatch",
               "ep_dedup_layout_dispatch_workspace_bytes", "ep_dispatch_geom", "ep_combine_geom",
               "ep_layout_dispatch_geom", "ep_layout_dispatch_plan", "ep_layout_dispatch_noalloc",
-              "ep_dedup_layout_dispatch_geom", "ep_dedup_layout_dispatch_plan"):
+              "ep_dedup_layout_dispatch_geom", "ep_dedup_layout_dispatch_plan",
+              "ep_combine_plan"):
         assert n in names, n
 
 
@@ -171,6 +172,38 @@ def test_layout_dispatch_geom_host_side_validation(lib):
     assert list(plan) == [3, 2, 256, 1024]
     assert L.ep_layout_dispatch_plan(4, 6144, 8, 256, 16, 7, 0, 0, 0, pp) == -2
     assert L.ep_layout_dispatch_plan(4, 6144, 8, 256, 16, 0, 0, 0, 0, None) == -1
+
+
+def test_combine_plan(lib):
+    """ep_combine's own geometry: 4 waves per workgroup while the combine's
+    gathered rows stay below 64 MiB (cached), 2 waves once they stream; a
+    given geometry is reported as ep_combine_geom would launch it, one it
+    would reject is rejected (host only, nothing launched)."""
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L = lib
+    L.ep_combine_plan.argtypes = [I] * 6 + [P]
+    plan = (ctypes.c_int32 * 4)()
+    pp = ctypes.cast(plan, P)
+    assert L.ep_combine_plan(128, 7168, 8, 0, 0, 0, pp) == 0
+    assert list(plan) == [4, 0, 512, 0]
+    assert L.ep_combine_plan(4096, 7168, 8, 0, 0, 0, pp) == 0
+    assert list(plan) == [2, 0, 512, 1]
+    assert L.ep_combine_plan(16384, 4096, 8, 0, 0, 0, pp) == 0
+    assert list(plan) == [2, 0, 512, 1]
+    # the threshold: T*K*H*2 bytes of gathered rows reaching 64 MiB
+    assert L.ep_combine_plan(4096, 1024, 8, 0, 0, 0, pp) == 0 and plan[3] == 1 and plan[0] == 2
+    assert L.ep_combine_plan(4095, 1024, 8, 0, 0, 0, pp) == 0 and plan[3] == 0 and plan[0] == 4
+    assert L.ep_combine_plan(4096, 7168, 8, 8, 256, 1024, pp) == 0
+    assert list(plan) == [8, 256, 1024, 1]
+    assert L.ep_combine_plan(0, 7168, 8, 0, 0, 0, pp) == 0
+    assert list(plan) == [4, 0, 512, 0]
+    plan[0] = 99
+    for args in [(4, 7168, 8, 3, 0, 0), (4, 7168, 8, 0, 256, 0), (4, 7168, 8, 0, 0, 1024),
+                 (4, 7168, 8, 4, 0, 768), (4, 7168, 8, 4, -1, 0), (4, 7168, 0, 0, 0, 0),
+                 (4, 7168, 17, 0, 0, 0), (4, 7164, 8, 0, 0, 0), (-1, 7168, 8, 0, 0, 0)]:
+        assert L.ep_combine_plan(*args, pp) == -1, args
+    assert plan[0] == 99                                  # untouched on error
+    assert L.ep_combine_plan(4, 7168, 8, 0, 0, 0, None) == -1
 
 
 def test_dedup_layout_dispatch_geom_host_side_validation(lib):
