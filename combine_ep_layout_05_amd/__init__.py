@@ -51,6 +51,7 @@ _SIGS = {
     "ep_graph_launch": ([_P, _P], _I),
     "ep_graph_destroy": ([_P], _I),
     "ep_e4m3fn_encode": ([_P, _I64, _P, _P], _I),
+    "ep_topk_idx_narrow": ([_P, _I64, _P, _P], _I),
     "ep_dispatch_geom": ([_P, _I, _I, _I, _P, _I, _P, _P, _I, _I, _I, _P], _I),
     "ep_combine_geom": ([_P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _P], _I),
     "ep_combine_plan": ([_I, _I, _I, _I, _I, _I, _P], _I),
@@ -319,6 +320,28 @@ def ep_combine(expert_out, row_of_pair, topk_w, out, stream=None, geometry=None)
             _stream(stream)))
 
 
+def ep_topk_idx_narrow(topk_idx64, out_i32, stream=None):
+    """int64 expert ids -> int32 ids on the GPU (negative -> -1, above
+    INT32_MAX -> INT32_MAX); out_i32 must have as many elements."""
+    _dt(topk_idx64, torch.int64)
+    _dt(out_i32, torch.int32)
+    _numel(out_i32, topk_idx64.numel(), "out_i32")
+    _check("ep_topk_idx_narrow", _lib.ep_topk_idx_narrow(_ptr(topk_idx64), topk_idx64.numel(),
+                                                         _ptr(out_i32), _stream(stream)))
+
+
+def _ids32(buf, topk_idx, stream):
+    """topk_idx as the int32 ids the layouts take: int32 as given, int64
+    narrowed into the buffers' own int32 ids (one extra launch)."""
+    if topk_idx.dtype != torch.int64:
+        return topk_idx
+    if tuple(topk_idx.shape) != (buf.T, buf.K):
+        raise ValueError("topk_idx: expected shape %s, got %s" % ((buf.T, buf.K),
+                                                                  tuple(topk_idx.shape)))
+    ep_topk_idx_narrow(topk_idx, buf.idx32, stream)
+    return buf.idx32
+
+
 def ep_e4m3fn_encode(values_f32, out_u8, stream=None):
     _dt(values_f32, torch.float32)
     _dt(out_u8, torch.uint8)
@@ -494,6 +517,7 @@ class EpBuffers:
         self.row_of_pair = torch.empty(T * K, **i32)
         self.src_pair = torch.empty(T * K, **i32)
         self.status = torch.empty(1, **i32)
+        self.idx32 = torch.empty((T, K), **i32)          # int64 ids narrowed here
         wsb = ep_layout_workspace_bytes(T, K, E)
         self.ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
         if payload == "fp8":
@@ -505,10 +529,14 @@ class EpBuffers:
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
     def layout(self, topk_idx, stream=None):
+        """topk_idx int32 [T, K], or int64 (narrowed first, one extra launch)."""
+        topk_idx = _ids32(self, topk_idx, stream)
         ep_layout(topk_idx, self.E, self.P, self.expert_count, self.expert_offset, self.part_count,
                   self.part_offset, self.row_of_pair, self.src_pair, self.status, self.ws, stream)
 
     def layout_dispatch(self, topk_idx, x, stream=None):
+        """topk_idx int32 [T, K], or int64 (narrowed first, one extra launch)."""
+        topk_idx = _ids32(self, topk_idx, stream)
         ep_layout_dispatch(topk_idx, x, self.E, self.P, self.payload, self.expert_count,
                            self.expert_offset, self.part_count, self.part_offset, self.row_of_pair,
                            self.src_pair, self.status, self.ws, self.recv_x, self.recv_scales, stream,
@@ -562,6 +590,7 @@ class EpDedupBuffers:
         self.tp_src = torch.empty(T * P, **i32)
         self.kmask = torch.empty(T * P, **i32)
         self.status = torch.empty(1, **i32)
+        self.idx32 = torch.empty((T, K), **i32)          # int64 ids narrowed here
         wsb = ep_dedup_layout_dispatch_workspace_bytes(T, K, E, P)
         self.ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
         if payload == "fp8":
@@ -574,6 +603,8 @@ class EpDedupBuffers:
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
     def layout(self, topk_idx, stream=None):
+        """topk_idx int32 [T, K], or int64 (narrowed first, one extra launch)."""
+        topk_idx = _ids32(self, topk_idx, stream)
         ep_dedup_layout(topk_idx, self.E, self.P, self.tp_row, self.part_tokens,
                         self.part_token_offset, self.tp_src, self.kmask, self.status, self.ws,
                         stream)
@@ -585,6 +616,7 @@ class EpDedupBuffers:
         max_blocks[, slice_cols]) tuple (ep_dedup_layout_dispatch_geom)."""
         if geometry is None:
             geometry = self.geometry
+        topk_idx = _ids32(self, topk_idx, stream)
         ep_dedup_layout_dispatch(topk_idx, x, self.E, self.P, self.payload, plain.expert_count,
                                  plain.expert_offset, plain.part_count, plain.part_offset,
                                  plain.row_of_pair, plain.src_pair, self.tp_row, self.part_tokens,

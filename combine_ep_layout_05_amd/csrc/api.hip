@@ -588,6 +588,14 @@ int ep_e4m3fn_encode(const float* in, int64_t n, uint8_t* out, void* stream)
     return from_hip(ep::launch_e4m3fn_encode(in, n, out, (hipStream_t)stream));
 }
 
+int ep_topk_idx_narrow(const int64_t* topk_idx64, int64_t n, int32_t* topk_idx32, void* stream)
+{
+    if (n < 0) return EP_EINVAL;
+    if (n == 0) return EP_OK;
+    if (!ptr_ok(topk_idx64, 8) || !ptr_ok(topk_idx32, 4)) return EP_EINVAL;
+    return from_hip(ep::launch_idx_narrow(topk_idx64, n, topk_idx32, (hipStream_t)stream));
+}
+
 int ep_graph_begin(void* stream)
 {
     if (stream == nullptr) return EP_EINVAL;

@@ -97,4 +97,6 @@ hipError_t launch_dedup_layout_dispatch(const int32_t* topk_idx, const uint16_t*
 hipError_t launch_e4m3fn_encode(const float* in, int64_t n, uint8_t* out,
                                 hipStream_t stream);
 
+hipError_t launch_idx_narrow(const int64_t* in, int64_t n, int32_t* out, hipStream_t stream);
+
 }  // namespace ep

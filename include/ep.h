@@ -473,6 +473,19 @@ int ep_graph_destroy(void* graph);
  */
 int ep_e4m3fn_encode(const float* in, int64_t n, uint8_t* out, void* stream);
 
+/*
+ * int64 expert ids (the index type a framework's top-k returns) to the int32
+ * ids the layout calls take, on the GPU: topk_idx32[i] = -1 for a negative
+ * topk_idx64[i] (negative ids are the sentinel for a dropped entry: MoRI PR
+ * #614 "perf(ep): InterNodeV1LL low-token latency on MI300X + CX7", routing
+ * scan paragraph), INT32_MAX for one above INT32_MAX (a bad id the layout then
+ * reports in its status), the value itself otherwise.  n entries;
+ * topk_idx64 8-B and topk_idx32 4-B aligned device pointers.  One extra
+ * launch: a router that emits int32 ids needs none.
+ * Errors: EP_EINVAL for n < 0, NULL or misaligned pointers when n > 0.
+ */
+int ep_topk_idx_narrow(const int64_t* topk_idx64, int64_t n, int32_t* topk_idx32, void* stream);
+
 /* Message for a return code; static storage. */
 const char* ep_strerror(int code);
 /* hipError_t of the last failed launch in the calling thread (0 if none). */

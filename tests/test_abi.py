@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
               "ep_dedup_layout_dispatch_workspace_bytes", "ep_dispatch_geom", "ep_combine_geom",
               "ep_layout_dispatch_geom", "ep_layout_dispatch_plan", "ep_layout_dispatch_noalloc",
               "ep_dedup_layout_dispatch_geom", "ep_dedup_layout_dispatch_plan",
-              "ep_combine_plan"):
+              "ep_combine_plan", "ep_topk_idx_narrow"):
         assert n in names, n
 
 
@@ -172,6 +172,22 @@ def test_layout_dispatch_geom_host_side_validation(lib):
     assert list(plan) == [3, 2, 256, 1024]
     assert L.ep_layout_dispatch_plan(4, 6144, 8, 256, 16, 7, 0, 0, 0, pp) == -2
     assert L.ep_layout_dispatch_plan(4, 6144, 8, 256, 16, 0, 0, 0, 0, None) == -1
+
+
+def test_topk_idx_narrow_host_validation(lib):
+    """Rejections happen on the host, before anything is enqueued (fake
+    pointers are never dereferenced: every call here returns before a
+    launch); n = 0 is a no-op whatever the pointers."""
+    P = ctypes.c_void_p
+    L = lib
+    L.ep_topk_idx_narrow.argtypes = [P, ctypes.c_int64, P, P]
+    fake = 0x10000
+    assert L.ep_topk_idx_narrow(P(fake), -1, P(fake), None) == -1
+    assert L.ep_topk_idx_narrow(None, 0, None, None) == 0
+    assert L.ep_topk_idx_narrow(None, 4, P(fake), None) == -1
+    assert L.ep_topk_idx_narrow(P(fake), 4, None, None) == -1
+    assert L.ep_topk_idx_narrow(P(fake + 4), 4, P(fake), None) == -1     # int64 input 8-B aligned
+    assert L.ep_topk_idx_narrow(P(fake), 4, P(fake + 2), None) == -1     # int32 output 4-B aligned
 
 
 def test_combine_plan(lib):
