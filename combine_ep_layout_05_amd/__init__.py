@@ -330,16 +330,27 @@ def ep_topk_idx_narrow(topk_idx64, out_i32, stream=None):
                                                          _ptr(out_i32), _stream(stream)))
 
 
+def _tokens(buf, topk_idx):
+    """The batch's token count, at most the buffers' T, from topk_idx [n, K]."""
+    if topk_idx.dim() != 2 or topk_idx.shape[1] != buf.K or topk_idx.shape[0] > buf.T:
+        raise ValueError("topk_idx: expected [n, %d] with n <= %d, got %s" % (
+            buf.K, buf.T, tuple(topk_idx.shape)))
+    return topk_idx.shape[0]
+
+
 def _ids32(buf, topk_idx, stream):
     """topk_idx as the int32 ids the layouts take: int32 as given, int64
     narrowed into the buffers' own int32 ids (one extra launch)."""
     if topk_idx.dtype != torch.int64:
         return topk_idx
-    if tuple(topk_idx.shape) != (buf.T, buf.K):
-        raise ValueError("topk_idx: expected shape %s, got %s" % ((buf.T, buf.K),
-                                                                  tuple(topk_idx.shape)))
-    ep_topk_idx_narrow(topk_idx, buf.idx32, stream)
-    return buf.idx32
+    n = _tokens(buf, topk_idx)
+    ep_topk_idx_narrow(topk_idx, buf.idx32[:n], stream)
+    return buf.idx32[:n]
+
+
+def _same_tokens(buf, n, what):
+    if n != buf.n:
+        raise ValueError("%s: %d tokens, but the last layout was of %d" % (what, n, buf.n))
 
 
 def ep_e4m3fn_encode(values_f32, out_u8, stream=None):
@@ -494,7 +505,10 @@ def ep_graph_end(stream) -> EpGraph:
 
 class EpBuffers:
     """Persistent device buffers for one shape (allocated once, reused by every
-    call, so the calls can be captured into a graph)."""
+    call, so the calls can be captured into a graph).  T is the most tokens a
+    batch may hold: a layout of n <= T tokens (topk_idx [n, K]) sets the batch
+    size the dispatch and the combine after it work on, over the first rows
+    of the same buffers (so a graph may still capture them)."""
 
     def __init__(self, T, H, K, E, P, payload="fp8", device="cuda", geometry=None):
         """geometry: None (library defaults), "tuned" (the saved rules for this
@@ -502,6 +516,7 @@ class EpBuffers:
         "layout_dispatch", "dispatch", "combine", each (waves_per_block,
         max_blocks, slice_cols) as the *_geom entry points take it."""
         self.T, self.H, self.K, self.E, self.P = T, H, K, E, P
+        self.n = T                                        # tokens of the current batch
         self.payload = payload
         if geometry == "tuned":
             from . import tuning
@@ -528,19 +543,31 @@ class EpBuffers:
             self.recv_scales = None
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
+    def _views(self, n):
+        m = n * self.K
+        return (self.row_of_pair[:m], self.src_pair[:m], self.recv_x[:m],
+                None if self.recv_scales is None else self.recv_scales[:m])
+
     def layout(self, topk_idx, stream=None):
-        """topk_idx int32 [T, K], or int64 (narrowed first, one extra launch)."""
+        """topk_idx int32 [n, K], n <= T, or int64 (narrowed first, one extra
+        launch); sets the batch to n tokens."""
+        n = _tokens(self, topk_idx)
         topk_idx = _ids32(self, topk_idx, stream)
+        rop, src, _, _ = self._views(n)
         ep_layout(topk_idx, self.E, self.P, self.expert_count, self.expert_offset, self.part_count,
-                  self.part_offset, self.row_of_pair, self.src_pair, self.status, self.ws, stream)
+                  self.part_offset, rop, src, self.status, self.ws, stream)
+        self.n = n
 
     def layout_dispatch(self, topk_idx, x, stream=None):
-        """topk_idx int32 [T, K], or int64 (narrowed first, one extra launch)."""
+        """topk_idx int32 [n, K], n <= T, or int64 (narrowed first, one extra
+        launch), x bf16 [n, H]; sets the batch to n tokens."""
+        n = _tokens(self, topk_idx)
         topk_idx = _ids32(self, topk_idx, stream)
+        rop, src, rx, rs = self._views(n)
         ep_layout_dispatch(topk_idx, x, self.E, self.P, self.payload, self.expert_count,
-                           self.expert_offset, self.part_count, self.part_offset, self.row_of_pair,
-                           self.src_pair, self.status, self.ws, self.recv_x, self.recv_scales, stream,
-                           self.geometry.get("layout_dispatch"))
+                           self.expert_offset, self.part_count, self.part_offset, rop, src,
+                           self.status, self.ws, rx, rs, stream, self.geometry.get("layout_dispatch"))
+        self.n = n
 
     def plan(self):
         """What layout_dispatch launches for this shape and geometry, and the
@@ -557,19 +584,27 @@ class EpBuffers:
         return d
 
     def dispatch(self, x, stream=None):
-        ep_dispatch(x, self.K, self.row_of_pair, self.payload, self.recv_x, self.recv_scales, stream,
-                    self.geometry.get("dispatch"))
+        """x bf16 [n, H] of the current batch (the last layout's n tokens)."""
+        _same_tokens(self, x.shape[0], "x")
+        rop, _, rx, rs = self._views(self.n)
+        ep_dispatch(x, self.K, rop, self.payload, rx, rs, stream, self.geometry.get("dispatch"))
 
     def combine(self, expert_out, topk_w, stream=None):
-        ep_combine(expert_out, self.row_of_pair, topk_w, self.out, stream,
-                   self.geometry.get("combine"))
-        return self.out
+        """expert_out bf16 [>= n*K, H], topk_w fp32 [n, K] of the current batch;
+        returns out[:n]."""
+        _same_tokens(self, topk_w.shape[0], "topk_w")
+        rop, _, _, _ = self._views(self.n)
+        out = self.out[:self.n]
+        ep_combine(expert_out, rop, topk_w, out, stream, self.geometry.get("combine"))
+        return out
 
 
 class EpDedupBuffers:
     """Persistent device buffers of the per-destination (dedup) path for one
     shape: the dedup layout, the dedup receive rows (one per present (token,
-    partition) couple), the partial rows and the output."""
+    partition) couple), the partial rows and the output.  T is the most tokens
+    a batch may hold; a layout of n <= T tokens sets the batch size, as in
+    EpBuffers."""
 
     def __init__(self, T, H, K, E, P, payload="fp8", device="cuda", geometry=None):
         """geometry: None (the library's choice), "tuned" (the saved rule of
@@ -577,6 +612,7 @@ class EpDedupBuffers:
         (waves_per_block, max_blocks[, slice_cols]) tuple, used by
         layout_dispatch when it is given none."""
         self.T, self.H, self.K, self.E, self.P = T, H, K, E, P
+        self.n = T                                        # tokens of the current batch
         self.payload = payload
         if geometry == "tuned":
             from . import tuning
@@ -602,12 +638,20 @@ class EpDedupBuffers:
         self.partial = torch.empty((T * P, H), dtype=torch.bfloat16, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
+    def _views(self, n):
+        m = n * self.P
+        return (self.tp_row[:m], self.tp_src[:m], self.kmask[:m], self.recv_x[:m],
+                None if self.recv_scales is None else self.recv_scales[:m], self.partial[:m])
+
     def layout(self, topk_idx, stream=None):
-        """topk_idx int32 [T, K], or int64 (narrowed first, one extra launch)."""
+        """topk_idx int32 [n, K], n <= T, or int64 (narrowed first, one extra
+        launch); sets the batch to n tokens."""
+        n = _tokens(self, topk_idx)
         topk_idx = _ids32(self, topk_idx, stream)
-        ep_dedup_layout(topk_idx, self.E, self.P, self.tp_row, self.part_tokens,
-                        self.part_token_offset, self.tp_src, self.kmask, self.status, self.ws,
-                        stream)
+        tpr, tps, km, _, _, _ = self._views(n)
+        ep_dedup_layout(topk_idx, self.E, self.P, tpr, self.part_tokens, self.part_token_offset,
+                        tps, km, self.status, self.ws, stream)
+        self.n = n
 
     def layout_dispatch(self, topk_idx, x, plain, stream=None, geometry=None):
         """ep_dedup_layout_dispatch: the per-expert layout into `plain` (an
@@ -616,12 +660,17 @@ class EpDedupBuffers:
         max_blocks[, slice_cols]) tuple (ep_dedup_layout_dispatch_geom)."""
         if geometry is None:
             geometry = self.geometry
+        n = _tokens(self, topk_idx)
+        if n > plain.T:
+            raise ValueError("plain buffers hold %d tokens, the batch has %d" % (plain.T, n))
         topk_idx = _ids32(self, topk_idx, stream)
+        tpr, tps, km, rx, rs, _ = self._views(n)
+        rop, src, _, _ = plain._views(n)
         ep_dedup_layout_dispatch(topk_idx, x, self.E, self.P, self.payload, plain.expert_count,
                                  plain.expert_offset, plain.part_count, plain.part_offset,
-                                 plain.row_of_pair, plain.src_pair, self.tp_row, self.part_tokens,
-                                 self.part_token_offset, self.tp_src, self.kmask, self.status,
-                                 self.ws, self.recv_x, self.recv_scales, stream, geometry)
+                                 rop, src, tpr, self.part_tokens, self.part_token_offset, tps, km,
+                                 self.status, self.ws, rx, rs, stream, geometry)
+        self.n = plain.n = n
 
     def plan(self, geometry=None):
         """How layout_dispatch runs this shape (ep_dedup_layout_dispatch_plan),
@@ -630,17 +679,28 @@ class EpDedupBuffers:
                                              self.geometry if geometry is None else geometry)
 
     def dispatch(self, x, stream=None):
-        """One copy of each token per partition it reaches (ep_dispatch, K = P, tp_row)."""
-        ep_dispatch(x, self.P, self.tp_row, self.payload, self.recv_x, self.recv_scales, stream)
+        """One copy of each token per partition it reaches (ep_dispatch, K = P,
+        tp_row); x bf16 [n, H] of the current batch."""
+        _same_tokens(self, x.shape[0], "x")
+        tpr, _, _, rx, rs, _ = self._views(self.n)
+        ep_dispatch(x, self.P, tpr, self.payload, rx, rs, stream)
 
     def combine_partial(self, expert_out, row_of_pair, topk_w, stream=None):
-        ep_combine_partial(expert_out, row_of_pair, topk_w, self.tp_row, self.kmask, self.P,
-                           self.partial, stream)
-        return self.partial
+        """topk_w fp32 [n, K] of the current batch and its row_of_pair (the
+        first n*K entries are used, e.g. the plain buffers' whole array);
+        returns partial[:n*P]."""
+        _same_tokens(self, topk_w.shape[0], "topk_w")
+        tpr, _, km, _, _, part = self._views(self.n)
+        ep_combine_partial(expert_out, row_of_pair[:self.n * self.K], topk_w, tpr, km, self.P,
+                           part, stream)
+        return part
 
     def combine_reduce(self, stream=None):
-        ep_combine_reduce(self.partial, self.tp_row, self.T, self.P, self.out, stream)
-        return self.out
+        """Returns out[:n] of the current batch."""
+        tpr, _, _, _, _, part = self._views(self.n)
+        out = self.out[:self.n]
+        ep_combine_reduce(part, tpr, self.n, self.P, out, stream)
+        return out
 
 
 class BoundStep:
