@@ -24,12 +24,15 @@ def to_dev(a, dtype=None):
     return t.cuda()
 
 
-def run_gpu(wl, d, stream=None, poison=True, fused=False, geometry=None):
+def run_gpu(wl, d, stream=None, poison=True, fused=False, geometry=None, capacity=None):
     """Layout + dispatch + combine on the GPU; returns numpy copies of every output.
     fused=True runs ep_layout_dispatch instead of ep_layout then ep_dispatch;
-    geometry is EpBuffers' launch geometry (None: the library default)."""
+    geometry is EpBuffers' launch geometry (None: the library default);
+    capacity: buffers for that many tokens (>= wl.T) holding the batch in
+    their first rows, the rest checked to stay untouched."""
     ep = gpu_lib()
-    buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload, geometry=geometry)
+    cap = wl.T if capacity is None else capacity
+    buf = ep.EpBuffers(cap, wl.H, wl.K, wl.E, wl.P, payload=wl.payload, geometry=geometry)
     if poison:
         buf.recv_x.view(torch.uint8).fill_(POISON_BYTE)
         if buf.recv_scales is not None:
@@ -48,18 +51,27 @@ def run_gpu(wl, d, stream=None, poison=True, fused=False, geometry=None):
         buf.dispatch(x, stream)
     buf.combine(y, w, stream)
     torch.cuda.synchronize()
-    return collect(buf)
+    if poison and cap > wl.T:
+        m = wl.T * wl.K
+        assert bool((buf.recv_x[m:].view(torch.uint8) == POISON_BYTE).all()), "recv_x past the batch"
+        assert bool((buf.row_of_pair[m:] == -7).all()) and bool((buf.src_pair[m:] == -7).all())
+        assert bool((buf.out[wl.T:].view(torch.int16) == 0x5A5A).all()), "out past the batch"
+    return collect(buf, wl.T)
 
 
-def collect(buf):
+def collect(buf, T=None):
+    T = buf.T if T is None else T
+    m = T * buf.K
     res = {k: getattr(buf, k).cpu().numpy() for k in
-           ("expert_count", "expert_offset", "part_count", "part_offset", "row_of_pair", "src_pair")}
+           ("expert_count", "expert_offset", "part_count", "part_offset")}
+    res["row_of_pair"] = buf.row_of_pair[:m].cpu().numpy()
+    res["src_pair"] = buf.src_pair[:m].cpu().numpy()
     res["status"] = buf.status.cpu().numpy().view(np.uint32)
-    res["recv_x"] = buf.recv_x.view(torch.uint8).cpu().numpy() if buf.payload == "fp8" else \
-        buf.recv_x.view(torch.int16).cpu().numpy().view(np.uint16)
+    res["recv_x"] = buf.recv_x[:m].view(torch.uint8).cpu().numpy() if buf.payload == "fp8" else \
+        buf.recv_x[:m].view(torch.int16).cpu().numpy().view(np.uint16)
     if buf.recv_scales is not None:
-        res["recv_scales"] = buf.recv_scales.cpu().numpy()
-    res["out"] = buf.out.view(torch.int16).cpu().numpy().view(np.uint16)
+        res["recv_scales"] = buf.recv_scales[:m].cpu().numpy()
+    res["out"] = buf.out[:T].view(torch.int16).cpu().numpy().view(np.uint16)
     return res
 
 
@@ -108,15 +120,17 @@ PLAIN_LAYOUT_KEYS = ("expert_count", "expert_offset", "part_count", "part_offset
                      "src_pair")
 
 
-def run_gpu_dedup(wl, d, stream=None, fused=False, geometry=None):
+def run_gpu_dedup(wl, d, stream=None, fused=False, geometry=None, capacity=None):
     """Per-destination path on the GPU: ep_layout (expert rows for the expert
     outputs), ep_dedup_layout, ep_dispatch with K = P over tp_row,
     ep_combine_partial and ep_combine_reduce; fused=True runs
     ep_dedup_layout_dispatch in place of the first three (with `geometry`,
-    ep_dedup_layout_dispatch_geom).  Buffers start poisoned."""
+    ep_dedup_layout_dispatch_geom).  Buffers start poisoned; capacity as in
+    run_gpu."""
     ep = gpu_lib()
-    buf = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
-    db = ep.EpDedupBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    cap = wl.T if capacity is None else capacity
+    buf = ep.EpBuffers(cap, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    db = ep.EpDedupBuffers(cap, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
     db.recv_x.view(torch.uint8).fill_(POISON_BYTE)
     if db.recv_scales is not None:
         db.recv_scales.view(torch.int32).fill_(POISON_F32_BITS)
@@ -137,17 +151,29 @@ def run_gpu_dedup(wl, d, stream=None, fused=False, geometry=None):
     db.combine_partial(y, buf.row_of_pair, w, stream)
     db.combine_reduce(stream)
     torch.cuda.synchronize()
-    res = {k: getattr(db, k).cpu().numpy() for k in DEDUP_KEYS}
+    T, mp, mk = wl.T, wl.T * wl.P, wl.T * wl.K
+    if cap > T:
+        assert bool((db.recv_x[mp:].view(torch.uint8) == POISON_BYTE).all()), "rows past the batch"
+        for t in (db.tp_row[mp:], db.tp_src[mp:], db.kmask[mp:], buf.row_of_pair[mk:],
+                  buf.src_pair[mk:]):
+            assert bool((t == -7).all()), "maps past the batch"
+        assert bool((db.partial[mp:].view(torch.int16) == 0x5A5A).all()), "partial past the batch"
+        assert bool((db.out[T:].view(torch.int16) == 0x5A5A).all()), "out past the batch"
+    res = {}
+    for k in DEDUP_KEYS:
+        t = getattr(db, k)
+        res[k] = (t[:mp] if k in ("tp_row", "tp_src", "kmask") else t).cpu().numpy()
     res["kmask"] = res["kmask"].view(np.uint32)
     res["status"] = db.status.cpu().numpy().view(np.uint32)
     for k in PLAIN_LAYOUT_KEYS:
-        res[k] = getattr(buf, k).cpu().numpy()
-    res["recv_x"] = db.recv_x.view(torch.uint8).cpu().numpy() if wl.payload == "fp8" else \
-        db.recv_x.view(torch.int16).cpu().numpy().view(np.uint16)
+        t = getattr(buf, k)
+        res[k] = (t[:mk] if k in ("row_of_pair", "src_pair") else t).cpu().numpy()
+    res["recv_x"] = db.recv_x[:mp].view(torch.uint8).cpu().numpy() if wl.payload == "fp8" else \
+        db.recv_x[:mp].view(torch.int16).cpu().numpy().view(np.uint16)
     if db.recv_scales is not None:
-        res["recv_scales"] = db.recv_scales.cpu().numpy()
-    res["partial"] = db.partial.view(torch.int16).cpu().numpy().view(np.uint16)
-    res["out"] = db.out.view(torch.int16).cpu().numpy().view(np.uint16)
+        res["recv_scales"] = db.recv_scales[:mp].cpu().numpy()
+    res["partial"] = db.partial[:mp].view(torch.int16).cpu().numpy().view(np.uint16)
+    res["out"] = db.out[:T].view(torch.int16).cpu().numpy().view(np.uint16)
     return res
 
 

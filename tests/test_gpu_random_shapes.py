@@ -2,7 +2,9 @@
 within the API's limits (every layout regime, both dispatch launches, partial
 512-column steps), for the plain path (separate calls, the fused call, and the
 fused call with a random geometry its plan accepts) and the per-destination
-path (the same three), each against the oracle.
+path (the same three), each against the oracle; two of each three through
+buffers for more tokens than the batch (up to 300 more), whose rows past the
+batch must stay untouched.
 
 64 shapes by default; EP_RANDOM_SHAPES and EP_RANDOM_SEED draw more (or other)
 shapes, e.g. EP_RANDOM_SHAPES=3000 for a long sweep."""
@@ -35,7 +37,8 @@ def _shapes(n, seed):
         T = int(rng.choice([1, 2, 3, 4, 7, 16, 33, 64, 100, 128, 129, 200, 256, 300, 511, 700]))
         out.append(dict(name="rand%04d" % i, T=T, H=H, E=E, P=P, K=K, payload=payload,
                         mask_frac=float(rng.choice([0.0, 0.05, 0.3])),
-                        pick=int(rng.integers(1 << 30)), dpick=int(rng.integers(1 << 30))))
+                        pick=int(rng.integers(1 << 30)), dpick=int(rng.integers(1 << 30)),
+                        extra=int(rng.choice([0, 0, 1, 7, 64, 300]))))
     return out
 
 
@@ -45,20 +48,22 @@ SHAPES = _shapes(COUNT, SEED)
 @pytest.mark.parametrize("shape", SHAPES, ids=[s["name"] for s in SHAPES])
 def test_random_shape_parity(shape):
     from combine_ep_layout_05_amd import tuning
-    sh = {k: v for k, v in shape.items() if k not in ("pick", "dpick")}
+    sh = {k: v for k, v in shape.items() if k not in ("pick", "dpick", "extra")}
+    cap = shape["T"] + shape["extra"]             # buffers for more tokens than the batch
     wl = WORKLOADS["tiny_4x1024"].with_(**sh)
     dims = dict(T=wl.T, H=wl.H, K=wl.K, E=wl.E, P=wl.P, payload=wl.payload)
     cands = tuning.candidates("layout_dispatch", dims)
     geom = cands[shape["pick"] % len(cands)]
     dcands = tuning.candidates("dedup_layout_dispatch", dims)
     dgeom = dcands[shape["dpick"] % len(dcands)]
-    print("random shape", sh, "geometry", geom, "dedup geometry", dgeom, flush=True)
+    print("random shape", sh, "capacity", cap, "geometry", geom, "dedup geometry", dgeom,
+          flush=True)
     d = generate(wl, seed=500 + int(shape["name"][4:]) + SEED)
     ref = run_oracle(wl, d)
-    for fused, g in ((False, None), (True, None), (True, {"layout_dispatch": geom})):
-        got = run_gpu(wl, d, fused=fused, geometry=g)
-        assert compare(wl, got, ref) == 0, (shape, fused, g)
+    for fused, g, c in ((False, None, cap), (True, None, None), (True, {"layout_dispatch": geom}, cap)):
+        got = run_gpu(wl, d, fused=fused, geometry=g, capacity=c)
+        assert compare(wl, got, ref) == 0, (shape, fused, g, c)
     dref = run_oracle_dedup(wl, d)
-    for fused, g in ((False, None), (True, None), (True, dgeom)):
-        got = run_gpu_dedup(wl, d, fused=fused, geometry=g)
-        assert compare_dedup(wl, got, dref) == 0, (shape, fused, g)
+    for fused, g, c in ((False, None, cap), (True, None, None), (True, dgeom, cap)):
+        got = run_gpu_dedup(wl, d, fused=fused, geometry=g, capacity=c)
+        assert compare_dedup(wl, got, dref) == 0, (shape, fused, g, c)
