@@ -68,6 +68,51 @@ def test_graph_replay_matches_eager(name, fused):
     g.destroy()
 
 
+def test_graph_replay_of_a_batch_below_capacity():
+    """Buffers for 256 tokens, a captured step of a 40-token batch (int64 ids:
+    the narrowing launch is captured too): every replay equals the eager
+    40-token step, with unrelated eager work in between, and leaves the rows
+    past the batch alone."""
+    import combine_ep_layout_05_amd as ep
+    wl = WORKLOADS["ll_128x7168"].with_(T=40)
+    d = generate(wl, seed=77)
+    idx64 = torch.from_numpy(d["idx"].astype(np.int64)).cuda()
+    w = to_dev(d["w"])
+    x = to_dev(d["x"].view(np.int16), torch.bfloat16)
+    y = to_dev(d["y"].view(np.int16), torch.bfloat16)
+    print("graph case below capacity: 40 of 256 tokens", flush=True)
+    eager = ep.EpBuffers(wl.T, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    eager.layout_dispatch(idx64, x)
+    eager.combine(y, w)
+    torch.cuda.synchronize()
+    ref = collect(eager)
+    compare(wl, ref, run_oracle(wl, d), check_poison=False)
+
+    buf = ep.EpBuffers(256, wl.H, wl.K, wl.E, wl.P, payload=wl.payload)
+    m = wl.T * wl.K
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ep.ep_graph_begin(s)
+        buf.layout_dispatch(idx64, x, s)
+        buf.combine(y, w, s)
+        g = ep.ep_graph_end(s)
+    for rep in range(3):
+        buf.recv_x.view(torch.uint8).fill_(0)
+        buf.out.zero_()
+        buf.row_of_pair.fill_(-5)
+        junk = torch.randn(1 << 20, device="cuda").sum()     # unrelated eager work
+        torch.cuda.synchronize()
+        g.launch(s)
+        s.synchronize()
+        got = collect(buf, wl.T)
+        for k in ref:
+            assert np.array_equal(got[k], ref[k]), "replay %d: %s" % (rep, k)
+        assert bool((buf.row_of_pair[m:] == -5).all()), "replay %d: rows past the batch" % rep
+        assert bool((buf.out[wl.T:].view(torch.int16) == 0).all())
+        del junk
+    g.destroy()
+
+
 @pytest.mark.parametrize("name", ["ll_128x7168", "bw_4096x7168_zipf"])
 def test_dedup_graph_replay_matches_eager(name):
     """The per-destination step (ep_dedup_layout_dispatch, ep_combine_partial,
